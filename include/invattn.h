@@ -1,0 +1,251 @@
+/*
+ * invattn.h -- C ABI of libinvattn.so, a batch-invariant paged-attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Every (sequence, head, query position) is reduced in one fixed order that
+ * depends only on that row's logical inputs, so output bits do not depend on
+ * batch composition, query length, chunk split points, prefix reuse or
+ * physical page placement.  Sources for the contracts:
+ *
+ *  - Vosti: Specifying, Implementing, and Verifying Deterministic LLM
+ *    Inference (arXiv:2609.38981): §5.3 and App. A.1 (the causal contract:
+ *    query row i of an invocation with query length s and key length n sits
+ *    at position p = n - s + i; equal queries and equal logical K/V through p
+ *    give bitwise-equal output rows), App. A.2 (the tile arithmetic), §4.1-4.3
+ *    and Figure 2 (prefix sharing, write isolation, leaf-only eviction), §4.1
+ *    "Fixed kernel choices" (an immutable configuration, no autotuning, a
+ *    missing configuration is rejected).
+ *  - Deterministic inference: results independent of the batch (AI infra
+ *    handbook), "Batch invariance: fixed splits that don't change with load":
+ *    attention splits its KV by a fixed length, never into a fixed number of
+ *    pieces.
+ *  - Defeating Nondeterminism in LLM Inference (summary), Overview: fixed-size
+ *    split-KV plus a KV cache updated before the attention kernel.
+ *
+ * Conventions
+ *  - All tensors are row-major.  "dev" pointers are device memory on the
+ *    current HIP device; "host" pointers are host memory.  The caller owns
+ *    every buffer.  The library never allocates or frees device memory, never
+ *    synchronises, and enqueues work only on the `stream` argument (a
+ *    hipStream_t; NULL is the default stream).  Device buffers must stay alive
+ *    until that work completes.
+ *  - Status codes are returned; no C++ exception crosses the ABI.  Every
+ *    host-checkable argument is validated before anything is launched; on
+ *    error nothing is launched and ia_last_error() (thread-local) describes
+ *    why.  There is no fallback path.
+ *  - Device-resident preconditions are not checked on the hot path (they
+ *    would need a synchronisation): 1 <= q_len <= seq_len <= max_seq_len,
+ *    block-table entries of positions < seq_len in [0, num_pages), write slots
+ *    in range and pairwise disjoint, finite K/V/Q.  The kernels stay memory
+ *    safe when they are violated (out-of-range page ids and lengths are
+ *    clamped or read as zeros) but the results are then unspecified.
+ *
+ * Page layout (per KV pool; element = bf16, or one e4m3 byte for fp8):
+ *    K: [num_pages][num_kv_heads][head_dim/8][page_size][8]
+ *    V: [num_pages][num_kv_heads][head_dim][page_size]
+ *  Token t of physical page pg holds logical position j with
+ *  block_table[b][j / page_size] = pg and t = j % page_size; slot = pg *
+ *  page_size + t.
+ */
+#ifndef INVATTN_H_
+#define INVATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IA_OK = 0,
+  IA_ERR_INVALID_ARG = 1,
+  IA_ERR_UNSUPPORTED_CONFIG = 2,
+  IA_ERR_WORKSPACE_TOO_SMALL = 3,
+  IA_ERR_OUT_OF_PAGES = 4,
+  IA_ERR_PAGE_REFERENCED = 5,
+  IA_ERR_HIP = 6,
+  IA_ERR_INTERNAL = 7
+} ia_status;
+
+typedef enum { IA_KV_BF16 = 0, IA_KV_FP8_E4M3 = 1 } ia_kv_dtype;
+
+/* IA_SPLIT_FIXED: decode splits each sequence's keys at absolute multiples of
+ * split_tokens (batch invariant).  IA_SPLIT_BY_COUNT: decode cuts sequence b
+ * into k = max(1, min(64, 256 / B)) pieces, each roundup(ceil(n_b / k), 64)
+ * tokens long -- the load-based heuristic of the handbook's split-KV example
+ * with 256 compute units in place of 132 SMs.  It is NOT batch invariant and
+ * exists only to measure what invariance costs.  Prefill always uses the
+ * fixed split. */
+typedef enum { IA_SPLIT_FIXED = 0, IA_SPLIT_BY_COUNT = 1 } ia_split_policy;
+
+typedef struct {
+  int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads, Hq / Hkv <= 16 */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t page_size;     /* P: 16 */
+  int32_t split_tokens;  /* S: a positive multiple of 64 (the key tile) */
+  int32_t kv_dtype;      /* ia_kv_dtype */
+  int32_t split_policy;  /* ia_split_policy */
+  float sm_scale;        /* softmax scale, e.g. 1/sqrt(d); scores use
+                            c = fp32(sm_scale * log2(e)) and exp2 (Vosti App. A.2,
+                            "shared base-two scale c") */
+} ia_config;
+
+typedef struct ia_ctx ia_ctx;
+typedef struct ia_pool ia_pool;
+typedef struct ia_seq ia_seq;
+
+/* Validates and freezes a configuration (Vosti §4.1: fixed kernel choices,
+ * no runtime autotuning; an unsupported configuration is rejected with
+ * IA_ERR_UNSUPPORTED_CONFIG rather than served by another kernel).  The
+ * context is immutable and may be used from several threads at once. */
+ia_status ia_create(const ia_config* cfg, ia_ctx** out);
+void ia_destroy(ia_ctx* ctx);
+
+/* Thread-local description of the last error of this thread ("" if none). */
+const char* ia_last_error(void);
+
+/* Library version string. */
+const char* ia_version(void);
+
+/* Device workspace (bytes) that ia_paged_attn_decode needs for `batch`
+ * sequences of at most max_seq_len keys: one fp32 partial state
+ * (max, sum, head_dim accumulators) per (sequence, split, query head). */
+size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
+
+/* Device workspace for ia_paged_attn_prefill (0: prefill folds its split
+ * partials in registers). */
+size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len);
+
+/*
+ * kv_append: writes T new K/V rows into their page slots.  Enqueue it on the
+ * same stream before the attention call that reads them (Defeating
+ * Nondeterminism, Overview: the cache is updated before the attention kernel,
+ * which then reads every key through the cache).
+ *   k_new, v_new   dev [T][Hkv][d] bf16
+ *   slot_mapping   dev [T] int64, slot = page * P + offset; a negative slot
+ *                  skips the row (padding)
+ *   k_cache,v_cache dev page pools (layout above) of num_pages pages
+ *   k_scale,v_scale dev [Hkv] fp32 static per-KV-head scales for
+ *                  IA_KV_FP8_E4M3 (stored code = e4m3_rne(clamp(x / s, +-448)),
+ *                  value = code * s); must be NULL for IA_KV_BF16.
+ * Slots must be pairwise disjoint and must not belong to pages another
+ * sequence reads (shared pages are immutable, Vosti §4.3).
+ */
+ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t T, void* k_cache, void* v_cache, int32_t num_pages, const float* k_scale,
+                       const float* v_scale, void* stream);
+
+/*
+ * Decode attention: one query row per sequence, at position p = seq_len - 1
+ * (its own K/V already appended).  Keys are cut into splits at absolute
+ * multiples of split_tokens; each split is walked in 64-key tiles in
+ * ascending order with the online-softmax update of Vosti App. A.2 (fp32
+ * state m, z, U; weights rounded to bf16 before the PV product, z summing the
+ * unrounded weights); the split states are then folded in ascending split
+ * order and the row is finalised as O = bf16(U * select(z > 0, 1/z, 0)).
+ *   q            dev [B][Hq][d] bf16
+ *   block_table  dev [B][bt_stride] int32
+ *   seq_lens     dev [B] int32, n_b >= 1 keys including the current token
+ *   max_seq_len  host upper bound of seq_lens; sizes the grid only and never
+ *                changes a row's arithmetic; bt_stride * P >= max_seq_len
+ *   out          dev [B][Hq][d] bf16
+ *   workspace    dev, >= ia_decode_workspace_bytes(ctx, B, max_seq_len)
+ * Bitwise equal to ia_paged_attn_prefill's row at the same position.
+ */
+ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_cache, const void* v_cache,
+                               int32_t num_pages, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                               int32_t B, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * Chunked / whole prefill (and mixed batches): packed ragged query rows,
+ * causal, grouped-query.  Sequence b owns rows cu_q_lens[b] ..
+ * cu_q_lens[b+1]-1; row i of it is position p = seq_lens[b] - q_len_b + i and
+ * attends keys 0..p, all read from the pages (append the chunk's own K/V
+ * first).  Each row visits the same splits and tiles, in the same order and
+ * with the same arithmetic, as a decode row at that position; tiles past a
+ * row's position leave its state bit-identical (Vosti App. A.3-A.5).
+ *   q            dev [total_q][Hq][d] bf16
+ *   cu_q_lens    dev [B+1] int32 (cu_q_lens[0] = 0, total_q = cu_q_lens[B])
+ *   seq_lens     dev [B] int32, seq_len_b >= q_len_b
+ *   max_q_len    host upper bound of q lengths (grid only)
+ *   max_seq_len  host upper bound of seq_lens (grid only)
+ *   out          dev [total_q][Hq][d] bf16
+ */
+ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
+                                const int32_t* seq_lens, const void* k_cache, const void* v_cache,
+                                int32_t num_pages, const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t total_q,
+                                int32_t max_q_len, int32_t max_seq_len, void* out, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host page table with prefix sharing (host memory only; one pool is not
+ * thread safe).  Vosti §4.1-4.3, Figure 2:
+ *  - a cached page is reused only for the token prefix that produced it: a
+ *    rolling hash finds candidates, then exact tokens, depth and physical
+ *    parent page are checked, so a hash collision never justifies reuse;
+ *  - hits are resolved when a sequence begins, before it registers the pages
+ *    it will produce; new K/V go to private pages; a page is published for
+ *    reuse after it is full and its K/V are computed (ia_seq_commit);
+ *  - published pages are immutable and refcounted; when the last reference
+ *    ends they are retained; only unreferenced leaves of the parent chain are
+ *    evicted (least recently released first, ties by page id), so a parent is
+ *    never recycled while a retained child refers to it.
+ * Free pages are handed out lowest id first.  A prompt always keeps at least
+ * one token to compute.  A full page identical to a published one, or whose
+ * parent is not published, stays private.
+ * ------------------------------------------------------------------------ */
+
+/* flags: 0, or IA_POOL_CONSTANT_HASH (every page hashes alike -- a test hook
+ * that forces collisions; reuse must still be exact). */
+#define IA_POOL_CONSTANT_HASH 1
+ia_status ia_pool_create(int32_t num_pages, int32_t page_size, int32_t flags, ia_pool** out);
+void ia_pool_destroy(ia_pool* pool);
+
+/* Starts a sequence with prompt tokens[0..n) (host) and attaches its longest
+ * exactly-matching published prefix; *cached_len = tokens already in cache
+ * (a multiple of page_size, < n). */
+ia_status ia_seq_begin(ia_pool* pool, const int32_t* tokens, int32_t n, ia_seq** out, int32_t* cached_len);
+
+/* Appends generated tokens (host) to the sequence's history. */
+ia_status ia_seq_append_tokens(ia_pool* pool, ia_seq* seq, const int32_t* tokens, int32_t n);
+
+/* Reserves private write slots for the next n_new history positions and
+ * writes them to slot_mapping_out (host [n_new] int64).  Allocates pages,
+ * evicting unreferenced leaves if the free list runs short;
+ * IA_ERR_OUT_OF_PAGES (nothing allocated) if that is not enough. */
+ia_status ia_seq_reserve(ia_pool* pool, ia_seq* seq, int32_t n_new, int64_t* slot_mapping_out);
+
+/* Marks n_done reserved positions as computed and publishes pages that became
+ * full. */
+ia_status ia_seq_commit(ia_pool* pool, ia_seq* seq, int32_t n_done);
+
+/* Copies the sequence's page ids in logical order to out (host, capacity cap);
+ * *n_pages = their number (IA_ERR_INVALID_ARG if cap is too small). */
+ia_status ia_seq_block_table(const ia_seq* seq, int32_t* out, int32_t cap, int32_t* n_pages);
+
+/* Positions computed so far. */
+int32_t ia_seq_len(const ia_seq* seq);
+
+/* Ends the sequence: drops its references (published pages are retained,
+ * private pages freed) and frees the handle. */
+ia_status ia_seq_end(ia_pool* pool, ia_seq* seq);
+
+/* Evicts up to `want` unreferenced leaf pages; *evicted = how many. */
+ia_status ia_pool_evict(ia_pool* pool, int32_t want, int32_t* evicted);
+
+/* Introspection: refcount of a page (-1 if out of range), whether it is
+ * published, number of free pages. */
+int32_t ia_pool_page_refs(const ia_pool* pool, int32_t page);
+int32_t ia_pool_page_published(const ia_pool* pool, int32_t page);
+int32_t ia_pool_num_free(const ia_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INVATTN_H_ */

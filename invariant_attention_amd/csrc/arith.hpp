@@ -1,0 +1,230 @@
+// arith.hpp -- the one arithmetic core shared by every attention kernel.
+//
+// Every value-relevant operation of a query row lives here, so decode, prefill
+// and the split merge apply the same operations in the same order (Vosti:
+// Specifying, Implementing, and Verifying Deterministic LLM Inference, App. A.2:
+// "operations retain fixed floating-point types, parameters, and value-relevant
+// order").  The library is compiled with -ffp-contract=off: no product is fused
+// into an add unless written as such here.
+//
+// Wave geometry (gfx950, wave64).  A wave owns one block of 16 query rows and
+// walks 64-key tiles.  Both contractions run on v_mfma_f32_16x16x32_bf16 with
+// the query rows as the N (column) index, so a row's arithmetic never depends
+// on its column slot or on the other rows:
+//   scores   D[key][row] = sum_d K[key][d] * Q[row][d]     A = K tile, B = Q^T
+//   values   D[dim][row] = sum_key V^T[dim][key] * P^T[key][row]
+//                                                          A = V^T,    B = P^T
+// Lane l (group g = l / 16) holds, for its row l % 16:
+//   scores of keys 16*blk + 4*g + j          (blk = 0..3, j = 0..3)
+//   accumulators of dims 16*mb + 4*g + j     (mb = 0..d/16-1, j = 0..3)
+// MFMA k-slot j (0..7) of lane group g is, in k-step ks of the score product,
+// dim 32*ks + 8*g + j; in k-step ks2 of the value product it is key
+// 32*ks2 + 4*g + j for j < 4 and key 32*ks2 + 16 + 4*g + (j - 4) for j >= 4.
+// So the weights a lane produces are exactly the B operand it feeds into the
+// value product, with no cross-lane shuffle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ia {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+
+constexpr int kTileKeys = 64;   // B_N: keys per tile (4 pages of 16)
+constexpr int kBlockKeys = 16;  // keys per MFMA block (one page)
+constexpr int kRows = 16;       // query rows per wave
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// The single exp2 of the library (v_exp_f32).  exp2(0) = 1 and
+// exp2(-inf) = 0 exactly.
+__device__ __forceinline__ float ia_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row reductions over the 4 lanes that share a row (lanes l, l^16, l^32,
+// l^48).  IEEE addition and max are commutative, so the butterfly leaves the
+// same bits in all four lanes.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v = v + __shfl_xor(v, 16);
+  v = v + __shfl_xor(v, 32);
+  return v;
+}
+
+// Online-softmax state of one row (replicated in its 4 lanes) plus the lane's
+// D/4 accumulators.
+template <int D>
+struct RowState {
+  float m;              // running max of scaled scores (base-2 units)
+  float z;              // running sum of weights
+  f32x4 u[D / 16];      // weighted values, dims 16*mb + 4*g + j
+  __device__ __forceinline__ void init() {
+    m = neg_inf();
+    z = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) u[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// K fragments of one tile: kf[blk][ks] = A operand of key block blk, k-step ks.
+template <int D>
+struct KTile {
+  bf16x8 f[4][D / 32];
+};
+// V^T fragments of one tile: vf[mb][ks2] = A operand of dim block mb, key k-step ks2.
+template <int D>
+struct VTile {
+  bf16x8 f[D / 16][2];
+};
+// Q^T fragments of the wave's rows: qf[ks] = B operand of k-step ks.
+template <int D>
+struct QFrag {
+  bf16x8 f[D / 32];
+};
+
+// Scores of one tile: s[blk][j] = <q_row, k_{16 blk + 4 g + j}> (fp32).
+template <int D>
+__device__ __forceinline__ void tile_scores(const KTile<D>& kt, const QFrag<D>& q, f32x4 (&s)[4]) {
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) acc = mfma(kt.f[blk][ks], q.f[ks], acc);
+    s[blk] = acc;
+  }
+}
+
+// One tile of the online softmax for one row (Vosti App. A.2):
+//   G  = dot(Q, K^T) * c,  masked lanes -> -inf
+//   m^ = max(m, max_b G),  alpha = exp2(m - m^)
+//   A  = select(mask, exp2(G - m^), 0)
+//   z^ = z * alpha + sum_b A
+//   U^ = dot(A_hi, V, dot(A_lo, V, U * alpha) ... )   (see below)
+//   (m, z, U) <- select(any_b mask, (m^, z^, U^), (m, z, U))
+// `limit` is the row's last visible key (its position p); keys beyond it and
+// keys of rows that do not exist (limit < 0) are masked.  tile_key0 is the
+// absolute index of the tile's first key.  z sums the fp32 weights.
+//
+// The value product takes each fp32 weight as the unevaluated sum of two bf16
+// numbers, A_hi = bf16(A) and A_lo = bf16(A - A_hi) (A - A_hi is exact), and
+// runs one MFMA on each, hi first, per key k-step.  Vosti casts the weights
+// once to the cache type; with a single bf16 cast a row over a few keys whose
+// values cancel misses the 2e-3 + 1e-2 |ref| oracle tolerance (the weight
+// carries only 8 significant bits), while the hi/lo pair carries ~16.
+template <int D>
+__device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4], const VTile<D>& vt,
+                                            float c, int tile_key0, int limit, int lane_group) {
+  float x[4][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
+      const float g = s[blk][j] * c;
+      x[blk][j] = key <= limit ? g : neg_inf();
+      mx = fmaxf(mx, x[blk][j]);
+    }
+  }
+  mx = row_max(mx);
+  const bool any_visible = tile_key0 <= limit;
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = ia_exp2(st.m - m_new);
+  float a[4][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
+      a[blk][j] = key <= limit ? ia_exp2(x[blk][j] - m_new) : 0.f;
+      sum = sum + a[blk][j];
+    }
+  }
+  sum = row_sum(sum);
+  const float t = st.z * alpha;
+  const float z_new = t + sum;
+  bf16x8 phi[2], plo[2];
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = a[2 * ks2 + hb][j];
+        const __bf16 hi = to_bf16(w);
+        phi[ks2][4 * hb + j] = hi;
+        plo[ks2][4 * hb + j] = to_bf16(w - (float)hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    f32x4 un;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) un[j] = st.u[mb][j] * alpha;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      un = mfma(vt.f[mb][ks2], phi[ks2], un);
+      un = mfma(vt.f[mb][ks2], plo[ks2], un);
+    }
+    if (any_visible) st.u[mb] = un;
+  }
+  if (any_visible) {
+    st.m = m_new;
+    st.z = z_new;
+  }
+}
+
+// Folds split partial (m_s, z_s, U_s) into the running merged state (M, Z, U);
+// splits are folded in ascending order, the first one seeding the state
+// (fixed-size split-KV with the LSE merge of "Deterministic inference: results
+// independent of the batch", split-KV decode example).
+__device__ __forceinline__ void merge_scalars(float& M, float& Z, float m_s, float z_s, float& a, float& b) {
+  const float M_new = fmaxf(M, m_s);
+  a = ia_exp2(M - M_new);
+  b = ia_exp2(m_s - M_new);
+  const float t1 = Z * a;
+  const float t2 = z_s * b;
+  Z = t1 + t2;
+  M = M_new;
+}
+__device__ __forceinline__ float merge_value(float U, float U_s, float a, float b) {
+  const float t1 = U * a;
+  const float t2 = U_s * b;
+  return t1 + t2;
+}
+
+// Reciprocal of the final sum: select(z > 0, 1/z, 0) (Vosti App. A.2), with
+// IEEE division.
+__device__ __forceinline__ float final_rz(float Z) { return Z > 0.f ? 1.0f / Z : 0.f; }
+
+// O = bf16((U * v_scale) * rz); v_scale is 1 for bf16 pages and the static
+// per-head scale for fp8 pages (scaling by 2^k commutes with rounding).
+__device__ __forceinline__ __bf16 finalize(float U, float v_scale, float rz) {
+  const float t = U * v_scale;
+  return to_bf16(t * rz);
+}
+
+// e4m3 (OCP) -> bf16, exact: 2 codes per instruction.
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+}  // namespace ia

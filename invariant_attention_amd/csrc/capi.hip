@@ -1,0 +1,279 @@
+// capi.hip -- the C ABI of libinvattn.so: configuration, argument validation
+// and launches.  Every host-checkable argument is checked before anything is
+// enqueued; on error nothing is launched (Detent, §5 "Legal values": a failed
+// precondition stops with an error and runs no kernel; Vosti §4.1: a missing
+// configuration is rejected, never autotuned or replaced).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/invattn.h"
+#include "errors.hpp"
+#include "launch.hpp"
+
+struct ia_ctx {
+  ia_config cfg;
+  float c;  // fp32(sm_scale * log2 e), rounded once from double
+  int group;
+};
+
+namespace {
+thread_local char g_err[512] = "";
+}  // namespace
+
+ia_status ia::fail(ia_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ia_status ia::ok() {
+  g_err[0] = '\0';
+  return IA_OK;
+}
+
+namespace {
+using ia::fail;
+using ia::ok;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kTileKeys = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len) {
+  if (ctx->cfg.split_policy == IA_SPLIT_FIXED) return ceil_div(max_seq_len, ctx->cfg.split_tokens);
+  int64_t k = 256 / (batch > 0 ? batch : 1);
+  k = k < 1 ? 1 : (k > 64 ? 64 : k);
+  const int64_t by_tile = ceil_div(max_seq_len, kTileKeys);
+  return k < by_tile ? k : by_tile;
+}
+
+// Bytes of the two workspace arrays (U accumulators, then (m, z) pairs).
+void decode_ws_parts(const ia_ctx* ctx, int64_t B, int64_t max_seq_len, size_t* u_bytes, size_t* ml_bytes) {
+  const int64_t ms = decode_max_splits(ctx, B, max_seq_len);
+  const int64_t rows = B * ms * ctx->cfg.num_q_heads;
+  *u_bytes = align_up((size_t)rows * ctx->cfg.head_dim * sizeof(float));
+  *ml_bytes = align_up((size_t)rows * 2 * sizeof(float));
+}
+
+ia_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(IA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+ia_status check_scales(const ia_ctx* ctx, const float* k_scale, const float* v_scale) {
+  if (ctx->cfg.kv_dtype == IA_KV_FP8_E4M3) {
+    if (!k_scale || !v_scale) return fail(IA_ERR_INVALID_ARG, "fp8 pages need k_scale and v_scale");
+  } else if (k_scale || v_scale) {
+    return fail(IA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pages");
+  }
+  return IA_OK;
+}
+
+ia_status check_pages(const void* k_cache, const void* v_cache, int32_t num_pages) {
+  if (!k_cache || !v_cache) return fail(IA_ERR_INVALID_ARG, "k_cache/v_cache is NULL");
+  if (num_pages <= 0) return fail(IA_ERR_INVALID_ARG, "num_pages must be positive (got %d)", num_pages);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(IA_ERR_INVALID_ARG, "page pools must be 16-byte aligned");
+  return IA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ia_last_error(void) { return g_err; }
+
+const char* ia_version(void) { return "invattn 0.1 gfx950"; }
+
+ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
+  if (!cfg || !out) return fail(IA_ERR_INVALID_ARG, "cfg and out must be non-NULL");
+  *out = nullptr;
+  const ia_config& c = *cfg;
+  if (c.num_kv_heads <= 0 || c.num_q_heads <= 0 || c.num_q_heads % c.num_kv_heads != 0)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                c.num_q_heads, c.num_kv_heads);
+  const int group = c.num_q_heads / c.num_kv_heads;
+  if (group > 16) return fail(IA_ERR_UNSUPPORTED_CONFIG, "query heads per kv head must be <= 16 (got %d)", group);
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "head_dim must be 64 or 128 (got %d)", c.head_dim);
+  if (c.page_size != 16) return fail(IA_ERR_UNSUPPORTED_CONFIG, "page_size must be 16 (got %d)", c.page_size);
+  if (c.split_tokens <= 0 || c.split_tokens % kTileKeys != 0)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "split_tokens must be a positive multiple of %d (got %d)", kTileKeys,
+                c.split_tokens);
+  if (c.kv_dtype != IA_KV_BF16 && c.kv_dtype != IA_KV_FP8_E4M3)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown kv_dtype %d", c.kv_dtype);
+  if (c.split_policy != IA_SPLIT_FIXED && c.split_policy != IA_SPLIT_BY_COUNT)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown split_policy %d", c.split_policy);
+  if (!(c.sm_scale > 0.f) || !std::isfinite(c.sm_scale))
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "sm_scale must be finite and positive");
+  ia_ctx* ctx = new (std::nothrow) ia_ctx;
+  if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
+  ctx->cfg = c;
+  ctx->group = group;
+  ctx->c = (float)((double)c.sm_scale * 1.4426950408889634073599246810018921);  // log2(e)
+  *out = ctx;
+  return ok();
+}
+
+void ia_destroy(ia_ctx* ctx) { delete ctx; }
+
+size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len) {
+  if (!ctx || batch <= 0 || max_seq_len <= 0) return 0;
+  size_t u, ml;
+  decode_ws_parts(ctx, batch, max_seq_len, &u, &ml);
+  return u + ml;
+}
+
+size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
+  (void)ctx;
+  (void)total_q;
+  (void)max_seq_len;
+  return 0;
+}
+
+ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t T, void* k_cache, void* v_cache, int32_t num_pages, const float* k_scale,
+                       const float* v_scale, void* stream) {
+  if (!ctx) return fail(IA_ERR_INVALID_ARG, "ctx is NULL");
+  if (T < 0) return fail(IA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  ia_status st = check_scales(ctx, k_scale, v_scale);
+  if (st != IA_OK) return st;
+  if ((st = check_pages(k_cache, v_cache, num_pages)) != IA_OK) return st;
+  if (T == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(IA_ERR_INVALID_ARG, "k_new/v_new/slot_mapping is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(IA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  if ((int64_t)T * ctx->cfg.num_kv_heads * (ctx->cfg.head_dim / 8) / 256 >= (int64_t)1 << 31)
+    return fail(IA_ERR_INVALID_ARG, "T too large for one launch");
+  ia::AppendArgs a;
+  a.k_new = static_cast<const __bf16*>(k_new);
+  a.v_new = static_cast<const __bf16*>(v_new);
+  a.slots = slot_mapping;
+  a.T = T;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.num_pages = num_pages;
+  a.Hkv = ctx->cfg.num_kv_heads;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return hip_status(ia::launch_kv_append(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
+                                         static_cast<hipStream_t>(stream)),
+                    "kv_append launch");
+}
+
+ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_cache, const void* v_cache,
+                               int32_t num_pages, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                               int32_t B, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  if (!ctx) return fail(IA_ERR_INVALID_ARG, "ctx is NULL");
+  if (B < 0) return fail(IA_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  ia_status st = check_scales(ctx, k_scale, v_scale);
+  if (st != IA_OK) return st;
+  if (B == 0) return ok();
+  if ((st = check_pages(k_cache, v_cache, num_pages)) != IA_OK) return st;
+  if (!q || !block_table || !seq_lens || !out) return fail(IA_ERR_INVALID_ARG, "q/block_table/seq_lens/out is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(IA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (max_seq_len <= 0) return fail(IA_ERR_INVALID_ARG, "max_seq_len must be positive (got %d)", max_seq_len);
+  if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
+    return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
+  size_t u_bytes, ml_bytes;
+  decode_ws_parts(ctx, B, max_seq_len, &u_bytes, &ml_bytes);
+  if (!workspace || ws_bytes < u_bytes + ml_bytes)
+    return fail(IA_ERR_WORKSPACE_TOO_SMALL, "decode workspace needs %zu bytes (got %zu)", u_bytes + ml_bytes, ws_bytes);
+  if (!aligned(workspace, 16)) return fail(IA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int64_t ms = decode_max_splits(ctx, B, max_seq_len);
+  if ((int64_t)B * ctx->cfg.num_kv_heads * ms >= ((int64_t)1 << 31))
+    return fail(IA_ERR_INVALID_ARG, "grid too large");
+  ia::DecodeArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<__bf16*>(out);
+  a.ws_u = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes);
+  a.c = ctx->c;
+  a.B = B;
+  a.Hq = ctx->cfg.num_q_heads;
+  a.Hkv = ctx->cfg.num_kv_heads;
+  a.group = ctx->group;
+  a.bt_stride = bt_stride;
+  a.num_pages = num_pages;
+  a.max_seq_len = max_seq_len;
+  a.max_splits = (int)ms;
+  a.split_tokens = ctx->cfg.split_tokens;
+  a.policy = ctx->cfg.split_policy;
+  return hip_status(ia::launch_decode(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
+                                      static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
+                                const int32_t* seq_lens, const void* k_cache, const void* v_cache,
+                                int32_t num_pages, const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t total_q,
+                                int32_t max_q_len, int32_t max_seq_len, void* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!ctx) return fail(IA_ERR_INVALID_ARG, "ctx is NULL");
+  if (B < 0 || total_q < 0 || max_q_len < 0)
+    return fail(IA_ERR_INVALID_ARG, "B, total_q and max_q_len must be >= 0");
+  ia_status st = check_scales(ctx, k_scale, v_scale);
+  if (st != IA_OK) return st;
+  if (B == 0 || total_q == 0) return ok();
+  if ((st = check_pages(k_cache, v_cache, num_pages)) != IA_OK) return st;
+  if (!q || !cu_q_lens || !seq_lens || !block_table || !out)
+    return fail(IA_ERR_INVALID_ARG, "q/cu_q_lens/seq_lens/block_table/out is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(IA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (max_q_len <= 0 || max_seq_len <= 0)
+    return fail(IA_ERR_INVALID_ARG, "max_q_len and max_seq_len must be positive when total_q > 0");
+  if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
+    return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
+  const int ppb = 16 / ctx->group;
+  const int64_t row_blocks = ceil_div(max_q_len, ppb);
+  if ((int64_t)B * row_blocks * ctx->cfg.num_kv_heads >= ((int64_t)1 << 31))
+    return fail(IA_ERR_INVALID_ARG, "grid too large");
+  ia::PrefillArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.cu_q_lens = cu_q_lens;
+  a.seq_lens = seq_lens;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.out = static_cast<__bf16*>(out);
+  a.c = ctx->c;
+  a.B = B;
+  a.Hq = ctx->cfg.num_q_heads;
+  a.Hkv = ctx->cfg.num_kv_heads;
+  a.group = ctx->group;
+  a.bt_stride = bt_stride;
+  a.num_pages = num_pages;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.max_row_blocks = (int)row_blocks;
+  a.split_tokens = ctx->cfg.split_tokens;
+  a.total_q = total_q;
+  return hip_status(ia::launch_prefill(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
+                                       static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// launch.hpp -- kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ia {
+
+struct AppendArgs {
+  const __bf16* k_new;
+  const __bf16* v_new;
+  const int64_t* slots;
+  int T;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int num_pages;
+  int Hkv;
+  const float* k_scale;
+  const float* v_scale;
+};
+
+struct DecodeArgs {
+  const __bf16* q;            // [B][Hq][D]
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;  // [B][bt_stride]
+  const int32_t* seq_lens;     // [B]
+  __bf16* out;                 // [B][Hq][D]
+  float* ws_u;                 // [B][max_splits][Hq][D]
+  float* ws_ml;                // [B][max_splits][Hq][2]
+  float c;                     // fp32(sm_scale * log2 e)
+  int B, Hq, Hkv, group;
+  int bt_stride, num_pages;
+  int max_seq_len, max_splits;
+  int split_tokens, policy;
+};
+
+struct PrefillArgs {
+  const __bf16* q;            // [total_q][Hq][D]
+  const int32_t* cu_q_lens;   // [B+1]
+  const int32_t* seq_lens;    // [B]
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  __bf16* out;
+  float c;
+  int B, Hq, Hkv, group;
+  int bt_stride, num_pages;
+  int max_q_len, max_seq_len, max_row_blocks;
+  int split_tokens;
+  int total_q;
+};
+
+hipError_t launch_kv_append(int D, bool fp8, const AppendArgs& a, hipStream_t st);
+hipError_t launch_decode(int D, bool fp8, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st);
+
+}  // namespace ia

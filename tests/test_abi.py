@@ -1,0 +1,115 @@
+"""CPU tests of the C ABI: the library loads, exports every function include/invattn.h declares,
+and rejects bad configurations and arguments on the host before anything is launched (no GPU
+call is made by any test here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from invariant_attention_amd import binding as ia
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "invattn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(ia_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    ia.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\sT\s+(ia_\w+)", out.stdout))
+    declared = _declared_functions()
+    assert len(declared) >= 20
+    missing = [n for n in declared if n not in exported]
+    assert not missing, missing
+    assert set(declared) == set(ia.EXPORTS)
+
+
+def test_version_and_clean_error_state():
+    assert "gfx950" in ia.ia_version()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(Hq=32, Hkv=8, d=96), "head_dim"),
+    (dict(Hq=30, Hkv=8, d=128), "multiple"),
+    (dict(Hq=64, Hkv=2, d=128), "<= 16"),
+    (dict(Hq=32, Hkv=8, d=128, page_size=32), "page_size"),
+    (dict(Hq=32, Hkv=8, d=128, split_tokens=100), "split_tokens"),
+    (dict(Hq=32, Hkv=8, d=128, split_tokens=0), "split_tokens"),
+    (dict(Hq=32, Hkv=8, d=128, kv_dtype=7), "kv_dtype"),
+    (dict(Hq=32, Hkv=8, d=128, split_policy=3), "split_policy"),
+    (dict(Hq=32, Hkv=8, d=128, sm_scale=-1.0), "sm_scale"),
+])
+def test_unsupported_configs_are_rejected(kw, msg):
+    Hq, Hkv, d = kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d")
+    with pytest.raises(ia.IAError) as e:
+        ia.Context(ia.make_config(Hq, Hkv, d, **kw))
+    assert e.value.status == ia.IA_ERR_UNSUPPORTED_CONFIG and msg in str(e.value)
+
+
+def test_workspace_size_formula():
+    ctx = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048))
+    # B * ceil(max_len / S) * Hq rows of (d + 2) floats, each array rounded up to 256 bytes
+    got = ia.ia_decode_workspace_bytes(ctx, 256, 8192)
+    rows = 256 * 4 * 32
+    up = lambda x: (x + 255) // 256 * 256
+    assert got == up(rows * 128 * 4) + up(rows * 2 * 4)
+    assert ia.ia_decode_workspace_bytes(ctx, 0, 8192) == 0
+    bc = ia.Context(ia.make_config(32, 8, 128, split_policy=ia.IA_SPLIT_BY_COUNT))
+    # split-by-count: at most min(64, 256 // B) pieces, and no more than one per 64-key tile
+    assert ia.ia_decode_workspace_bytes(bc, 1, 64) == up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4)
+    assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
+
+
+def _decode(ctx, **over):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, num_pages=10, ks=None, vs=None, bt=FAKE, bt_stride=512, sl=FAKE,
+                B=4, max_seq_len=8192, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    args.update(over)
+    lib = ia.load()
+    return lib.ia_paged_attn_decode(ctx.handle, args["q"], args["kc"], args["vc"], args["num_pages"], args["ks"],
+                                    args["vs"], args["bt"], args["bt_stride"], args["sl"], args["B"],
+                                    args["max_seq_len"], args["out"], args["ws"], args["ws_bytes"], None)
+
+
+def test_decode_argument_errors_launch_nothing():
+    ctx = ia.Context(ia.make_config(32, 8, 128))
+    assert _decode(ctx, B=0) == ia.IA_OK  # empty batch: nothing to do
+    assert _decode(ctx, B=-1) == ia.IA_ERR_INVALID_ARG
+    assert _decode(ctx, ws_bytes=100) == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in ia.ia_last_error()
+    assert _decode(ctx, bt_stride=10) == ia.IA_ERR_INVALID_ARG  # 10 pages cannot hold 8192 keys
+    assert _decode(ctx, num_pages=0) == ia.IA_ERR_INVALID_ARG
+    assert _decode(ctx, q=None) == ia.IA_ERR_INVALID_ARG
+    assert _decode(ctx, max_seq_len=0) == ia.IA_ERR_INVALID_ARG
+    assert _decode(ctx, ks=FAKE) == ia.IA_ERR_INVALID_ARG  # scales only for fp8 pages
+    assert _decode(ctx, q=ctypes.c_void_p((1 << 20) + 2)) == ia.IA_ERR_INVALID_ARG  # misaligned
+    fp8 = ia.Context(ia.make_config(32, 8, 128, kv_dtype=ia.IA_KV_FP8_E4M3))
+    assert _decode(fp8) == ia.IA_ERR_INVALID_ARG  # fp8 pages need scales
+
+
+def test_append_and_prefill_argument_errors():
+    ctx = ia.Context(ia.make_config(8, 2, 64, split_tokens=128))
+    lib = ia.load()
+    assert lib.ia_kv_append(ctx.handle, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 4, None, None, None) == ia.IA_OK
+    assert lib.ia_kv_append(ctx.handle, FAKE, FAKE, FAKE, -1, FAKE, FAKE, 4, None, None, None) == ia.IA_ERR_INVALID_ARG
+    assert lib.ia_kv_append(ctx.handle, None, FAKE, FAKE, 3, FAKE, FAKE, 4, None, None, None) == ia.IA_ERR_INVALID_ARG
+    assert lib.ia_kv_append(ctx.handle, FAKE, FAKE, FAKE, 3, None, FAKE, 4, None, None, None) == ia.IA_ERR_INVALID_ARG
+    pre = lib.ia_paged_attn_prefill
+    assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 0, 0, 0, 0, FAKE, None, 0,
+               None) == ia.IA_OK
+    assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 1, 2, 10, 5, 100, FAKE, None, 0,
+               None) == ia.IA_ERR_INVALID_ARG  # bt_stride too small for max_seq_len
+    assert pre(ctx.handle, FAKE, None, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 100, FAKE, None, 0,
+               None) == ia.IA_ERR_INVALID_ARG
+    assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 0, 100, FAKE, None, 0,
+               None) == ia.IA_ERR_INVALID_ARG  # rows but max_q_len 0
