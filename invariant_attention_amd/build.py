@@ -11,8 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libinvattn.so")
-SOURCES = ["attention.hip", "capi.hip", "pool.cpp"]
-HEADERS = ["arith.hpp", "launch.hpp", "errors.hpp"]
+SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "capi.hip", "pool.cpp"]
+HEADERS = ["arith.hpp", "pages.hpp", "launch.hpp", "errors.hpp"]
 
 # -ffp-contract=off: no implicit FMA contraction -- the arithmetic order is the one
 # written in arith.hpp.  The packed-fp32 feature is turned off for the device pass.

@@ -97,38 +97,48 @@ struct QFrag {
   bf16x8 f[D / 32];
 };
 
-// Scores of one tile: s[blk][j] = <q_row, k_{16 blk + 4 g + j}> (fp32).
+// Scores of one key block (16 keys) for the wave's rows: s[j] = <q_row,
+// k_{16 blk + 4 g + j}> as one MFMA chain over the D/32 k-steps of the head
+// dim, in ascending order.  Which wave computes a block does not change its
+// bits: a column of the product depends only on its own operands.
+template <int D>
+__device__ __forceinline__ f32x4 block_scores(const bf16x8 (&kf)[D / 32], const QFrag<D>& q) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) acc = mfma(kf[ks], q.f[ks], acc);
+  return acc;
+}
+
+// Scores of one tile: s[blk] = block_scores(K block blk).
 template <int D>
 __device__ __forceinline__ void tile_scores(const KTile<D>& kt, const QFrag<D>& q, f32x4 (&s)[4]) {
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) acc = mfma(kt.f[blk][ks], q.f[ks], acc);
-    s[blk] = acc;
-  }
+  for (int blk = 0; blk < 4; ++blk) s[blk] = block_scores<D>(kt.f[blk], q);
 }
 
-// One tile of the online softmax for one row (Vosti App. A.2):
+// The softmax half of one tile's update for one row (Vosti App. A.2):
 //   G  = dot(Q, K^T) * c,  masked lanes -> -inf
 //   m^ = max(m, max_b G),  alpha = exp2(m - m^)
 //   A  = select(mask, exp2(G - m^), 0)
 //   z^ = z * alpha + sum_b A
-//   U^ = dot(A_hi, V, dot(A_lo, V, U * alpha) ... )   (see below)
-//   (m, z, U) <- select(any_b mask, (m^, z^, U^), (m, z, U))
 // `limit` is the row's last visible key (its position p); keys beyond it and
 // keys of rows that do not exist (limit < 0) are masked.  tile_key0 is the
-// absolute index of the tile's first key.  z sums the fp32 weights.
-//
-// The value product takes each fp32 weight as the unevaluated sum of two bf16
-// numbers, A_hi = bf16(A) and A_lo = bf16(A - A_hi) (A - A_hi is exact), and
-// runs one MFMA on each, hi first, per key k-step.  Vosti casts the weights
-// once to the cache type; with a single bf16 cast a row over a few keys whose
-// values cancel misses the 2e-3 + 1e-2 |ref| oracle tolerance (the weight
-// carries only 8 significant bits), while the hi/lo pair carries ~16.
-template <int D>
-__device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4], const VTile<D>& vt,
-                                            float c, int tile_key0, int limit, int lane_group) {
+// absolute index of the tile's first key.  z sums the fp32 weights.  The
+// weights leave as the B operands of the value product: each fp32 weight is
+// the unevaluated sum of two bf16 numbers, A_hi = bf16(A) and
+// A_lo = bf16(A - A_hi) (A - A_hi is exact).  Vosti casts the weights once to
+// the cache type; with a single bf16 cast a row over a few keys whose values
+// cancel misses the 2e-3 + 1e-2 |ref| oracle tolerance (the weight carries
+// only 8 significant bits), while the hi/lo pair carries ~16.
+struct TileStep {
+  float m_new, z_new, alpha;
+  bool any_visible;   // the tile holds a key <= limit; otherwise the state is kept bit for bit
+  bf16x8 phi[2], plo[2];
+};
+
+__device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (&s)[4], float c, int tile_key0,
+                                                 int limit, int lane_group) {
+  TileStep ts;
   float x[4][4];
   float mx = neg_inf();
 #pragma unroll
@@ -142,9 +152,9 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4]
     }
   }
   mx = row_max(mx);
-  const bool any_visible = tile_key0 <= limit;
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = ia_exp2(st.m - m_new);
+  ts.any_visible = tile_key0 <= limit;
+  ts.m_new = fmaxf(m, mx);
+  ts.alpha = ia_exp2(m - ts.m_new);
   float a[4][4];
   float sum = 0.f;
 #pragma unroll
@@ -152,14 +162,13 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
-      a[blk][j] = key <= limit ? ia_exp2(x[blk][j] - m_new) : 0.f;
+      a[blk][j] = key <= limit ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
       sum = sum + a[blk][j];
     }
   }
   sum = row_sum(sum);
-  const float t = st.z * alpha;
-  const float z_new = t + sum;
-  bf16x8 phi[2], plo[2];
+  const float t = z * ts.alpha;
+  ts.z_new = t + sum;
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
@@ -168,27 +177,46 @@ __device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4]
       for (int j = 0; j < 4; ++j) {
         const float w = a[2 * ks2 + hb][j];
         const __bf16 hi = to_bf16(w);
-        phi[ks2][4 * hb + j] = hi;
-        plo[ks2][4 * hb + j] = to_bf16(w - (float)hi);
+        ts.phi[ks2][4 * hb + j] = hi;
+        ts.plo[ks2][4 * hb + j] = to_bf16(w - (float)hi);
       }
     }
   }
+  return ts;
+}
+
+// The value half of the update for one dim block mb of a row:
+//   U^ = U * alpha, then per key k-step ks2 (ascending) U^ += V^T A_hi, U^ += V^T A_lo
+// (one MFMA each, hi first); the block keeps U when the tile is fully masked.
+__device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2], const TileStep& ts) {
+  f32x4 un;
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) {
-    f32x4 un;
+  for (int j = 0; j < 4; ++j) un[j] = u[j] * ts.alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) un[j] = st.u[mb][j] * alpha;
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      un = mfma(vt.f[mb][ks2], phi[ks2], un);
-      un = mfma(vt.f[mb][ks2], plo[ks2], un);
-    }
-    if (any_visible) st.u[mb] = un;
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    un = mfma(vf[ks2], ts.phi[ks2], un);
+    un = mfma(vf[ks2], ts.plo[ks2], un);
   }
-  if (any_visible) {
-    st.m = m_new;
-    st.z = z_new;
+  return ts.any_visible ? un : u;
+}
+
+// Commits the scalar half of a tile step.
+__device__ __forceinline__ void commit_scalars(float& m, float& z, const TileStep& ts) {
+  if (ts.any_visible) {
+    m = ts.m_new;
+    z = ts.z_new;
   }
+}
+
+// One whole tile of the online softmax for one row: the softmax half, the
+// value half for every dim block, then the scalars.
+template <int D>
+__device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4], const VTile<D>& vt,
+                                            float c, int tile_key0, int limit, int lane_group) {
+  const TileStep ts = tile_softmax(st.m, st.z, s, c, tile_key0, limit, lane_group);
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) st.u[mb] = pv_block(st.u[mb], vt.f[mb], ts);
+  commit_scalars(st.m, st.z, ts);
 }
 
 // Folds split partial (m_s, z_s, U_s) into the running merged state (M, Z, U);

@@ -245,8 +245,7 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
     return fail(IA_ERR_INVALID_ARG, "max_q_len and max_seq_len must be positive when total_q > 0");
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  const int ppb = 16 / ctx->group;
-  const int64_t row_blocks = ceil_div(max_q_len, ppb);
+  const int64_t row_blocks = ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group));
   if ((int64_t)B * row_blocks * ctx->cfg.num_kv_heads >= ((int64_t)1 << 31))
     return fail(IA_ERR_INVALID_ARG, "grid too large");
   ia::PrefillArgs a;

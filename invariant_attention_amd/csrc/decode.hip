@@ -1,0 +1,263 @@
+// decode.hip -- decode attention: the fixed-split kernel and the ascending
+// split merge.  All value-relevant arithmetic is in arith.hpp.
+//
+// One workgroup of 4 waves per (sequence b, kv head, split s).  The g query
+// heads of the group are the rows (padded to 16).  Per 64-key tile, wave w
+// computes the scores of key block w (its own 16 keys, all head dims),
+// the 4 waves exchange scores through LDS, every wave runs the same softmax
+// step on the whole tile, and wave w applies it to dim blocks
+// [w * D/64, (w + 1) * D/64) of the value accumulators.  A row's operations
+// and their order are those of tile_update (arith.hpp), so the bits equal
+// prefill's at the same position; splitting the blocks over waves only
+// changes where each operation runs.  Each wave loads exactly the operand
+// fragments it consumes, straight from the pages into registers, one tile
+// ahead of the compute.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arith.hpp"
+#include "launch.hpp"
+#include "pages.hpp"
+
+namespace ia {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kBtWindowTiles = 256;  // block-table entries staged per LDS refill: 4 per tile
+
+// Split length for sequence b: the fixed deployment constant, or (comparison
+// variant only) the load-based length roundup(ceil(n / k), 64) with
+// k = max(1, min(64, 256 / B)).
+__device__ __forceinline__ int split_len(int policy, int S, int n, int B) {
+  if (policy == 0) return S;
+  int k = 256 / (B > 0 ? B : 1);
+  k = k < 1 ? 1 : (k > 64 ? 64 : k);
+  int len = (n + k - 1) / k;
+  len = (len + 63) & ~63;
+  return len < 64 ? 64 : len;
+}
+
+// Raw fragments one wave needs for one tile: K block w (all k-steps) and the
+// V^T fragments of its D/64 dim blocks (4 key quads each), plus the key
+// counts for the zero fill (k_valid: block w; valid: every block).
+template <int D, bool FP8>
+struct DecodeFrags {
+  static constexpr int MB = D / 64;
+  typename Raw<FP8>::K k[D / 32];
+  typename Raw<FP8>::V v[MB][2][2];
+  int k_valid;
+  int valid[4];
+};
+
+// Loads the fragments of the tile at t0 given its 4 block-table entries.
+// Addresses are a wave-uniform page base plus a 32-bit per-lane offset that
+// is the same for every tile.
+template <int D, bool FP8>
+__device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const uint8_t* kc, const uint8_t* vc,
+                                                  const int4& e, int t0, int n, int num_pages, int kvh, int Hkv,
+                                                  int w, int r, int g) {
+  constexpr int MB = D / 64;
+  constexpr int EB = Raw<FP8>::kElemBytes;
+  constexpr size_t kHeadBytes = (size_t)D * 16 * EB;  // one (page, kv head) block
+  const TilePages tp = tile_pages_of(e, t0, n, num_pages);
+  const int kpg = w == 0 ? tp.page[0] : (w == 1 ? tp.page[1] : (w == 2 ? tp.page[2] : tp.page[3]));
+  f.k_valid = w == 0 ? tp.valid[0] : (w == 1 ? tp.valid[1] : (w == 2 ? tp.valid[2] : tp.valid[3]));
+  const uint8_t* kp = kc + ((size_t)kpg * Hkv + kvh) * kHeadBytes;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const uint32_t off = (uint32_t)(((4 * ks + g) * 16 + r) * 8 * EB);
+    f.k[ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(kp + off);
+  }
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint8_t* vp = vc + ((size_t)tp.page[2 * ks2 + hb] * Hkv + kvh) * kHeadBytes;
+#pragma unroll
+      for (int mbi = 0; mbi < MB; ++mbi) {
+        const uint32_t off = (uint32_t)(((16 * (w * MB + mbi) + r) * 16 + 4 * g) * EB);
+        f.v[mbi][ks2][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(vp + off);
+      }
+    }
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) f.valid[blk] = tp.valid[blk];
+}
+
+// One tile of a decode unit: wave w's scores of key block w go through LDS
+// buffer `xb` to all 4 waves; each wave runs the softmax step of the whole
+// tile and the value step of its own dim blocks.
+template <int D, bool FP8>
+__device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const QFrag<D>& q, f32x4 (*xb)[64],
+                                            float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int limit,
+                                            int w, int lane, int r, int g) {
+  constexpr int MB = D / 64;
+  bf16x8 kf[D / 32];
+  const bool key_ok = r < f.k_valid;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(f.k[ks], key_ok);
+  xb[w][lane] = block_scores<D>(kf, q);
+  __syncthreads();
+  f32x4 sc[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) sc[blk] = xb[blk][lane];
+  const TileStep ts = tile_softmax(m, z, sc, c, t0, limit, g);
+#pragma unroll
+  for (int mbi = 0; mbi < MB; ++mbi) {
+    bf16x8 vf[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const bf16x4 v4 = v_to_bf16(f.v[mbi][ks2][hb], f.valid[2 * ks2 + hb] - 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
+      }
+    }
+    u[mbi] = pv_block(u[mbi], vf, ts);
+  }
+  commit_scalars(m, z, ts);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr int MB = D / 64;
+  __shared__ f32x4 xs[2][4][64];  // score exchange, double buffered by tile parity
+  __shared__ __attribute__((aligned(16))) int bt_lds[4 * kBtWindowTiles];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int unit = blockIdx.x;
+  const int s = unit % a.max_splits;
+  const int kvh = (unit / a.max_splits) % a.Hkv;
+  const int b = unit / a.max_splits / a.Hkv;
+  const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int S = split_len(a.policy, a.split_tokens, n, a.B);
+  const int nsplit = (n + S - 1) / S;
+  if (s >= nsplit) return;  // uniform over the workgroup
+  const int p = n - 1;
+  const bool row_ok = r < a.group;
+  const int limit = row_ok ? p : -1;
+  const int hq = kvh * a.group + (row_ok ? r : 0);
+  const QFrag<D> q = load_q<D>(a.q + ((size_t)b * a.Hq + hq) * D, row_ok, g);
+  float c = a.c;
+  if constexpr (FP8) c = c * a.k_scale[kvh];
+
+  const int k_begin = s * S;
+  const int k_end = min(k_begin + S, n);
+  const int ntiles = (k_end - k_begin + kTileKeys - 1) / kTileKeys;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  const int nblk = (n + 15) >> 4;
+
+  float m = neg_inf(), z = 0.f;
+  f32x4 u[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The split's block-table entries are staged in LDS, kBtWindowTiles tiles
+  // at a time, so page lookups never wait on the memory loads in flight.
+  const int tid = threadIdx.x;
+  const uint8_t* kc = a.k_cache;
+  const uint8_t* vc = a.v_cache;
+  const int np = a.num_pages;
+  DecodeFrags<D, FP8> fa, fb;
+  for (int w0 = 0; w0 < ntiles; w0 += kBtWindowTiles) {
+    const int wn = min(ntiles - w0, kBtWindowTiles);
+    __syncthreads();
+    const int e0 = (k_begin >> 4) + 4 * w0;
+    for (int i = tid; i < 4 * wn; i += 64 * kDecodeWaves) {
+      const int e = e0 + i < nblk ? e0 + i : nblk - 1;
+      bt_lds[i] = bt_row[e];
+    }
+    __syncthreads();
+
+    // Software pipeline over the window's tiles, unrolled by two so no
+    // register set is ever copied: while tile lt computes from one fragment
+    // set, tile lt+1 loads into the other.  A tile index past the window
+    // clamps to its last tile (a re-read that hits the cache), so every load
+    // is unconditional and a wait for one tile's operands never drains the
+    // next tile's loads.
+    const int last = wn - 1;
+    auto load = [&](DecodeFrags<D, FP8>& f, int lt) {
+      lt = lt < last ? lt : last;
+      const int4 e = *reinterpret_cast<const int4*>(&bt_lds[4 * lt]);
+      const int4 eu = make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                                __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+      load_decode_frags<D, FP8>(f, kc, vc, eu, k_begin + kTileKeys * (w0 + lt), n, np, kvh, a.Hkv, w, r, g);
+    };
+    load(fa, 0);
+    for (int lt = 0; lt < wn; lt += 2) {
+      load(fb, lt + 1);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting on this tile
+      decode_tile<D, FP8>(fa, q, xs[0], m, z, u, c, k_begin + kTileKeys * (w0 + lt), limit, w, lane, r, g);
+      if (lt + 1 >= wn) break;
+      load(fa, lt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_tile<D, FP8>(fb, q, xs[1], m, z, u, c, k_begin + kTileKeys * (w0 + lt + 1), limit, w, lane, r, g);
+    }
+  }
+
+  if (row_ok) {
+    const size_t row = ((size_t)b * a.max_splits + s) * a.Hq + hq;
+    float* uo = a.ws_u + row * D;
+#pragma unroll
+    for (int mbi = 0; mbi < MB; ++mbi) *reinterpret_cast<f32x4*>(uo + 16 * (w * MB + mbi) + 4 * g) = u[mbi];
+    if (w == 0 && g == 0) *reinterpret_cast<f32x2*>(a.ws_ml + row * 2) = f32x2{m, z};
+  }
+}
+
+// One wave per (sequence, query head): folds the split partials in ascending
+// split order and writes the bf16 output row.
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kPer = D / 64;
+  const int lane = threadIdx.x;
+  const int hq = blockIdx.x % a.Hq;
+  const int b = blockIdx.x / a.Hq;
+  const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int S = split_len(a.policy, a.split_tokens, n, a.B);
+  const int nsplit = n > 0 ? (n + S - 1) / S : 0;
+  __bf16* out = a.out + ((size_t)b * a.Hq + hq) * D + kPer * lane;
+  if (nsplit == 0) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) out[k] = (__bf16)0.f;
+    return;
+  }
+  const size_t row0 = (size_t)b * a.max_splits * a.Hq + hq;
+  const f32x2 ml0 = *reinterpret_cast<const f32x2*>(a.ws_ml + row0 * 2);
+  float M = ml0[0], Z = ml0[1];
+  float U[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) U[k] = a.ws_u[row0 * D + kPer * lane + k];
+  for (int s = 1; s < nsplit; ++s) {
+    const size_t row = row0 + (size_t)s * a.Hq;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + row * 2);
+    float wa, wb;
+    merge_scalars(M, Z, ml[0], ml[1], wa, wb);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) U[k] = merge_value(U[k], a.ws_u[row * D + kPer * lane + k], wa, wb);
+  }
+  const float rz = final_rz(Z);
+  const float vs = FP8 ? a.v_scale[hq / a.group] : 1.0f;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) out[k] = finalize(U[k], vs, rz);
+}
+
+template <int D, bool FP8>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  const int64_t units = (int64_t)a.B * a.Hkv * a.max_splits;
+  hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, FP8>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int D, bool fp8, const DecodeArgs& a, hipStream_t st) {
+  if (D == 128 && fp8) return launch_decode_t<128, true>(a, st);
+  if (D == 128) return launch_decode_t<128, false>(a, st);
+  if (D == 64 && fp8) return launch_decode_t<64, true>(a, st);
+  if (D == 64) return launch_decode_t<64, false>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ia

@@ -58,5 +58,8 @@ struct PrefillArgs {
 hipError_t launch_kv_append(int D, bool fp8, const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(int D, bool fp8, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st);
+// Query positions one prefill workgroup covers (its grid has
+// ceil(max_q_len / this) row blocks per (sequence, kv head)).
+int prefill_positions_per_block(int group);
 
 }  // namespace ia

@@ -1,0 +1,146 @@
+// pages.hpp -- paged K/V addressing and loads shared by the attention kernels.
+// Data movement only: nothing here changes a value except the zero fill of
+// keys that do not exist (Vosti App. A.2: out-of-range loads are
+// zero-padded).
+//
+// Page layout (page size 16, one page = one 16-key MFMA block):
+//   K: [num_pages][Hkv][D/8][16][8]   a 16-byte chunk = 8 dims of one token
+//   V: [num_pages][Hkv][D][16]        the 16 tokens of one dim are contiguous
+// Key j of a sequence lives in page block_table[j / 16], token j % 16 (Vosti
+// App. A.1: K_X[j] = K_phys[pi(floor(j / P)), j mod P]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arith.hpp"
+
+namespace ia {
+
+// ---------------------------------------------------------------- raw types
+
+// Raw page words of one K chunk (8 dims of one token) and of one V quad
+// (4 tokens of one dim): bf16 bits, or e4m3 codes.
+template <bool FP8>
+struct Raw;
+template <>
+struct Raw<false> {
+  using K = uint4;
+  using V = uint2;
+  static constexpr int kElemBytes = 2;
+};
+template <>
+struct Raw<true> {
+  using K = uint2;
+  using V = uint32_t;
+  static constexpr int kElemBytes = 1;
+};
+
+template <bool FP8>
+__device__ __forceinline__ typename Raw<FP8>::K load_k_raw(const uint8_t* base, size_t elem) {
+  return *reinterpret_cast<const typename Raw<FP8>::K*>(base + elem * Raw<FP8>::kElemBytes);
+}
+template <bool FP8>
+__device__ __forceinline__ typename Raw<FP8>::V load_v_raw(const uint8_t* base, size_t elem) {
+  return *reinterpret_cast<const typename Raw<FP8>::V*>(base + elem * Raw<FP8>::kElemBytes);
+}
+
+// K chunk -> bf16x8; `keep` false gives +0 (a token that is not a key).
+__device__ __forceinline__ bf16x8 k_to_bf16(uint4 w, bool keep) {
+  w.x = keep ? w.x : 0u;
+  w.y = keep ? w.y : 0u;
+  w.z = keep ? w.z : 0u;
+  w.w = keep ? w.w : 0u;
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ bf16x8 k_to_bf16(uint2 w, bool keep) {
+  w.x = keep ? w.x : 0u;
+  w.y = keep ? w.y : 0u;
+  const bf16x2 a = fp8x2_to_bf16(w.x, false), b = fp8x2_to_bf16(w.x, true);
+  const bf16x2 c = fp8x2_to_bf16(w.y, false), d = fp8x2_to_bf16(w.y, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// V quad -> bf16x4; only the first nv of the 4 tokens are keys (nv may be
+// <= 0 or >= 4), the rest become +0.
+__device__ __forceinline__ bf16x4 v_to_bf16(uint2 w, int nv) {
+  w.x = nv >= 2 ? w.x : (nv == 1 ? (w.x & 0xFFFFu) : 0u);
+  w.y = nv >= 4 ? w.y : (nv == 3 ? (w.y & 0xFFFFu) : 0u);
+  return __builtin_bit_cast(bf16x4, w);
+}
+__device__ __forceinline__ bf16x4 v_to_bf16(uint32_t w, int nv) {
+  w = nv >= 4 ? w : (nv <= 0 ? 0u : (w & ((1u << (8 * nv)) - 1u)));
+  const bf16x2 a = fp8x2_to_bf16(w, false), b = fp8x2_to_bf16(w, true);
+  bf16x4 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  return r;
+}
+
+// Element offsets inside a page pool.
+template <int D>
+__device__ __forceinline__ size_t k_elem(int page, int kvh, int Hkv, int chunk, int tok) {
+  return ((((size_t)page * Hkv + kvh) * (D / 8) + chunk) * 16 + tok) * 8;
+}
+template <int D>
+__device__ __forceinline__ size_t v_elem(int page, int kvh, int Hkv, int dim, int tok) {
+  return (((size_t)page * Hkv + kvh) * D + dim) * 16 + tok;
+}
+
+// ------------------------------------------------------------ block table
+
+struct TilePages {
+  int page[4];
+  int valid[4];
+};
+
+// Page and key count of the 16-key block starting at key k0 whose
+// block-table entry is e.  A block without keys, or whose page id is out of
+// range, is marked empty (valid = 0) and addressed at page 0, so every load
+// stays in bounds.
+__device__ __forceinline__ void block_page(int e, int k0, int n, int num_pages, int& pg, int& v) {
+  v = n - k0;
+  v = v < 0 ? 0 : (v > 16 ? 16 : v);
+  pg = e;
+  if (v == 0 || pg < 0 || pg >= num_pages) {
+    pg = 0;
+    v = 0;
+  }
+}
+
+// The 4 blocks of the tile starting at key t0, from their entries.
+__device__ __forceinline__ TilePages tile_pages_of(const int4& e, int t0, int n, int num_pages) {
+  TilePages tp;
+  block_page(e.x, t0, n, num_pages, tp.page[0], tp.valid[0]);
+  block_page(e.y, t0 + 16, n, num_pages, tp.page[1], tp.valid[1]);
+  block_page(e.z, t0 + 32, n, num_pages, tp.page[2], tp.valid[2]);
+  block_page(e.w, t0 + 48, n, num_pages, tp.page[3], tp.valid[3]);
+  return tp;
+}
+
+// Block-table entry of block (lane & 3) of the tile starting at key t0, for
+// one lane; the index is clamped to the sequence's last block so the load is
+// in bounds and unconditional (blocks past the last one hold no keys and
+// never use their entry).
+__device__ __forceinline__ int load_tile_bt(const int32_t* bt_row, int t0, int nblk, int lane) {
+  int e = (t0 >> 4) + (lane & 3);
+  e = e < nblk ? e : nblk - 1;
+  return bt_row[e];
+}
+
+__device__ __forceinline__ int clamp_len(int n, int max_len) { return n < 0 ? 0 : (n > max_len ? max_len : n); }
+
+template <int D>
+__device__ __forceinline__ QFrag<D> load_q(const __bf16* qrow, bool ok, int g) {
+  QFrag<D> q;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+    q.f[ks] = k_to_bf16(w, ok);
+  }
+  return q;
+}
+
+}  // namespace ia
