@@ -2,24 +2,38 @@
 """Benchmark: batch-invariant paged-attention decode on one MI355X.
 
 A step is one decode step of the Llama-3-8B-shaped workload (32 query / 8 KV heads, head_dim
-128, bf16 pages of 16 tokens, fixed 2048-token splits, contexts uniform in [512, 8192]): the
-step's new K/V rows are written into their page slots (kv_append) and every sequence's query
-row attends its whole paged context (decode split kernel + ascending split merge).  The timed
-region starts with every input resident in HBM.
+128, bf16 pages of 16 tokens, fixed 2048-token splits, contexts uniform in [512, 8192], batch
+256): the step's new K/V rows are written into their page slots (kv_append) and every
+sequence's query row attends its whole paged context (decode split kernel + ascending split
+merge).  The timed region starts with every input resident in HBM.
 
-`value` is decode KV-read throughput at batch 256: the algorithmic KV bytes of the step
-(sum_b n_b * Hkv * d * 2 tensors * 2 bytes -- each sequence's K and V read once per KV head)
-divided by the step time.  The JSON line also carries the roofline of the decode kernels
-(their own duration, from HIP events on the launch stream), the batch sizes 1/8/64, the
-split-by-count comparison variant (the cost of invariance), a bitwise invariance rate measured
-in the same run, prefill TFLOP/s, and the fp64 CPU oracle timed on a bounded sample.
+`value` is decode KV-read throughput: the algorithmic KV bytes of a step (sum_b n_b * Hkv * d *
+2 tensors * 2 bytes -- each sequence's K and V read once per KV head) divided by the step time
+(K steps timed between two device synchronisations).  The JSON line also carries the roofline of
+the decode call (its own duration from HIP events on the launch stream), batch sizes 1/8/64,
+the split-by-count comparison variant (the cost of invariance), a bitwise invariance rate
+measured in the same run, whole-prefill TFLOP/s, a plain device copy as the achievable-bandwidth
+reference, and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py --decode-only ...   headline decode only (for profilers)
+    python bench.py --copy-probe        a plain copy of known size (counter calibration)
+    python bench.py --suite             also the long-context, mixed and shared-prefix workloads
+    python bench.py --summarize-profile TRACE_DIR PMC_DIR   write the profile summary under profiles/
+
+The roofline's `traffic` (HBM bytes per launch of the decode split kernel) comes from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters, each scaled by what the same counter reads for a plain 1 GiB
+device copy; the figures live in profiles/ with the source hash of the kernel they were taken on,
+and `traffic` is null whenever the kernel's sources have changed since.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
+import math
 import os
 import subprocess
 import sys
@@ -38,6 +52,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 DEV = "cuda"
 SEED = 0
+COPY_PROBE_BYTES = 1 << 30
+PROFILE_MD = os.path.join(ROOT, "profiles", "decode_split_kernel_llama3-8b_b256.md")
+KERNEL_SOURCES = ["decode.hip", "arith.hpp", "pages.hpp", "launch.hpp"]
 
 
 def log(*a):
@@ -62,27 +79,154 @@ def cpu_model():
     return None
 
 
-class DecodeWorld:
-    """The decode workload resident on the GPU: pages, tables, queries, new-token rows, slots."""
+def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the decode kernel's sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "invariant_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
-    def __init__(self, shape: wl.AttnShape, lens, fp8=False):
+
+def recorded_traffic():
+    """HBM bytes per decode_split_kernel launch recorded in profiles/, if taken on these sources."""
+    try:
+        text = open(PROFILE_MD).read()
+    except OSError:
+        return None
+    rec = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_record:"):
+            rec = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
+    if rec.get("source_sha") != kernel_source_hash():
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def _csv_rows(pattern):
+    rows = []
+    for path in glob.glob(pattern, recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_profile(trace_dir, pmc_dir):
+    """Writes the decode profile summary (rocprofv3 kernel-trace stats + calibrated FETCH/WRITE)."""
+    stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    split = [r for r in stats if "decode_split_kernel<128, false>" in r["Name"]]
+    merge = [r for r in stats if "decode_merge_kernel<128, false>" in r["Name"]]
+    avg_ns = float(split[0]["AverageNs"])
+
+    def pmc_mean(kind, counter, kernel):
+        rows = _csv_rows(os.path.join(pmc_dir, f"pmc_{kind}_{counter}", "**", "*counter_collection.csv"))
+        vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return float(np.mean(vals)), len(vals)
+
+    fetch_kib, nf = pmc_mean("decode", "FETCH_SIZE", "decode_split_kernel<128, false>")
+    write_kib, nw = pmc_mean("decode", "WRITE_SIZE", "decode_split_kernel<128, false>")
+    copy_fetch, _ = pmc_mean("copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    copy_write, _ = pmc_mean("copy", "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    f_scale = COPY_PROBE_BYTES / (copy_fetch * 1024)
+    w_scale = COPY_PROBE_BYTES / (copy_write * 1024)
+    fetch_b = fetch_kib * 1024 * f_scale
+    write_b = write_kib * 1024 * w_scale
+    lens = wl.uniform_lens(SEED, 256, 512, 8192)
+    alg = int(sum(lens)) * 8 * 128 * 2 * 2
+    tr = int(round(fetch_b + write_b))
+    cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o decode -- "
+                 "python3 bench.py --decode-only --steps 10 --warmup 3 --no-cpu-baseline")
+    cmd_pmc = ("rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- "
+               "python3 bench.py --decode-only --steps 3 --warmup 1 --no-cpu-baseline")
+    cmd_copy = "rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- python3 bench.py --copy-probe --steps 3"
+    lines = [
+        "# decode_split_kernel<128, bf16> -- Llama-3-8B-shaped decode, batch 256, contexts U[512, 8192]",
+        "",
+        "32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits, "
+        f"{int(sum(lens))} context tokens; algorithmic KV bytes per launch {alg} "
+        "(sum_b n_b x 8 heads x 128 dims x 2 tensors x 2 bytes).",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)",
+        "",
+        f"    {cmd_trace}",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+    ]
+    for r in split + merge:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    lines += [
+        "",
+        f"Achieved from the trace: {alg / avg_ns:.1f} GB/s = {alg / avg_ns / HBM_PEAK_GBS:.4f} of the 8 TB/s HBM peak "
+        "(split kernel alone; the split merge adds about 6 us per call).",
+        "",
+        "## HBM traffic (rocprofv3 --pmc, one counter per run)",
+        "",
+        f"    {cmd_pmc.format(C='FETCH_SIZE')}",
+        f"    {cmd_pmc.format(C='WRITE_SIZE')}",
+        f"    {cmd_copy.format(C='FETCH_SIZE')}",
+        f"    {cmd_copy.format(C='WRITE_SIZE')}",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| FETCH_SIZE per decode_split_kernel dispatch (KiB, mean of {nf}) | {fetch_kib:.1f} |",
+        f"| WRITE_SIZE per decode_split_kernel dispatch (KiB, mean of {nw}) | {write_kib:.1f} |",
+        f"| FETCH_SIZE of a 1 GiB device copy (KiB) | {copy_fetch:.1f} |",
+        f"| WRITE_SIZE of a 1 GiB device copy (KiB) | {copy_write:.1f} |",
+        f"| fetch scale (bytes read / counter bytes) | {f_scale:.4f} |",
+        f"| write scale | {w_scale:.4f} |",
+        f"| HBM bytes read per launch | {fetch_b:.4e} |",
+        f"| HBM bytes written per launch | {write_b:.4e} |",
+        f"| traffic / algorithmic bytes | {tr / alg:.4f} |",
+        "",
+        f"traffic_record: source_sha={kernel_source_hash()} bytes_per_launch={tr} read={int(fetch_b)} "
+        f"write={int(write_b)} algorithmic={alg}",
+        "",
+    ]
+    os.makedirs(os.path.dirname(PROFILE_MD), exist_ok=True)
+    with open(PROFILE_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(PROFILE_MD)
+
+
+def make_ctx(shape, by_count=False, fp8=False):
+    return ia.Context(ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P, split_tokens=shape.S,
+                                     kv_dtype=ia.IA_KV_FP8_E4M3 if fp8 else ia.IA_KV_BF16,
+                                     split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
+                                     sm_scale=shape.scale))
+
+
+class DecodeWorld:
+    """A decode workload resident on the GPU: pages, tables, queries, new-token rows, slots."""
+
+    def __init__(self, shape: wl.AttnShape, lens, fp8=False, shared_prefix=0, width=None, scales=None):
         self.shape = shape
         self.lens = [int(n) for n in lens]
         self.B = len(self.lens)
-        self.seqs = wl.make_sequences(self.lens)
-        self.layout = wl.layout_pages(3, self.lens, shape.P)
-        self.ctx = make_ctx(shape)
+        self.fp8 = fp8
+        self.seqs = wl.make_sequences(self.lens, shared_prefix=shared_prefix)
+        self.layout = wl.layout_pages(3, self.lens, shape.P, shared_prefix=shared_prefix, width=width)
+        self.ctx = make_ctx(shape, fp8=fp8)
         dt = torch.uint8 if fp8 else torch.bfloat16
         npg = self.layout.num_pages
         self.k = torch.zeros((npg, shape.Hkv, shape.d // 8, shape.P, 8), dtype=dt, device=DEV)
         self.v = torch.zeros((npg, shape.Hkv, shape.d, shape.P), dtype=dt, device=DEV)
+        if fp8:
+            ks, vs = scales if scales is not None else wl.fp8_scales(2, shape.Hkv, power_of_two=False)
+            self.k_scale = torch.as_tensor(ks, device=DEV)
+            self.v_scale = torch.as_tensor(vs, device=DEV)
+        else:
+            self.k_scale = self.v_scale = None
         t0 = time.time()
         qs, knew, vnew, slots = [], [], [], []
+        n_shared = shared_prefix // shape.P
         for b, s in enumerate(self.seqs):
-            kr = s.k(SEED, shape)
-            vr = s.v(SEED, shape)
-            sl = torch.as_tensor(self.layout.slots(b, 0, s.n, shape.P), device=DEV)
-            ia.ia_kv_append(self.ctx, kr.to(DEV), vr.to(DEV), sl, self.k, self.v)
+            # Shared prefix pages are written once (by the first sequence), as a prefix cache would.
+            p0 = 0 if b == 0 else min(s.n, n_shared * shape.P)
+            kr = s.k(SEED, shape, p0, s.n)
+            vr = s.v(SEED, shape, p0, s.n)
+            sl = torch.as_tensor(self.layout.slots(b, p0, s.n, shape.P), device=DEV)
+            ia.ia_kv_append(self.ctx, kr.to(DEV), vr.to(DEV), sl, self.k, self.v, self.k_scale, self.v_scale)
             qs.append(s.q(SEED, shape, s.n - 1, s.n))
             knew.append(kr[-1:])
             vnew.append(vr[-1:])
@@ -95,110 +239,114 @@ class DecodeWorld:
         self.slots = torch.as_tensor(np.concatenate(slots), device=DEV)
         self.bt = torch.as_tensor(self.layout.block_table, device=DEV)
         self.seq_lens = torch.as_tensor(np.array(self.lens, np.int32), device=DEV)
-        self.max_len = max(self.lens)
+        self.distinct_pages = len(set(np.concatenate(self.layout.pages).tolist()))
 
     def kv_bytes(self, idx=None) -> int:
+        """Algorithmic (logical) KV bytes: every sequence reads its whole context once per KV head."""
         lens = self.lens if idx is None else [self.lens[i] for i in idx]
-        return int(sum(lens)) * self.shape.Hkv * self.shape.d * 2 * 2
-
-
-def make_ctx(shape, by_count=False):
-    return ia.Context(ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P, split_tokens=shape.S,
-                                     split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
-                                     sm_scale=shape.scale))
+        return int(sum(lens)) * self.shape.Hkv * self.shape.d * 2 * (1 if self.fp8 else 2)
 
 
 class DecodeRunner:
-    """One batch (a prefix of the world's sequences) ready to step."""
+    """One batch (a subset of the world's sequences) ready to step."""
 
-    def __init__(self, world: DecodeWorld, B: int, ctx=None):
+    def __init__(self, world: DecodeWorld, idx, ctx=None):
         self.w = world
-        self.B = B
+        idx = list(idx)
+        self.idx = idx
+        self.B = len(idx)
         self.ctx = world.ctx if ctx is None else ctx
-        self.q = world.q[:B].contiguous()
-        self.bt = world.bt[:B].contiguous()
-        self.sl = world.seq_lens[:B].contiguous()
-        self.k_new = world.k_new[:B].contiguous()
-        self.v_new = world.v_new[:B].contiguous()
-        self.slots = world.slots[:B].contiguous()
-        self.max_len = max(world.lens[:B])
-        self.out = torch.empty((B, world.shape.Hq, world.shape.d), dtype=torch.bfloat16, device=DEV)
-        nb = ia.ia_decode_workspace_bytes(self.ctx, B, self.max_len)
+        ii = torch.as_tensor(idx, device=DEV)
+        self.q = world.q[ii].contiguous()
+        self.bt = world.bt[ii].contiguous()
+        self.sl = world.seq_lens[ii].contiguous()
+        self.k_new = world.k_new[ii].contiguous()
+        self.v_new = world.v_new[ii].contiguous()
+        self.slots = world.slots[ii].contiguous()
+        self.max_len = max(world.lens[i] for i in idx)
+        self.out = torch.empty((self.B, world.shape.Hq, world.shape.d), dtype=torch.bfloat16, device=DEV)
+        nb = ia.ia_decode_workspace_bytes(self.ctx, self.B, self.max_len)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
 
     def append(self, stream):
-        ia.ia_kv_append(self.ctx, self.k_new, self.v_new, self.slots, self.w.k, self.w.v, stream=stream)
+        ia.ia_kv_append(self.ctx, self.k_new, self.v_new, self.slots, self.w.k, self.w.v, self.w.k_scale,
+                        self.w.v_scale, stream=stream)
 
     def decode(self, stream):
         ia.ia_paged_attn_decode(self.ctx, self.q, self.w.k, self.w.v, self.bt, self.sl, self.max_len, self.out,
-                                self.ws, stream=stream)
+                                self.ws, self.w.k_scale, self.w.v_scale, stream=stream)
 
 
-def time_steps(runner: DecodeRunner, steps: int, warmup: int):
-    """Times `steps` steps (kv_append + decode).  Returns (step ms, decode-kernels ms) medians."""
+def time_steps(runner: DecodeRunner, steps: int, warmup: int, with_append=True):
+    """Times `steps` steps.  Returns (ms per step over the whole timed region, mean ms of the decode
+    call alone).  All work goes to torch's current stream, which the events are recorded on."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        runner.append(stream)
+        if with_append:
+            runner.append(stream)
         runner.decode(stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        runner.append(stream)
+    start.record(stream)
+    for e1, e2 in ev:
+        if with_append:
+            runner.append(stream)
         e1.record(stream)
         runner.decode(stream)
         e2.record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    step_ms = [e0.elapsed_time(e2) for e0, _, e2 in ev]
-    dec_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
-    return float(np.median(step_ms)), float(np.median(dec_ms)), wall
+    step_ms = start.elapsed_time(end) / steps
+    dec_ms = float(np.mean([e1.elapsed_time(e2) for e1, e2 in ev]))
+    return step_ms, dec_ms
 
 
 def invariance_pairs(world: DecodeWorld, ctx, probes):
-    """Bitwise comparisons of output rows across batch compositions: batch B vs alone, vs the
-    first 8 and first 64, and vs the reversed batch.  Returns (equal, compared)."""
+    """Bitwise comparisons of output rows across batch compositions: the full batch against each
+    probe alone, the first 8, the first 64 and the reversed batch.  Returns (equal, compared)."""
     B = world.B
-    full = DecodeRunner(world, B, ctx)
+    full = DecodeRunner(world, range(B), ctx)
     full.decode(None)
     ref = full.out.clone()
     eq = tot = 0
 
-    def rows(idx):
-        r = DecodeRunner.__new__(DecodeRunner)
-        r.w, r.B, r.ctx = world, len(idx), ctx
-        ii = torch.as_tensor(idx, device=DEV)
-        r.q = world.q[ii].contiguous()
-        r.bt = world.bt[ii].contiguous()
-        r.sl = world.seq_lens[ii].contiguous()
-        r.max_len = max(world.lens[i] for i in idx)
-        r.out = torch.empty((len(idx), world.shape.Hq, world.shape.d), dtype=torch.bfloat16, device=DEV)
-        r.ws = torch.empty(ia.ia_decode_workspace_bytes(ctx, len(idx), r.max_len), dtype=torch.uint8, device=DEV)
-        r.decode(None)
-        return r.out
-
-    def cmp(out, idx):
+    def cmp(idx):
         nonlocal eq, tot
-        a = out.view(torch.int16).cpu().numpy().reshape(len(idx), -1)
+        r = DecodeRunner(world, idx, ctx)
+        r.decode(None)
+        a = r.out.view(torch.int16).cpu().numpy().reshape(len(idx), -1)
         b = ref[torch.as_tensor(idx, device=DEV)].view(torch.int16).cpu().numpy().reshape(len(idx), -1)
-        same = (a == b).all(axis=1)
-        eq += int(same.sum())
+        eq += int((a == b).all(axis=1).sum())
         tot += len(idx)
 
     for p in probes:
-        cmp(rows([p]), [p])
+        cmp([p])
     for sub in (list(range(8)), list(range(64))):
-        cmp(rows(sub), sub)
-    rev = list(reversed(range(B)))
-    cmp(rows(rev), rev)
+        cmp(sub)
+    cmp(list(reversed(range(B))))
     return eq, tot
 
 
+def copy_gbs(nbytes=COPY_PROBE_BYTES, reps=10):
+    """A plain device copy (torch's copy kernel) of nbytes: read + write bytes / time."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=DEV).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 4), "gbs": round(2 * nbytes / ms / 1e6, 1)}
+
+
 def prefill_tflops(steps: int, warmup: int):
-    """Whole prefill of 8 prompts x 4096 tokens (Qwen3-8B shape); flops = 4 d sum_rows (p+1) Hq."""
+    """Whole prefill of 8 prompts x 4096 tokens (Qwen3-8B shape); flops = 4 d Hq sum_rows (p+1)."""
     shape = wl.QWEN3_8B
     lens = [4096] * 8
     seqs = wl.make_sequences(lens, first_sid=1000)
@@ -232,18 +380,19 @@ def prefill_tflops(steps: int, warmup: int):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     flops = 4.0 * shape.d * shape.Hq * sum(n * (n + 1) / 2 for n in lens)
-    return {"workload": "qwen3-8b-prefill-8x4096", "ms": ms, "tflops": flops / ms / 1e9,
-            "frac_of_bf16_peak": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
+    return {"workload": "qwen3-8b-shaped whole prefill, 8 x 4096 tokens, causal", "ms": round(ms, 4),
+            "tflops": round(flops / ms / 1e9, 1), "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": flops}
 
 
-def cpu_baseline(world: DecodeWorld, sample: int = 8):
-    """The fp64 oracle (as it stands) on `sample` sequences of the batch, all heads, on the host."""
+def cpu_baseline(lens, shape, target_s=10.0, sample=32):
+    """The fp64 oracle, as it stands, on a bounded sample of the headline workload: the first
+    `sample` sequences' decode rows (all query heads), on all host threads, repeated until about
+    target_s seconds of CPU time.  Its inputs come from the oracle's own page scatter."""
     from oracle import oracle
-    shape = world.shape
     oracle.build(force=False)
-    idx = list(range(sample))
-    seqs = [world.seqs[i] for i in idx]
-    lens = [s.n for s in seqs]
+    lens = [int(n) for n in lens[:sample]]
+    seqs = wl.make_sequences(lens)
     layout = wl.layout_pages(9, lens, shape.P)
     kshape, vshape = oracle.kv_cache_shapes(layout.num_pages, shape.Hkv, shape.d, shape.P)
     kc, vc = np.zeros(kshape, np.uint16), np.zeros(vshape, np.uint16)
@@ -254,14 +403,56 @@ def cpu_baseline(world: DecodeWorld, sample: int = 8):
     q = torch.cat([s.q(SEED, shape, s.n - 1, s.n) for s in seqs]).view(torch.int16).numpy().view(np.uint16)
     cu = np.arange(sample + 1, dtype=np.int32)
     threads = oracle.max_threads()
+
+    def once():
+        oracle.paged_attention(q, cu, np.array(lens, np.int32), kc, vc, layout.block_table, Hq=shape.Hq,
+                               Hkv=shape.Hkv, d=shape.d, P=shape.P, scale=shape.scale, nthreads=threads)
+
     t0 = time.perf_counter()
-    oracle.paged_attention(q, cu, np.array(lens, np.int32), kc, vc, layout.block_table, Hq=shape.Hq,
-                           Hkv=shape.Hkv, d=shape.d, P=shape.P, scale=shape.scale, nthreads=threads)
-    dt = time.perf_counter() - t0
-    gbs = world.kv_bytes(idx) / dt / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sample} of the batch-256 sequences ({sum(lens)} tokens, all 32 query heads), "
-                      f"decode rows, fp64, {dt:.2f} s", "cpu": cpu_model()}
+    once()
+    t1 = time.perf_counter() - t0
+    reps = max(1, min(200, int(math.ceil(target_s / max(t1, 1e-3)))) - 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once()
+    dt = time.perf_counter() - t0 if reps else t1
+    reps = max(reps, 1)
+    kvb = int(sum(lens)) * shape.Hkv * shape.d * 2 * 2
+    return {"value": round(kvb * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample} of the batch-256 sequences ({sum(lens)} tokens), their decode rows over "
+                      f"all 32 query heads in fp64, {reps} passes in {dt:.1f} s",
+            "cpu": cpu_model()}
+
+
+def suite(args):
+    """Long-context (Qwen3-235B shape), mixed-batch and shared-prefix (Llama-3.1-70B shape, bf16 and
+    fp8) decode points, each timed alone."""
+    out = {}
+    # 16 decode rows at 32768 context + batch 1 vs 64.
+    shape = wl.QWEN3_235B
+    w = DecodeWorld(shape, [32768] * 64)
+    for B in (1, 16, 64):
+        s_ms, d_ms = time_steps(DecodeRunner(w, range(B)), args.steps, args.warmup, with_append=False)
+        out[f"qwen3-235b-32k-B{B}"] = {"decode_ms": round(d_ms, 4),
+                                       "gbs": round(w.kv_bytes(range(B)) / d_ms / 1e6, 1)}
+        log(f"qwen3-235b 32k B={B}: {out[f'qwen3-235b-32k-B{B}']}")
+    del w
+    torch.cuda.empty_cache()
+    # 128 sequences sharing a 16384-token prefix + private suffixes of 256-4096.
+    shape = wl.LLAMA31_70B
+    rng = np.random.default_rng([SEED, 5])
+    lens = [16384 + int(x) for x in rng.integers(256, 4097, 128)]
+    for fp8 in (False, True):
+        w = DecodeWorld(shape, lens, fp8=fp8, shared_prefix=16384, width=8192)
+        s_ms, d_ms = time_steps(DecodeRunner(w, range(128)), args.steps, args.warmup, with_append=False)
+        bpt = shape.Hkv * shape.d * 2 * (1 if fp8 else 2)
+        key = f"llama70b-shared-prefix-{'fp8' if fp8 else 'bf16'}"
+        out[key] = {"decode_ms": round(d_ms, 4), "logical_gbs": round(w.kv_bytes() / d_ms / 1e6, 1),
+                    "distinct_page_gbs": round(w.distinct_pages * shape.P * bpt / d_ms / 1e6, 1)}
+        log(f"{key}: {out[key]}")
+        del w
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -271,70 +462,84 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--decode-only", action="store_true", help="time the headline batch only (for profilers)")
+    ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--suite", action="store_true", help="also time the long-context and shared-prefix points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
+        print("bench.py: this build measures one GPU only; there is no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ia.load()
+    if args.copy_probe:
+        print(json.dumps({"copy_probe": copy_gbs(reps=args.steps)}), flush=True)
+        return
     shape = wl.LLAMA3_8B
     lens = wl.uniform_lens(SEED, args.batch, 512, 8192)
     log(f"decode workload: llama3-8b shape, B={args.batch}, {sum(lens)} tokens")
     world = DecodeWorld(shape, lens)
-    head = DecodeRunner(world, args.batch)
-    step_ms, dec_ms, wall_ms = time_steps(head, args.steps, args.warmup)
+    head = DecodeRunner(world, range(args.batch))
+    torch.cuda.synchronize()
+    step_ms, dec_ms = time_steps(head, args.steps, args.warmup)
     kvb = world.kv_bytes()
     value = kvb / (step_ms * 1e-3) / 1e9
     dec_gbs = kvb / (dec_ms * 1e-3) / 1e9
-    log(f"B={args.batch}: step {step_ms:.3f} ms ({value:.0f} GB/s), decode kernels {dec_ms:.3f} ms "
-        f"({dec_gbs:.0f} GB/s), host wall {wall_ms:.3f} ms/step")
+    log(f"B={args.batch}: step {step_ms:.4f} ms ({value:.0f} GB/s), decode call {dec_ms:.4f} ms ({dec_gbs:.0f} GB/s)")
     result = {
         "metric": "batch-invariant paged-attn decode KV GB/s (% HBM peak) + bitwise invariance rate",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama3-8b-shaped decode (kv_append + decode)", "batch": args.batch,
-                   "q_heads": shape.Hq, "kv_heads": shape.Hkv, "head_dim": shape.d, "page_size": shape.P,
-                   "split_tokens": shape.S, "context": "uniform [512, 8192]", "tokens": int(sum(lens)),
-                   "kv_dtype": "bf16"},
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/Q, random page placement)",
+        "config": {"workload": "llama3-8b-shaped paged decode step (kv_append + decode), batch 256, "
+                               "contexts uniform in [512, 8192]",
+                   "batch": args.batch, "q_heads": shape.Hq, "kv_heads": shape.Hkv, "head_dim": shape.d,
+                   "page_size": shape.P, "split_tokens": shape.S, "tokens": int(sum(lens)), "kv_dtype": "bf16"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "decode_split_kernel + decode_merge_kernel (one ia_paged_attn_decode call)",
+        "roofline": {"kernel": "decode_split_kernel (with its split merge: one ia_paged_attn_decode call)",
                      "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes_per_launch": kvb, "avg_launch_ms": round(dec_ms, 4)},
     }
     if not args.decode_only:
-        batches = {}
-        by_count = {}
+        result["copy_reference"] = copy_gbs()
+        log(f"plain copy: {result['copy_reference']}")
+        batches, by_count = {}, {}
         bc_ctx = make_ctx(shape, by_count=True)
         for B in (1, 8, 64, args.batch):
-            r = DecodeRunner(world, B)
-            s_ms, d_ms, _ = time_steps(r, args.steps, args.warmup)
+            s_ms, d_ms = time_steps(DecodeRunner(world, range(B)), args.steps, args.warmup)
             kb = world.kv_bytes(range(B))
             batches[str(B)] = {"step_ms": round(s_ms, 4), "decode_ms": round(d_ms, 4),
                                "gbs": round(kb / (s_ms * 1e-3) / 1e9, 1)}
-            rc = DecodeRunner(world, B, bc_ctx)
-            s2, d2, _ = time_steps(rc, args.steps, args.warmup)
+            s2, d2 = time_steps(DecodeRunner(world, range(B), bc_ctx), args.steps, args.warmup)
             by_count[str(B)] = {"step_ms": round(s2, 4), "gbs": round(kb / (s2 * 1e-3) / 1e9, 1),
-                                "fixed_over_by_count": round(s2 / s_ms, 3)}
+                                "fixed_over_by_count_time": round(s_ms / s2, 3)}
             log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
         result["batches"] = batches
         result["split_by_count"] = by_count
-        eq, tot = invariance_pairs(world, world.ctx, probes=[0, 1, 37, 100, 200, args.batch - 1])
-        eq_c, tot_c = invariance_pairs(world, bc_ctx, probes=[0, 1, 37, 100, 200, args.batch - 1])
+        probes = [0, 1, 37, 100, 200, args.batch - 1]
+        eq, tot = invariance_pairs(world, world.ctx, probes)
+        eq_c, tot_c = invariance_pairs(world, bc_ctx, probes)
         result["invariance_rate"] = round(eq / tot, 6)
         result["invariance_pairs"] = f"{eq}/{tot}"
         result["split_by_count_invariance_rate"] = round(eq_c / tot_c, 6)
         log(f"invariance: fixed {eq}/{tot}, split-by-count {eq_c}/{tot_c}")
+        del world, head
+        torch.cuda.empty_cache()
         result["prefill"] = prefill_tflops(max(3, args.steps // 4), 1)
         log(f"prefill: {result['prefill']}")
+        if args.suite:
+            result["suite"] = suite(args)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(world)
+        result["cpu_baseline"] = cpu_baseline(lens, shape)
         log(f"cpu baseline: {result['cpu_baseline']}")
     result["manifest"] = {"git": git_sha(), "torch": torch.__version__, "hip": torch.version.hip,
-                          "device": torch.cuda.get_device_name(0), "seed": SEED}
+                          "device": torch.cuda.get_device_name(0), "seed": SEED,
+                          "host_threads": os.cpu_count(), "cpu": cpu_model()}
     print(json.dumps(result), flush=True)
 
 

@@ -136,6 +136,19 @@ struct TileStep {
   bf16x8 phi[2], plo[2];
 };
 
+// Splits weights w0, w1 into bf16 hi parts and bf16 lo parts (w - hi is exact
+// in fp32), both rounded to nearest even.
+__device__ __forceinline__ void split_hi_lo(float w0, float w1, bf16x2& hi, bf16x2& lo) {
+  hi = __builtin_convertvector((f32x2{w0, w1}), bf16x2);
+  const float r0 = w0 - (float)hi[0];
+  const float r1 = w1 - (float)hi[1];
+  lo = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
+}
+
+// MASK = false is the same computation for a tile whose keys are all visible
+// to every row that will be stored (the selects below are then identities);
+// rows that are never stored may compute anything there.
+template <bool MASK>
 __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (&s)[4], float c, int tile_key0,
                                                  int limit, int lane_group) {
   TileStep ts;
@@ -147,12 +160,12 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
       const float g = s[blk][j] * c;
-      x[blk][j] = key <= limit ? g : neg_inf();
+      x[blk][j] = (!MASK || key <= limit) ? g : neg_inf();
       mx = fmaxf(mx, x[blk][j]);
     }
   }
   mx = row_max(mx);
-  ts.any_visible = tile_key0 <= limit;
+  ts.any_visible = !MASK || tile_key0 <= limit;
   ts.m_new = fmaxf(m, mx);
   ts.alpha = ia_exp2(m - ts.m_new);
   float a[4][4];
@@ -162,7 +175,7 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
-      a[blk][j] = key <= limit ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
+      a[blk][j] = (!MASK || key <= limit) ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
       sum = sum + a[blk][j];
     }
   }
@@ -174,11 +187,13 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float w = a[2 * ks2 + hb][j];
-        const __bf16 hi = to_bf16(w);
-        ts.phi[ks2][4 * hb + j] = hi;
-        ts.plo[ks2][4 * hb + j] = to_bf16(w - (float)hi);
+      for (int j = 0; j < 4; j += 2) {
+        bf16x2 hi, lo;
+        split_hi_lo(a[2 * ks2 + hb][j], a[2 * ks2 + hb][j + 1], hi, lo);
+        ts.phi[ks2][4 * hb + j] = hi[0];
+        ts.phi[ks2][4 * hb + j + 1] = hi[1];
+        ts.plo[ks2][4 * hb + j] = lo[0];
+        ts.plo[ks2][4 * hb + j + 1] = lo[1];
       }
     }
   }
@@ -213,7 +228,7 @@ __device__ __forceinline__ void commit_scalars(float& m, float& z, const TileSte
 template <int D>
 __device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4], const VTile<D>& vt,
                                             float c, int tile_key0, int limit, int lane_group) {
-  const TileStep ts = tile_softmax(st.m, st.z, s, c, tile_key0, limit, lane_group);
+  const TileStep ts = tile_softmax<true>(st.m, st.z, s, c, tile_key0, limit, lane_group);
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) st.u[mb] = pv_block(st.u[mb], vt.f[mb], ts);
   commit_scalars(st.m, st.z, ts);

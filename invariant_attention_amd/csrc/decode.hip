@@ -38,13 +38,12 @@ __device__ __forceinline__ int split_len(int policy, int S, int n, int B) {
 
 // Raw fragments one wave needs for one tile: K block w (all k-steps) and the
 // V^T fragments of its D/64 dim blocks (4 key quads each), plus the key
-// counts for the zero fill (k_valid: block w; valid: every block).
+// count of every block for the zero fill of V.
 template <int D, bool FP8>
 struct DecodeFrags {
   static constexpr int MB = D / 64;
   typename Raw<FP8>::K k[D / 32];
   typename Raw<FP8>::V v[MB][2][2];
-  int k_valid;
   int valid[4];
 };
 
@@ -60,7 +59,6 @@ __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const 
   constexpr size_t kHeadBytes = (size_t)D * 16 * EB;  // one (page, kv head) block
   const TilePages tp = tile_pages_of(e, t0, n, num_pages);
   const int kpg = w == 0 ? tp.page[0] : (w == 1 ? tp.page[1] : (w == 2 ? tp.page[2] : tp.page[3]));
-  f.k_valid = w == 0 ? tp.valid[0] : (w == 1 ? tp.valid[1] : (w == 2 ? tp.valid[2] : tp.valid[3]));
   const uint8_t* kp = kc + ((size_t)kpg * Hkv + kvh) * kHeadBytes;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
@@ -84,22 +82,25 @@ __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const 
 
 // One tile of a decode unit: wave w's scores of key block w go through LDS
 // buffer `xb` to all 4 waves; each wave runs the softmax step of the whole
-// tile and the value step of its own dim blocks.
-template <int D, bool FP8>
+// tile and the value step of its own dim blocks.  FULL: every key of the tile
+// exists (t0 + 64 <= n), so no key is masked and nothing needs zero filling;
+// otherwise keys >= n get -inf scores and zero values.  (Their K needs no
+// fill: a key's score column depends only on its own K row, and a masked
+// score is replaced, never used.)
+template <int D, bool FP8, bool FULL>
 __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const QFrag<D>& q, f32x4 (*xb)[64],
                                             float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int limit,
                                             int w, int lane, int r, int g) {
   constexpr int MB = D / 64;
   bf16x8 kf[D / 32];
-  const bool key_ok = r < f.k_valid;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(f.k[ks], key_ok);
+  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(f.k[ks], true);
   xb[w][lane] = block_scores<D>(kf, q);
   __syncthreads();
   f32x4 sc[4];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) sc[blk] = xb[blk][lane];
-  const TileStep ts = tile_softmax(m, z, sc, c, t0, limit, g);
+  const TileStep ts = tile_softmax<!FULL>(m, z, sc, c, t0, limit, g);
 #pragma unroll
   for (int mbi = 0; mbi < MB; ++mbi) {
     bf16x8 vf[2];
@@ -107,7 +108,7 @@ __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const 
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const bf16x4 v4 = v_to_bf16(f.v[mbi][ks2][hb], f.valid[2 * ks2 + hb] - 4 * g);
+        const bf16x4 v4 = v_to_bf16(f.v[mbi][ks2][hb], FULL ? 4 : f.valid[2 * ks2 + hb] - 4 * g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
       }
@@ -118,17 +119,31 @@ __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const 
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_tile_any(const DecodeFrags<D, FP8>& f, const QFrag<D>& q, f32x4 (*xb)[64],
+                                                float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int n,
+                                                int limit, int w, int lane, int r, int g) {
+  if (t0 + kTileKeys <= n)
+    decode_tile<D, FP8, true>(f, q, xb, m, z, u, c, t0, limit, w, lane, r, g);
+  else
+    decode_tile<D, FP8, false>(f, q, xb, m, z, u, c, t0, limit, w, lane, r, g);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   constexpr int MB = D / 64;
   __shared__ f32x4 xs[2][4][64];  // score exchange, double buffered by tile parity
   __shared__ __attribute__((aligned(16))) int bt_lds[4 * kBtWindowTiles];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
+  // Split-major order: every sequence's first split is dispatched before any
+  // second split, and so on.  Early splits are whole (S keys) while last
+  // splits are partial, so the longest units start first and the short ones
+  // fill the tail (longest-first list scheduling).
   const int unit = blockIdx.x;
-  const int s = unit % a.max_splits;
-  const int kvh = (unit / a.max_splits) % a.Hkv;
-  const int b = unit / a.max_splits / a.Hkv;
+  const int kvh = unit % a.Hkv;
+  const int b = (unit / a.Hkv) % a.B;
+  const int s = unit / a.Hkv / a.B;
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int S = split_len(a.policy, a.split_tokens, n, a.B);
   const int nsplit = (n + S - 1) / S;
@@ -187,11 +202,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int lt = 0; lt < wn; lt += 2) {
       load(fb, lt + 1);
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting on this tile
-      decode_tile<D, FP8>(fa, q, xs[0], m, z, u, c, k_begin + kTileKeys * (w0 + lt), limit, w, lane, r, g);
+      decode_tile_any<D, FP8>(fa, q, xs[0], m, z, u, c, k_begin + kTileKeys * (w0 + lt), n, limit, w, lane, r, g);
       if (lt + 1 >= wn) break;
       load(fa, lt + 2);
       __builtin_amdgcn_sched_barrier(0);
-      decode_tile<D, FP8>(fb, q, xs[1], m, z, u, c, k_begin + kTileKeys * (w0 + lt + 1), limit, w, lane, r, g);
+      decode_tile_any<D, FP8>(fb, q, xs[1], m, z, u, c, k_begin + kTileKeys * (w0 + lt + 1), n, limit, w, lane, r,
+                              g);
     }
   }
 

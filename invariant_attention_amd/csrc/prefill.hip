@@ -249,7 +249,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         lds_k_block<D>(tile, blk, r, g, kf);
         sc[blk] = block_scores<D>(kf, q);
       }
-      const TileStep ts = tile_softmax(st.m, st.z, sc, c, t0, limit, g);
+      // The tile is whole for the wave when its last key is visible to the
+      // wave's first position (and so to every stored row of the wave).
+      const TileStep ts = t0 + kTileKeys - 1 <= n - ql + iw ? tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g)
+                                                           : tile_softmax<true>(st.m, st.z, sc, c, t0, limit, g);
 #pragma unroll
       for (int mb = 0; mb < D / 16; ++mb) {
         bf16x8 vf[2];
