@@ -92,6 +92,14 @@ class Sequence:
     def q(self, seed: int, shape: AttnShape, p0: int, p1: int) -> torch.Tensor:
         return rows(seed, self.content, _STREAM_Q, shape.Hq, shape.d, p0, p1)
 
+    def tokens(self, p0: int = 0, p1: int | None = None) -> list[int]:
+        """Synthetic token ids of positions [p0, p1): a function of the position and of its block's
+        content id, so sequences that share a prefix share its tokens (what a prefix cache keys on)."""
+        p1 = self.n if p1 is None else p1
+        pos = np.arange(p0, p1, dtype=np.int64)
+        c = self.content[pos // ROW_BLOCK]
+        return [int(x) for x in ((c * 1000003 + pos * 7919) % 49999 + 1)]
+
 
 def make_sequences(lens, shared_prefix: int = 0, first_sid: int = 0) -> list[Sequence]:
     """Sequences with the given lengths; the first `shared_prefix` positions (a multiple of 16)

@@ -99,3 +99,61 @@ def prefill(ctx, pages: DevicePages, q: torch.Tensor, cu: np.ndarray, layout: wl
 
 def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy()
+
+
+class MiniEngine:
+    """An attention-only stand-in for an inference engine.  The library's page pool (C ABI) decides
+    which cached pages a new sequence reuses and where each computed position's K/V goes;
+    kv_append writes them; prefill and decode read them through the pool's block table.  No model:
+    a position's K/V/Q rows come from the seeded generators."""
+
+    def __init__(self, shape: wl.AttnShape, num_pages: int, seed: int = 0, fp8=False, scales=(None, None),
+                 flags: int = 0, ctx=None):
+        self.shape = shape
+        self.seed = seed
+        self.num_pages = num_pages
+        self.pool = ia.Pool(num_pages, shape.P, flags)
+        self.pages = DevicePages(shape, num_pages, fp8, *scales)
+        self.ctx = make_ctx(shape, fp8=fp8) if ctx is None else ctx
+        self.hist = {}  # handle -> positions that have a token in the pool's history
+
+    def begin(self, seq: wl.Sequence, n_prompt: int | None = None):
+        """Starts seq with its first n_prompt tokens; returns (handle, cached positions)."""
+        n_prompt = seq.n if n_prompt is None else n_prompt
+        h, cached = ia.ia_seq_begin(self.pool, seq.tokens(0, n_prompt))
+        self.hist[h.value] = n_prompt
+        return h, cached
+
+    def _layout(self, h) -> wl.PageLayout:
+        bt = np.array(ia.ia_seq_block_table(h), dtype=np.int32)
+        return wl.PageLayout(self.num_pages, bt[None, :], [bt.astype(np.int64)])
+
+    def _append(self, seq, h, p0, p1):
+        slots = np.array(ia.ia_seq_reserve(self.pool, h, p1 - p0), dtype=np.int64)
+        self.pages.append(self.ctx, seq.k(self.seed, self.shape, p0, p1), seq.v(self.seed, self.shape, p0, p1),
+                          slots)
+
+    def prefill(self, seq, h, p0: int, p1: int) -> torch.Tensor:
+        """Computes positions [p0, p1) (the next ones of the history) in one prefill call."""
+        assert ia.ia_seq_len(h) == p0 and p1 <= self.hist[h.value]
+        self._append(seq, h, p0, p1)
+        out = prefill(self.ctx, self.pages, seq.q(self.seed, self.shape, p0, p1), np.array([0, p1 - p0]),
+                      self._layout(h), [p1])
+        ia.ia_seq_commit(self.pool, h, p1 - p0)
+        return out
+
+    def decode(self, seq, h, p: int) -> torch.Tensor:
+        """Computes position p (the next one) with the decode entry point, appending its token to
+        the history first if it is not part of the prompt."""
+        assert ia.ia_seq_len(h) == p
+        if p >= self.hist[h.value]:
+            ia.ia_seq_append_tokens(self.pool, h, seq.tokens(p, p + 1))
+            self.hist[h.value] = p + 1
+        self._append(seq, h, p, p + 1)
+        out = decode(self.ctx, self.pages, seq.q(self.seed, self.shape, p, p + 1), self._layout(h), [p + 1])
+        ia.ia_seq_commit(self.pool, h, 1)
+        return out
+
+    def end(self, h) -> None:
+        ia.ia_seq_end(self.pool, h)
+        self.hist.pop(h.value, None)
