@@ -53,17 +53,33 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 }
 
 // Row reductions over the 4 lanes that share a row (lanes l, l^16, l^32,
-// l^48).  IEEE addition and max are commutative, so the butterfly leaves the
-// same bits in all four lanes.
+// l^48), as two swap steps on the VALU (gfx950 v_permlane16_swap /
+// v_permlane32_swap).  Swapping a register with itself hands each lane the
+// pair (x[lo], x[hi]) of its butterfly partners in the same order in both
+// lanes, so all four lanes end with the same bits.
+__device__ __forceinline__ void swap16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a, b;
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  swap32(v, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float row_sum(float v) {
-  v = v + __shfl_xor(v, 16);
-  v = v + __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
 }
 
 // Online-softmax state of one row (replicated in its 4 lanes) plus the lane's

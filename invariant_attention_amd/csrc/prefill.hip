@@ -11,13 +11,15 @@
 // running merge (ascending order, as in decode).  Tiles past all of a wave's
 // positions are skipped, which is the identity on its rows' states.
 //
-// Staging.  While the waves compute tile t from LDS buffer t&1, the
-// workgroup's global loads of tile t+1 are in flight; after the compute they
-// are zero filled past the sequence end (and, for e4m3 pages, converted to
-// bf16, exactly) and written to buffer (t+1)&1; one barrier per tile.
+// Staging.  Tiles pass through a three-slot LDS ring: while the waves take
+// the scores of tile t+1 and finish tile t, the workgroup's global loads of
+// tile t+2 are in flight; they are then zero filled past the sequence end
+// (and, for e4m3 pages, converted to bf16, exactly) and written to the slot
+// tile t-1 freed; one barrier per tile.
 //   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B   (the pages' own layout)
 //   LDS V: [2 key halves][D dims][4 quads][2 blocks] x 8 B
-// so every MFMA operand fragment is one conflict-free 16-byte LDS read.
+// so every MFMA operand fragment is one 16-byte LDS read and every LDS write
+// of a wave is one contiguous run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,58 +38,66 @@ constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
 
-// Source 16-byte units of one tile, and their staging registers.
+// Staging registers of one thread for one tile.
+//  K: the tile's K is 4 page blocks of D * 16 elements in the pages' own
+//     order; 16-byte units of it are copied as they are (kKUnits units).
+//  V: slot (ks2, dim, g) of the LDS layout holds tokens 4g..4g+3 of dim `dim`
+//     from page block 2 ks2 (8 bytes as bf16) followed by the same tokens of
+//     block 2 ks2 + 1; a thread gathers both quads and writes the slot whole,
+//     so every LDS write of a wave is one contiguous run.
 template <int D, bool FP8>
 struct Stage {
-  static constexpr int kUnits = 2 * kTileKeys * D * Raw<FP8>::kElemBytes / 16;
-  static constexpr int kPerThread = kUnits / kPrefillThreads;
-  static_assert(kUnits % kPrefillThreads == 0, "tile units must divide over the workgroup");
-  uint4 w[kPerThread];
-  int nv[kPerThread];  // keys among the unit's page block (tokens past it are zero filled)
+  static constexpr int kKUnits = kTileKeys * D * Raw<FP8>::kElemBytes / 16;
+  static constexpr int kKPer = (kKUnits + kPrefillThreads - 1) / kPrefillThreads;
+  static constexpr int kVSlots = 2 * D * 4;
+  static constexpr int kVPer = kVSlots / kPrefillThreads;
+  static_assert(kKUnits % 64 == 0 && kVSlots % kPrefillThreads == 0, "tile must divide over the waves");
+  uint4 k[kKPer];
+  int knv[kKPer];                  // keys in the unit's page block
+  typename Raw<FP8>::V v[kVPer][2];
+  int vnv[kVPer][2];               // keys among each quad's 4 tokens
 };
 
-// Whether unit i of thread tid is a V unit: units [0, kUnits/2) of a tile are
-// K, the rest V (known at compile time per i when a half spans whole rounds of
-// the workgroup, else uniform per wave).
-template <int D, bool FP8>
-__device__ __forceinline__ bool unit_is_v(int i, int tid) {
-  constexpr int kHalf = Stage<D, FP8>::kUnits / 2;
-  if constexpr (kHalf >= kPrefillThreads) return i >= kHalf / kPrefillThreads;
-  else return tid >= kHalf;
+// x[blk] for a lane-varying blk in 0..3, as two levels of selects on its bits
+// (no branches).
+__device__ __forceinline__ int select4(int blk, const int (&x)[4]) {
+  const int lo = (blk & 1) ? x[1] : x[0];
+  const int hi = (blk & 1) ? x[3] : x[2];
+  return (blk & 2) ? hi : lo;
 }
 
-// Issues the global loads of the tile at t0 for this thread's units.  Unit c
-// of a tile: units [0, kUnits/2) are K, the rest V; each half is 4 page
-// blocks of kUnits/8 units in the pages' own order (a page block of one kv
-// head is D * 16 contiguous elements in both pools).  btv holds the tile's
-// block-table entries in lanes 0..3.
+// Issues the global loads of the tile at t0 for this thread's share.  btv
+// holds the tile's block-table entries in lanes 0..3.
 template <int D, bool FP8>
 __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc, const uint8_t* vc, int btv, int t0,
                                            int n, int num_pages, int kvh, int Hkv, int tid) {
-  constexpr int kHalf = Stage<D, FP8>::kUnits / 2;
-  constexpr int kBlk = kHalf / 4;
-  constexpr size_t kHeadBytes = (size_t)D * 16 * Raw<FP8>::kElemBytes;
+  using S = Stage<D, FP8>;
+  constexpr int EB = Raw<FP8>::kElemBytes;
+  constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
+  const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
+                           __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
+  const TilePages tp = tile_pages_of(e, t0, n, num_pages);
 #pragma unroll
-  for (int i = 0; i < Stage<D, FP8>::kPerThread; ++i) {
+  for (int i = 0; i < S::kKPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const bool is_v = unit_is_v<D, FP8>(i, tid);
-    const int cc = is_v ? c - kHalf : c;
-    const int blk = cc / kBlk, u = cc % kBlk;
-    int pg;
-    block_page(__shfl(btv, blk), t0 + 16 * blk, n, num_pages, pg, st.nv[i]);
-    const uint8_t* base = (is_v ? vc : kc) + ((size_t)pg * Hkv + kvh) * kHeadBytes;
-    st.w[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)u * 16);
+    const int cc = c < S::kKUnits ? c : S::kKUnits - 1;
+    const int blk = cc / (S::kKUnits / 4), u = cc % (S::kKUnits / 4);
+    st.knv[i] = select4(blk, tp.valid);
+    const uint8_t* base = kc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
+    st.k[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)u * 16);
   }
-}
-
-// Zero-fills tokens >= valid of 8 consecutive bf16 tokens starting at tok0.
-__device__ __forceinline__ uint4 mask8_bf16(uint4 w, int nv) {
-  // nv = valid tokens among the 8 (may be <= 0 or >= 8); 2 tokens per dword.
-  w.x = nv >= 2 ? w.x : (nv == 1 ? (w.x & 0xFFFFu) : 0u);
-  w.y = nv >= 4 ? w.y : (nv == 3 ? (w.y & 0xFFFFu) : 0u);
-  w.z = nv >= 6 ? w.z : (nv == 5 ? (w.z & 0xFFFFu) : 0u);
-  w.w = nv >= 8 ? w.w : (nv == 7 ? (w.w & 0xFFFFu) : 0u);
-  return w;
+#pragma unroll
+  for (int i = 0; i < S::kVPer; ++i) {
+    const int c = tid + kPrefillThreads * i;
+    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = c % 4;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int blk = 2 * ks2 + hb;
+      st.vnv[i][hb] = select4(blk, tp.valid) - 4 * g;
+      const uint8_t* base = vc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
+      st.v[i][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(base + (uint32_t)((dim * 16 + 4 * g) * EB));
+    }
+  }
 }
 
 __device__ __forceinline__ uint2 fp8x8_to_bf16(uint32_t lo, uint32_t hi, uint2* second) {
@@ -100,68 +110,46 @@ __device__ __forceinline__ uint2 fp8x8_to_bf16(uint32_t lo, uint32_t hi, uint2* 
   return __builtin_bit_cast(uint2, x);
 }
 
-// Writes staged unit c (masked, as bf16) into the LDS tile; nv = keys in
-// its page block.
+// Writes the staged share (keys past the sequence end zero filled, e4m3
+// converted to bf16 exactly) into the LDS tile.
 template <int D, bool FP8>
-__device__ __forceinline__ void stage_store_unit(uint8_t* lds, int c, bool is_v, uint4 w, int nv) {
-  constexpr int kHalf = Stage<D, FP8>::kUnits / 2;
-  constexpr int kBlk = kHalf / 4;
+__device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& st, int tid) {
+  using S = Stage<D, FP8>;
   constexpr int kKBytes = kTileKeys * D * 2;  // LDS K region
-  const int cc = is_v ? c - kHalf : c;
-  const int blk = cc / kBlk, u = cc % kBlk;
-  if constexpr (!FP8) {
-    if (!is_v) {
-      // K unit u = chunk u / 16, token u % 16: 8 dims of one token.
-      const bool keep = (u & 15) < nv;
+#pragma unroll
+  for (int i = 0; i < S::kKPer; ++i) {
+    const int c = tid + kPrefillThreads * i;
+    if (S::kKUnits % kPrefillThreads != 0 && c >= S::kKUnits) continue;  // uniform per wave
+    const int blk = c / (S::kKUnits / 4), u = c % (S::kKUnits / 4);
+    uint4 w = st.k[i];
+    if constexpr (!FP8) {
+      // unit u = chunk u / 16, token u % 16: 8 dims of one token
+      const bool keep = (u & 15) < st.knv[i];
       w.x = keep ? w.x : 0u;
       w.y = keep ? w.y : 0u;
       w.z = keep ? w.z : 0u;
       w.w = keep ? w.w : 0u;
-      *reinterpret_cast<uint4*>(lds + ((size_t)blk * (D / 8) * 16 + u) * 16) = w;
+      *reinterpret_cast<uint4*>(lds + (size_t)c * 16) = w;
     } else {
-      // V unit u = dim u / 2, tokens 8 (u % 2) .. +7 (quads g = 2 (u % 2), +1).
-      const int dim = u >> 1, half = u & 1;
-      w = mask8_bf16(w, nv - 8 * half);
-      const int ks2 = blk >> 1, hb = blk & 1;
-      uint8_t* dst = lds + kKBytes + ((size_t)(ks2 * D + dim) * 4 + 2 * half) * 16 + hb * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
-      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(w.z, w.w);
-    }
-  } else {
-    if (!is_v) {
-      // K unit u = chunk u / 8, tokens 2 (u % 8), +1: 8 codes each.
+      // unit u = chunk u / 8, tokens 2 (u % 8) and +1: 8 codes each
       const int chunk = u >> 3, tok = 2 * (u & 7);
-      const bool k0 = tok < nv, k1 = tok + 1 < nv;
+      const bool k0 = tok < st.knv[i], k1 = tok + 1 < st.knv[i];
       uint2 a1, b1;
       const uint2 a0 = fp8x8_to_bf16(k0 ? w.x : 0u, k0 ? w.y : 0u, &a1);
       const uint2 b0 = fp8x8_to_bf16(k1 ? w.z : 0u, k1 ? w.w : 0u, &b1);
       uint8_t* dst = lds + ((size_t)(blk * (D / 8) + chunk) * 16 + tok) * 16;
       *reinterpret_cast<uint4*>(dst) = make_uint4(a0.x, a0.y, a1.x, a1.y);
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(b0.x, b0.y, b1.x, b1.y);
-    } else {
-      // V unit u = dim u: its 16 tokens.
-      const int dim = u;
-      const int ks2 = blk >> 1, hb = blk & 1;
-      const uint32_t src[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int k = nv - 4 * qd;
-        const uint32_t x = k >= 4 ? src[qd] : (k <= 0 ? 0u : (src[qd] & ((1u << (8 * k)) - 1u)));
-        const bf16x2 a = fp8x2_to_bf16(x, false), b = fp8x2_to_bf16(x, true);
-        bf16x4 y;
-        y[0] = a[0]; y[1] = a[1]; y[2] = b[0]; y[3] = b[1];
-        uint8_t* dst = lds + kKBytes + ((size_t)(ks2 * D + dim) * 4 + qd) * 16 + hb * 8;
-        *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, y);
-      }
     }
   }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& st, int tid) {
 #pragma unroll
-  for (int i = 0; i < Stage<D, FP8>::kPerThread; ++i)
-    stage_store_unit<D, FP8>(lds, tid + kPrefillThreads * i, unit_is_v<D, FP8>(i, tid), st.w[i], st.nv[i]);
+  for (int i = 0; i < S::kVPer; ++i) {
+    const int c = tid + kPrefillThreads * i;
+    const bf16x4 lo = v_to_bf16(st.v[i][0], st.vnv[i][0]);
+    const bf16x4 hi = v_to_bf16(st.v[i][1], st.vnv[i][1]);
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    *reinterpret_cast<uint4*>(lds + kKBytes + (size_t)c * 16) = make_uint4(l.x, l.y, h.x, h.y);
+  }
 }
 
 // Operand fragments of one tile from LDS.
@@ -181,12 +169,25 @@ __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, i
         bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + g) * 16));
 }
 
+// Scores of one tile for the wave's rows, from the LDS copy of its K.
+template <int D>
+__device__ __forceinline__ void lds_tile_scores(const uint8_t* tile, const QFrag<D>& q, int r, int g,
+                                                f32x4 (&sc)[4]) {
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    bf16x8 kf[D / 32];
+    lds_k_block<D>(tile, blk, r, g, kf);
+    sc[blk] = block_scores<D>(kf, q);
+  }
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   constexpr int kTileBytes = tile_lds_bytes<D>();
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   // Heaviest row blocks first: block index -> (row block from the end, b, kvh).
   const int unit = blockIdx.x;
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int hq = kvh * a.group + r % a.group;
   const QFrag<D> q = load_q<D>(a.q + ((size_t)(q0 + (row_ok ? i : i0)) * a.Hq + hq) * D, row_ok, g);
   const int pmax_w = iw < ql ? n - ql + min(iw + ppw, ql) - 1 : -1;  // last position of the wave
+  const int p_first = n - ql + iw;                                     // first position of the wave
   float c = a.c;
   if constexpr (FP8) c = c * a.k_scale[kvh];
   const int S = a.split_tokens;
@@ -220,13 +222,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
   const int T = pmax_wg / kTileKeys;  // last tile
-  // Block-table entries run one tile ahead of the staging loads, which run one
-  // tile ahead of the compute.
+  auto buf = [&](int t) { return lds_raw + (t % 3) * kTileBytes; };
+  // Pipeline.  LDS holds three tiles in a ring.  In step t the waves take
+  // the scores of tile t+1 (MFMA) while running the softmax of tile t (VALU),
+  // then the value product of tile t; meanwhile the workgroup's global loads
+  // of tile t+2 are in flight and land in the ring slot that tile t-1 freed.
+  // One barrier per step.  Block-table entries run one tile ahead of the
+  // loads.
   auto bt_of = [&](int t) { return load_tile_bt(bt_row, kTileKeys * (t < T ? t : T), nblk, lane); };
-  int bt_next = bt_of(1);
   Stage<D, FP8> stg;
   stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_of(0), 0, n, a.num_pages, kvh, a.Hkv, tid);
-  stage_store<D, FP8>(lds_raw, stg, tid);
+  int bt_next = bt_of(1);
+  stage_store<D, FP8>(buf(0), stg, tid);
+  if (T >= 1) {
+    stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+    bt_next = bt_of(2);
+    stage_store<D, FP8>(buf(1), stg, tid);
+  }
   __syncthreads();
 
   RowState<D> st;
@@ -236,23 +248,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  f32x4 sc[4];
+  if (0 <= pmax_w) lds_tile_scores<D>(buf(0), q, r, g, sc);
   for (int t = 0; t <= T; ++t) {
     const int t0 = t * kTileKeys;
-    if (t < T) stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-    const int bt_after = bt_of(t + 2);
-    if (t0 <= pmax_w) {
-      const uint8_t* tile = lds_raw + (t & 1) * kTileBytes;
-      f32x4 sc[4];
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        bf16x8 kf[D / 32];
-        lds_k_block<D>(tile, blk, r, g, kf);
-        sc[blk] = block_scores<D>(kf, q);
-      }
-      // The tile is whole for the wave when its last key is visible to the
-      // wave's first position (and so to every stored row of the wave).
-      const TileStep ts = t0 + kTileKeys - 1 <= n - ql + iw ? tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g)
-                                                           : tile_softmax<true>(st.m, st.z, sc, c, t0, limit, g);
+    const bool more = t + 2 <= T;
+    const int bt_after = bt_of(t + 3);
+    f32x4 sc_next[4];
+    // Steady state: tile t is whole for every stored row of the wave, the wave
+    // needs tile t+1, and tile t+2 is staged.  One straight-line block, so the
+    // scores of tile t+1 (MFMA) can issue under the softmax of tile t (VALU)
+    // and the value product of tile t under the staging of tile t+2.
+    if (more && t0 + kTileKeys - 1 <= p_first && t0 + kTileKeys <= pmax_w) {
+      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + 2 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+      __builtin_amdgcn_sched_barrier(0);  // the loads of tile t+2 go out first
+      const TileStep ts = tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g);
+      lds_tile_scores<D>(buf(t + 1), q, r, g, sc_next);
+      const uint8_t* tile = buf(t);
 #pragma unroll
       for (int mb = 0; mb < D / 16; ++mb) {
         bf16x8 vf[2];
@@ -260,6 +272,26 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         st.u[mb] = pv_block(st.u[mb], vf, ts);
       }
       commit_scalars(st.m, st.z, ts);
+      stage_store<D, FP8>(buf(t + 2), stg, tid);
+    } else {
+      if (more) stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + 2 * kTileKeys, n, a.num_pages, kvh,
+                                   a.Hkv, tid);
+      if (t + 1 <= T && t0 + kTileKeys <= pmax_w) lds_tile_scores<D>(buf(t + 1), q, r, g, sc_next);
+      if (t0 <= pmax_w) {
+        // The tile is whole for the wave when its last key is visible to the
+        // wave's first position (and so to every stored row of the wave).
+        const TileStep ts = t0 + kTileKeys - 1 <= p_first ? tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g)
+                                                          : tile_softmax<true>(st.m, st.z, sc, c, t0, limit, g);
+        const uint8_t* tile = buf(t);
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb) {
+          bf16x8 vf[2];
+          lds_v_block<D>(tile, mb, r, g, vf);
+          st.u[mb] = pv_block(st.u[mb], vf, ts);
+        }
+        commit_scalars(st.m, st.z, ts);
+      }
+      if (more) stage_store<D, FP8>(buf(t + 2), stg, tid);
     }
     // Split end: fold this split's state into the rows that reach into it.
     const int s = t0 / S;
@@ -281,10 +313,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       }
       st.init();
     }
-    if (t < T) {
-      stage_store<D, FP8>(lds_raw + ((t + 1) & 1) * kTileBytes, stg, tid);
-      __syncthreads();
-    }
+    if (t < T) __syncthreads();
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) sc[blk] = sc_next[blk];
     bt_next = bt_after;
   }
   if (!row_ok) return;
@@ -304,7 +335,10 @@ template <int D, bool FP8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (a.B == 0 || a.max_q_len == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.max_row_blocks * a.Hkv;
-  const size_t lds = 2 * (size_t)tile_lds_bytes<D>();
+  const int lds = 3 * tile_lds_bytes<D>();  // the three-tile ring (96 KiB at head_dim 128)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3((unsigned)units), dim3(kPrefillThreads), lds, st, a);
   return hipGetLastError();
 }
