@@ -179,12 +179,21 @@ static void gather_prefix(const attn_args* a, int b, int kvh, int p, double* K, 
   }
 }
 
+/* First key a query at position p sees: 0 for full causal attention; with a
+ * sliding window of w > 0 keys, key j is visible iff p - w < j <= p (Vosti,
+ * App. A.5: sliding-window attention adds the mask term j > p - w). */
+static int first_key(int p, int window) {
+  if (window <= 0) return 0;
+  return p - window + 1 > 0 ? p - window + 1 : 0;
+}
+
 /* One output row by the plain definition: scores s_j = scale * <q, k_j> for
- * j = 0..p, weights exp(s_j - max s), O = sum_j w_j v_j / sum_j w_j. */
-static void attend_plain(const double* qrow, const double* K, const double* V, int p, int d, double scale,
-                         double* s, double* out) {
+ * the visible keys j = lo..p, weights exp(s_j - max s),
+ * O = sum_j w_j v_j / sum_j w_j. */
+static void attend_plain(const double* qrow, const double* K, const double* V, int lo, int p, int d,
+                         double scale, double* s, double* out) {
   double mx = -INFINITY;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     double acc = 0.0;
     for (int c = 0; c < d; ++c) acc += qrow[c] * K[(size_t)j * d + c];
     s[j] = scale * acc;
@@ -192,7 +201,7 @@ static void attend_plain(const double* qrow, const double* K, const double* V, i
   }
   double den = 0.0;
   for (int c = 0; c < d; ++c) out[c] = 0.0;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     double w = exp(s[j] - mx);
     den += w;
     for (int c = 0; c < d; ++c) out[c] += w * V[(size_t)j * d + c];
@@ -206,30 +215,31 @@ static void attend_plain(const double* qrow, const double* K, const double* V, i
  * M = max m_s, num = sum e^{m_s - M} o_s, den = sum e^{m_s - M} l_s
  * (Deterministic inference: results independent of the batch, the split-KV
  * decode example and the "Attention" rule of "Batch invariance: fixed splits
- * that don't change with load").  Used to cross-check the merge algebra. */
-static void attend_split(const double* qrow, const double* K, const double* V, int p, int d, double scale,
-                         int S, double* s, double* out, double* tmp) {
-  int nsplit = p / S + 1;
+ * that don't change with load").  Used to cross-check the merge algebra.
+ * Only splits holding visible keys (lo..p) take part. */
+static void attend_split(const double* qrow, const double* K, const double* V, int lo, int p, int d,
+                         double scale, int S, double* s, double* out, double* tmp) {
+  int s0 = lo / S, nsplit = p / S + 1;
   double M = -INFINITY;
-  for (int j = 0; j <= p; ++j) {
+  for (int j = lo; j <= p; ++j) {
     double acc = 0.0;
     for (int c = 0; c < d; ++c) acc += qrow[c] * K[(size_t)j * d + c];
     s[j] = scale * acc;
   }
   /* per-split maxima, then the global maximum over splits */
-  for (int sp = 0; sp < nsplit; ++sp) {
+  for (int sp = s0; sp < nsplit; ++sp) {
     double m = -INFINITY;
-    for (int j = sp * S; j <= p && j < (sp + 1) * S; ++j) m = s[j] > m ? s[j] : m;
+    for (int j = sp * S > lo ? sp * S : lo; j <= p && j < (sp + 1) * S; ++j) m = s[j] > m ? s[j] : m;
     if (m > M) M = m;
   }
   double den = 0.0;
   for (int c = 0; c < d; ++c) out[c] = 0.0;
-  for (int sp = 0; sp < nsplit; ++sp) {
+  for (int sp = s0; sp < nsplit; ++sp) {
     double m = -INFINITY;
-    for (int j = sp * S; j <= p && j < (sp + 1) * S; ++j) m = s[j] > m ? s[j] : m;
+    for (int j = sp * S > lo ? sp * S : lo; j <= p && j < (sp + 1) * S; ++j) m = s[j] > m ? s[j] : m;
     double l = 0.0;
     for (int c = 0; c < d; ++c) tmp[c] = 0.0;
-    for (int j = sp * S; j <= p && j < (sp + 1) * S; ++j) {
+    for (int j = sp * S > lo ? sp * S : lo; j <= p && j < (sp + 1) * S; ++j) {
       double w = exp(s[j] - m);
       l += w;
       for (int c = 0; c < d; ++c) tmp[c] += w * V[(size_t)j * d + c];
@@ -241,7 +251,7 @@ static void attend_split(const double* qrow, const double* K, const double* V, i
   for (int c = 0; c < d; ++c) out[c] /= den;
 }
 
-static int run_attention(const attn_args* a, int split_tokens, double* out, int nthreads) {
+static int run_attention(const attn_args* a, int split_tokens, int window, double* out, int nthreads) {
   if (a->Hkv <= 0 || a->Hq % a->Hkv != 0 || a->d % 8 != 0 || a->P <= 0) return 1;
   int g = a->Hq / a->Hkv;
   int max_n = 0;
@@ -281,10 +291,11 @@ static int run_attention(const attn_args* a, int split_tokens, double* out, int 
           const uint16_t* qb = a->q + ((size_t)(q0 + i) * a->Hq + h) * a->d;
           for (int c = 0; c < a->d; ++c) qrow[c] = oracle_bf16_to_f64(qb[c]);
           double* o = out + ((size_t)(q0 + i) * a->Hq + h) * a->d;
+          const int lo = first_key(p, window);
           if (split_tokens > 0)
-            attend_split(qrow, K, V, p, a->d, a->scale, split_tokens, sc, o, tmp);
+            attend_split(qrow, K, V, lo, p, a->d, a->scale, split_tokens, sc, o, tmp);
           else
-            attend_plain(qrow, K, V, p, a->d, a->scale, sc, o);
+            attend_plain(qrow, K, V, lo, p, a->d, a->scale, sc, o);
         }
       }
     }
@@ -297,17 +308,18 @@ static int run_attention(const attn_args* a, int split_tokens, double* out, int 
 /*
  * Paged attention over ragged packed queries.  Decode is the case
  * cu_q_lens = 0,1,..,B.  q: [total_q][Hq][d] bf16; out: [total_q][Hq][d]
- * fp64.  split_tokens = 0 gives the plain definition; > 0 computes the same
+ * fp64.  window = 0 is full causal attention, window = w > 0 a sliding window
+ * of w keys.  split_tokens = 0 gives the plain definition; > 0 computes the same
  * rows through fixed-size splits merged in ascending order.
  */
 int oracle_paged_attention(const uint16_t* q, const int32_t* cu_q_lens, const int32_t* seq_lens,
                            const void* k_cache, const void* v_cache, int kv_fp8, const float* k_scale,
                            const float* v_scale, const int32_t* block_table, int32_t bt_stride, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t d, int32_t P, double scale, int32_t split_tokens,
-                           double* out, int32_t nthreads) {
+                           int32_t window, double* out, int32_t nthreads) {
   attn_args a = {q, cu_q_lens, seq_lens, k_cache, v_cache, kv_fp8, k_scale, v_scale, block_table,
                  bt_stride, B, Hq, Hkv, d, P, scale};
-  return run_attention(&a, split_tokens, out, nthreads);
+  return run_attention(&a, split_tokens, window, out, nthreads);
 }
 
 int oracle_max_threads(void) {

@@ -55,7 +55,7 @@ def _load():
     lib.oracle_kv_append.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, P]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_paged_attention.argtypes = [P, P, P, P, P, ctypes.c_int, P, P, P, i32, i32, i32, i32, i32, i32,
-                                           ctypes.c_double, i32, P, i32]
+                                           ctypes.c_double, i32, i32, P, i32]
     lib.oracle_paged_attention.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -123,9 +123,10 @@ def kv_append(k_new: np.ndarray, v_new: np.ndarray, slot_mapping: np.ndarray, k_
 def paged_attention(q: np.ndarray, cu_q_lens: np.ndarray, seq_lens: np.ndarray, k_cache: np.ndarray,
                     v_cache: np.ndarray, block_table: np.ndarray, *, Hq: int, Hkv: int, d: int, P: int,
                     scale: float, kv_fp8: bool = False, k_scale: np.ndarray | None = None,
-                    v_scale: np.ndarray | None = None, split_tokens: int = 0,
+                    v_scale: np.ndarray | None = None, split_tokens: int = 0, window: int = 0,
                     nthreads: int = 0) -> np.ndarray:
-    """fp64 attention output [total_q][Hq][d] for packed ragged queries (bf16 bits as uint16)."""
+    """fp64 attention output [total_q][Hq][d] for packed ragged queries (bf16 bits as uint16).
+    window = 0: full causal attention; window = w > 0: position p sees keys p - w < j <= p."""
     q = np.ascontiguousarray(q.view(np.uint16))
     total_q = int(q.shape[0])
     cu_q_lens = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
@@ -140,7 +141,7 @@ def paged_attention(q: np.ndarray, cu_q_lens: np.ndarray, seq_lens: np.ndarray, 
     rc = _load().oracle_paged_attention(_ptr(q), _ptr(cu_q_lens), _ptr(seq_lens), _ptr(k_cache), _ptr(v_cache),
                                         int(kv_fp8), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
                                         int(block_table.shape[1]), B, Hq, Hkv, d, P, float(scale),
-                                        int(split_tokens), _ptr(out), int(nthreads))
+                                        int(split_tokens), int(window), _ptr(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_paged_attention failed with code %d" % rc)
     return out

@@ -42,7 +42,7 @@ def queries(shape, seqs, seed, q_lens):
 
 
 def run_oracle(shape, seqs, layout, seed, q_lens, fp8=False, k_scale=None, v_scale=None, split_tokens=0,
-               nthreads=0):
+               nthreads=0, window=0):
     kc, vc = host_pools(shape, layout.num_pages, fp8)
     scatter_sequences(shape, seqs, layout, seed, kc, vc, fp8, k_scale, v_scale)
     q, cu = queries(shape, seqs, seed, q_lens)
@@ -50,12 +50,13 @@ def run_oracle(shape, seqs, layout, seed, q_lens, fp8=False, k_scale=None, v_sca
     out = oracle.paged_attention(bits16(q), cu, seq_lens, kc, vc, layout.block_table, Hq=shape.Hq,
                                  Hkv=shape.Hkv, d=shape.d, P=shape.P, scale=shape.scale, kv_fp8=fp8,
                                  k_scale=k_scale, v_scale=v_scale, split_tokens=split_tokens,
-                                 nthreads=nthreads)
+                                 nthreads=nthreads, window=window)
     return out, q, cu, kc, vc
 
 
-def brute_force(shape, seqs, seed, q_lens, scale=None, dequant=None):
-    """Dense numpy fp64 causal softmax(Q K^T * scale) V on the logical rows (no pages)."""
+def brute_force(shape, seqs, seed, q_lens, scale=None, dequant=None, window=0):
+    """Dense numpy fp64 causal softmax(Q K^T * scale) V on the logical rows (no pages); with
+    window = w > 0 a key j is visible to position p iff p - w < j <= p."""
     scale = shape.scale if scale is None else scale
     outs = []
     g = shape.Hq // shape.Hkv
@@ -71,6 +72,8 @@ def brute_force(shape, seqs, seed, q_lens, scale=None, dequant=None):
             sc = scale * (Q[:, h, :] @ K[:, kv, :].T)  # [ql][n]
             pos = s.n - ql + np.arange(ql)
             mask = np.arange(s.n)[None, :] <= pos[:, None]
+            if window > 0:
+                mask &= np.arange(s.n)[None, :] > pos[:, None] - window
             sc = np.where(mask, sc, -np.inf)
             sc = sc - sc.max(axis=1, keepdims=True)
             w = np.exp(sc)

@@ -231,3 +231,74 @@ def test_kv_append_layout(oracle_lib):
     for s in np.nonzero(~written)[0]:
         page, tok = divmod(int(s), 16)
         assert not kc[page, :, :, tok, :].any() and not vc[page, :, :, tok].any()
+
+
+# ------------------------------------------------------ sliding window (Vosti App. A.5)
+
+WINDOWS = [1, 5, 16, 64, 100, 250, 1000]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("mode", ["decode", "prefill", "chunk"])
+def test_window_matches_dense_bruteforce(oracle_lib, window, mode):
+    """Sliding window of w keys: position p sees keys p - w < j <= p (dense numpy fp64 on logical
+    rows, a different formulation), in plain and fixed-split form."""
+    shape = wl.AttnShape(Hq=8, Hkv=2, d=64, P=16, S=64)
+    lens = list(wl.TINY_LENS)
+    seqs = wl.make_sequences(lens)
+    layout = wl.layout_pages(3, lens, shape.P)
+    q_lens = {"decode": [1] * 4, "prefill": lens, "chunk": [5, 64, 33, 17]}[mode]
+    ref = osd.brute_force(shape, seqs, 0, q_lens, window=window)
+    for split in (0, shape.S):
+        out, *_ = osd.run_oracle(shape, seqs, layout, 0, q_lens, window=window, split_tokens=split)
+        assert _close(out, ref) < 1e-12
+
+
+def test_window_of_one_returns_own_value_row(oracle_lib):
+    """w = 1: each position sees only itself, so O = v_p exactly."""
+    shape = wl.AttnShape(Hq=4, Hkv=2, d=32, P=16, S=64)
+    lens = [70, 33]
+    seqs = wl.make_sequences(lens)
+    layout = wl.layout_pages(3, lens, shape.P)
+    out, *_ = osd.run_oracle(shape, seqs, layout, 0, lens, window=1)
+    want = np.concatenate([s.v(0, shape).to(torch.float64).numpy().repeat(shape.g, axis=1) for s in seqs])
+    assert np.array_equal(out, want)
+
+
+def test_window_wider_than_context_equals_full_attention(oracle_lib):
+    shape = wl.AttnShape(Hq=8, Hkv=2, d=64, P=16, S=128)
+    lens = list(wl.TINY_LENS)
+    seqs = wl.make_sequences(lens)
+    layout = wl.layout_pages(3, lens, shape.P)
+    full, *_ = osd.run_oracle(shape, seqs, layout, 0, lens)
+    for w in (300, 301, 10_000):
+        out, *_ = osd.run_oracle(shape, seqs, layout, 0, lens, window=w)
+        assert np.array_equal(out, full)
+
+
+def test_window_zero_query_gives_mean_of_window(oracle_lib):
+    shape = wl.AttnShape(Hq=2, Hkv=1, d=16, P=4, S=64)
+    rng = np.random.default_rng(5)
+    n, w = 23, 6
+    K = _bf16(rng.standard_normal((n, 1, 16)))
+    V = _bf16(rng.standard_normal((n, 1, 16)))
+    Q = _bf16(np.zeros((n, 2, 16)))
+    kc, vc = osd.host_pools(shape, 6)
+    pos = np.arange(n)
+    oracle.kv_append(osd.bits16(K), osd.bits16(V), pos, kc, vc, Hkv=1, d=16, P=4)
+    out = oracle.paged_attention(osd.bits16(Q), np.array([0, n], np.int32), np.array([n], np.int32), kc, vc,
+                                 np.arange(6, dtype=np.int32)[None, :], Hq=2, Hkv=1, d=16, P=4,
+                                 scale=shape.scale, window=w)
+    Vd = V.to(torch.float64).numpy()[:, 0, :]
+    for i in range(n):
+        mean = Vd[max(0, i - w + 1):i + 1].mean(axis=0)
+        assert np.max(np.abs(out[i, 0] - mean)) < 1e-14
+
+
+def test_window_page_permutation_is_bit_identical(oracle_lib):
+    shape = wl.AttnShape(Hq=8, Hkv=2, d=64, P=16, S=128)
+    lens = list(wl.TINY_LENS)
+    seqs = wl.make_sequences(lens)
+    a, *_ = osd.run_oracle(shape, seqs, wl.layout_pages(3, lens, shape.P), 0, lens, window=77)
+    b, *_ = osd.run_oracle(shape, seqs, wl.layout_pages(8, lens, shape.P), 0, lens, window=77)
+    assert np.array_equal(a, b)
