@@ -90,6 +90,12 @@ typedef struct {
   float sm_scale;        /* softmax scale, e.g. 1/sqrt(d); scores use
                             c = fp32(sm_scale * log2(e)) and exp2 (Vosti App. A.2,
                             "shared base-two scale c") */
+  int32_t sliding_window; /* 0: full causal attention.  w > 0: position p sees
+                             keys p - w < j <= p (Vosti App. A.5, sliding-window
+                             attention).  Splits and tiles with no visible key
+                             are skipped, which is the identity on a row's state,
+                             so decode = prefill and batch invariance hold as for
+                             full attention. */
 } ia_config;
 
 typedef struct ia_ctx ia_ctx;

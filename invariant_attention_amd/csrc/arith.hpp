@@ -97,16 +97,6 @@ struct RowState {
   }
 };
 
-// K fragments of one tile: kf[blk][ks] = A operand of key block blk, k-step ks.
-template <int D>
-struct KTile {
-  bf16x8 f[4][D / 32];
-};
-// V^T fragments of one tile: vf[mb][ks2] = A operand of dim block mb, key k-step ks2.
-template <int D>
-struct VTile {
-  bf16x8 f[D / 16][2];
-};
 // Q^T fragments of the wave's rows: qf[ks] = B operand of k-step ks.
 template <int D>
 struct QFrag {
@@ -125,21 +115,17 @@ __device__ __forceinline__ f32x4 block_scores(const bf16x8 (&kf)[D / 32], const 
   return acc;
 }
 
-// Scores of one tile: s[blk] = block_scores(K block blk).
-template <int D>
-__device__ __forceinline__ void tile_scores(const KTile<D>& kt, const QFrag<D>& q, f32x4 (&s)[4]) {
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) s[blk] = block_scores<D>(kt.f[blk], q);
-}
-
 // The softmax half of one tile's update for one row (Vosti App. A.2):
 //   G  = dot(Q, K^T) * c,  masked lanes -> -inf
 //   m^ = max(m, max_b G),  alpha = exp2(m - m^)
 //   A  = select(mask, exp2(G - m^), 0)
 //   z^ = z * alpha + sum_b A
-// `limit` is the row's last visible key (its position p); keys beyond it and
-// keys of rows that do not exist (limit < 0) are masked.  tile_key0 is the
-// absolute index of the tile's first key.  z sums the fp32 weights.  The
+// The row sees keys lo..limit: limit is its position p (keys beyond it, and
+// every key of a row that does not exist, limit < 0, are masked) and lo is 0,
+// or p - w + 1 under a sliding window of w keys (Vosti App. A.5: the mask
+// adds j > p - w).  tile_key0 is the absolute index of the tile's first key.
+// A tile with no visible key keeps the state bit for bit.  z sums the fp32
+// weights.  The
 // weights leave as the B operands of the value product: each fp32 weight is
 // the unevaluated sum of two bf16 numbers, A_hi = bf16(A) and
 // A_lo = bf16(A - A_hi) (A - A_hi is exact).  Vosti casts the weights once to
@@ -166,7 +152,7 @@ __device__ __forceinline__ void split_hi_lo(float w0, float w1, bf16x2& hi, bf16
 // rows that are never stored may compute anything there.
 template <bool MASK>
 __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (&s)[4], float c, int tile_key0,
-                                                 int limit, int lane_group) {
+                                                 int lo, int limit, int lane_group) {
   TileStep ts;
   float x[4][4];
   float mx = neg_inf();
@@ -176,12 +162,12 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
       const float g = s[blk][j] * c;
-      x[blk][j] = (!MASK || key <= limit) ? g : neg_inf();
+      x[blk][j] = (!MASK || (key <= limit && key >= lo)) ? g : neg_inf();
       mx = fmaxf(mx, x[blk][j]);
     }
   }
   mx = row_max(mx);
-  ts.any_visible = !MASK || tile_key0 <= limit;
+  ts.any_visible = !MASK || (tile_key0 <= limit && tile_key0 + kTileKeys - 1 >= lo);
   ts.m_new = fmaxf(m, mx);
   ts.alpha = ia_exp2(m - ts.m_new);
   float a[4][4];
@@ -191,7 +177,7 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
-      a[blk][j] = (!MASK || key <= limit) ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
+      a[blk][j] = (!MASK || (key <= limit && key >= lo)) ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
       sum = sum + a[blk][j];
     }
   }
@@ -237,17 +223,6 @@ __device__ __forceinline__ void commit_scalars(float& m, float& z, const TileSte
     m = ts.m_new;
     z = ts.z_new;
   }
-}
-
-// One whole tile of the online softmax for one row: the softmax half, the
-// value half for every dim block, then the scalars.
-template <int D>
-__device__ __forceinline__ void tile_update(RowState<D>& st, const f32x4 (&s)[4], const VTile<D>& vt,
-                                            float c, int tile_key0, int limit, int lane_group) {
-  const TileStep ts = tile_softmax<true>(st.m, st.z, s, c, tile_key0, limit, lane_group);
-#pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) st.u[mb] = pv_block(st.u[mb], vt.f[mb], ts);
-  commit_scalars(st.m, st.z, ts);
 }
 
 // Folds split partial (m_s, z_s, U_s) into the running merged state (M, Z, U);

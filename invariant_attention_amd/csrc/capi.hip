@@ -118,6 +118,8 @@ ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown split_policy %d", c.split_policy);
   if (!(c.sm_scale > 0.f) || !std::isfinite(c.sm_scale))
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "sm_scale must be finite and positive");
+  if (c.sliding_window < 0)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "sliding_window must be >= 0 (got %d)", c.sliding_window);
   ia_ctx* ctx = new (std::nothrow) ia_ctx;
   if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
   ctx->cfg = c;
@@ -218,6 +220,7 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.max_splits = (int)ms;
   a.split_tokens = ctx->cfg.split_tokens;
   a.policy = ctx->cfg.split_policy;
+  a.window = ctx->cfg.sliding_window;
   return hip_status(ia::launch_decode(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
                                       static_cast<hipStream_t>(stream)),
                     "decode launch");
@@ -270,6 +273,7 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
   a.max_row_blocks = (int)row_blocks;
   a.split_tokens = ctx->cfg.split_tokens;
   a.total_q = total_q;
+  a.window = ctx->cfg.sliding_window;
   return hip_status(ia::launch_prefill(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
                                        static_cast<hipStream_t>(stream)),
                     "prefill launch");

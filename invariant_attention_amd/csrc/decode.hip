@@ -7,7 +7,7 @@
 // the 4 waves exchange scores through LDS, every wave runs the same softmax
 // step on the whole tile, and wave w applies it to dim blocks
 // [w * D/64, (w + 1) * D/64) of the value accumulators.  A row's operations
-// and their order are those of tile_update (arith.hpp), so the bits equal
+// and their order are those of a single wave's tile step, so the bits equal
 // prefill's at the same position; splitting the blocks over waves only
 // changes where each operation runs.  Each wave loads exactly the operand
 // fragments it consumes, straight from the pages into registers, one tile
@@ -89,8 +89,8 @@ __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const 
 // score is replaced, never used.)
 template <int D, bool FP8, bool FULL>
 __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const QFrag<D>& q, f32x4 (*xb)[64],
-                                            float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int limit,
-                                            int w, int lane, int r, int g) {
+                                            float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int lo,
+                                            int limit, int w, int lane, int r, int g) {
   constexpr int MB = D / 64;
   bf16x8 kf[D / 32];
 #pragma unroll
@@ -100,7 +100,7 @@ __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const 
   f32x4 sc[4];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) sc[blk] = xb[blk][lane];
-  const TileStep ts = tile_softmax<!FULL>(m, z, sc, c, t0, limit, g);
+  const TileStep ts = tile_softmax<!FULL>(m, z, sc, c, t0, lo, limit, g);
 #pragma unroll
   for (int mbi = 0; mbi < MB; ++mbi) {
     bf16x8 vf[2];
@@ -121,11 +121,18 @@ __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const 
 template <int D, bool FP8>
 __device__ __forceinline__ void decode_tile_any(const DecodeFrags<D, FP8>& f, const QFrag<D>& q, f32x4 (*xb)[64],
                                                 float& m, float& z, f32x4 (&u)[D / 64], float c, int t0, int n,
-                                                int limit, int w, int lane, int r, int g) {
-  if (t0 + kTileKeys <= n)
-    decode_tile<D, FP8, true>(f, q, xb, m, z, u, c, t0, limit, w, lane, r, g);
+                                                int lo, int limit, int w, int lane, int r, int g) {
+  if (t0 >= lo && t0 + kTileKeys <= n)
+    decode_tile<D, FP8, true>(f, q, xb, m, z, u, c, t0, lo, limit, w, lane, r, g);
   else
-    decode_tile<D, FP8, false>(f, q, xb, m, z, u, c, t0, limit, w, lane, r, g);
+    decode_tile<D, FP8, false>(f, q, xb, m, z, u, c, t0, lo, limit, w, lane, r, g);
+}
+
+// First key a decode row at position p sees: 0, or p - w + 1 under a sliding
+// window of w keys (Vosti App. A.5).
+__device__ __forceinline__ int first_key(int p, int window) {
+  if (window <= 0) return 0;
+  return p - window + 1 > 0 ? p - window + 1 : 0;
 }
 
 template <int D, bool FP8>
@@ -147,8 +154,11 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int S = split_len(a.policy, a.split_tokens, n, a.B);
   const int nsplit = (n + S - 1) / S;
-  if (s >= nsplit) return;  // uniform over the workgroup
   const int p = n - 1;
+  const int lo = first_key(p, a.window);
+  // Splits past the sequence, and (sliding window) splits before the window,
+  // hold no visible key: no unit runs for them and the merge skips them.
+  if (s >= nsplit || (s + 1) * S <= lo) return;  // uniform over the workgroup
   const bool row_ok = r < a.group;
   const int limit = row_ok ? p : -1;
   const int hq = kvh * a.group + (row_ok ? r : 0);
@@ -156,8 +166,8 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   float c = a.c;
   if constexpr (FP8) c = c * a.k_scale[kvh];
 
-  const int k_begin = s * S;
-  const int k_end = min(k_begin + S, n);
+  const int k_begin = max(s * S, lo & ~(kTileKeys - 1));  // the window's first tile, if later
+  const int k_end = min(s * S + S, n);
   const int ntiles = (k_end - k_begin + kTileKeys - 1) / kTileKeys;
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
@@ -202,12 +212,13 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
     for (int lt = 0; lt < wn; lt += 2) {
       load(fb, lt + 1);
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting on this tile
-      decode_tile_any<D, FP8>(fa, q, xs[0], m, z, u, c, k_begin + kTileKeys * (w0 + lt), n, limit, w, lane, r, g);
+      decode_tile_any<D, FP8>(fa, q, xs[0], m, z, u, c, k_begin + kTileKeys * (w0 + lt), n, lo, limit, w, lane, r,
+                            g);
       if (lt + 1 >= wn) break;
       load(fa, lt + 2);
       __builtin_amdgcn_sched_barrier(0);
-      decode_tile_any<D, FP8>(fb, q, xs[1], m, z, u, c, k_begin + kTileKeys * (w0 + lt + 1), n, limit, w, lane, r,
-                              g);
+      decode_tile_any<D, FP8>(fb, q, xs[1], m, z, u, c, k_begin + kTileKeys * (w0 + lt + 1), n, lo, limit, w, lane,
+                            r, g);
     }
   }
 
@@ -237,14 +248,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     for (int k = 0; k < kPer; ++k) out[k] = (__bf16)0.f;
     return;
   }
-  const size_t row0 = (size_t)b * a.max_splits * a.Hq + hq;
+  const int s0 = first_key(n - 1, a.window) / S;  // first split with a visible key
+  const size_t row0 = ((size_t)b * a.max_splits + s0) * a.Hq + hq;
   const f32x2 ml0 = *reinterpret_cast<const f32x2*>(a.ws_ml + row0 * 2);
   float M = ml0[0], Z = ml0[1];
   float U[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) U[k] = a.ws_u[row0 * D + kPer * lane + k];
-  for (int s = 1; s < nsplit; ++s) {
-    const size_t row = row0 + (size_t)s * a.Hq;
+  for (int s = s0 + 1; s < nsplit; ++s) {
+    const size_t row = row0 + (size_t)(s - s0) * a.Hq;
     const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + row * 2);
     float wa, wb;
     merge_scalars(M, Z, ml[0], ml[1], wa, wb);

@@ -35,6 +35,7 @@ struct DecodeArgs {
   int bt_stride, num_pages;
   int max_seq_len, max_splits;
   int split_tokens, policy;
+  int window;                  // 0: full causal attention; w > 0: keys p - w < j <= p
 };
 
 struct PrefillArgs {
@@ -53,6 +54,7 @@ struct PrefillArgs {
   int max_q_len, max_seq_len, max_row_blocks;
   int split_tokens;
   int total_q;
+  int window;                 // 0: full causal attention; w > 0: keys p - w < j <= p
 };
 
 hipError_t launch_kv_append(int D, bool fp8, const AppendArgs& a, hipStream_t st);

@@ -11,11 +11,10 @@
 // running merge (ascending order, as in decode).  Tiles past all of a wave's
 // positions are skipped, which is the identity on its rows' states.
 //
-// Staging.  Tiles pass through a three-slot LDS ring: while the waves take
-// the scores of tile t+1 and finish tile t, the workgroup's global loads of
-// tile t+2 are in flight; they are then zero filled past the sequence end
-// (and, for e4m3 pages, converted to bf16, exactly) and written to the slot
-// tile t-1 freed; one barrier per tile.
+// Staging.  Tiles pass through two LDS slots: while the waves compute tile t,
+// the workgroup's global loads of tile t+1 are in flight; they are then zero
+// filled past the sequence end (and, for e4m3 pages, converted to bf16,
+// exactly) and written to the other slot; one barrier per tile.
 //   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B   (the pages' own layout)
 //   LDS V: [2 key halves][D dims][4 quads][2 blocks] x 8 B
 // so every MFMA operand fragment is one 16-byte LDS read and every LDS write
@@ -31,6 +30,13 @@ namespace ia {
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+
+// First key position p sees: 0, or p - w + 1 under a sliding window of w keys
+// (Vosti App. A.5).
+__device__ __forceinline__ int first_key(int p, int window) {
+  if (window <= 0) return 0;
+  return p - window + 1 > 0 ? p - window + 1 : 0;
+}
 
 // LDS bytes of one staged tile: K and V, 64 keys x D dims x 2 bytes each.
 template <int D>
@@ -215,30 +221,31 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const QFrag<D> q = load_q<D>(a.q + ((size_t)(q0 + (row_ok ? i : i0)) * a.Hq + hq) * D, row_ok, g);
   const int pmax_w = iw < ql ? n - ql + min(iw + ppw, ql) - 1 : -1;  // last position of the wave
   const int p_first = n - ql + iw;                                     // first position of the wave
+  // Visible keys: lo..p per row, lo = 0 or p - w + 1 under a sliding window
+  // of w keys (Vosti App. A.5).  lo_first / lo_last bound the wave's rows.
+  const int lo = first_key(p, a.window);
+  const int lo_first = first_key(p_first, a.window);
+  const int lo_last = first_key(pmax_w, a.window);
+  // Whether the wave has a row that sees some key of tile t.
+  auto needs = [&](int t) { return t * kTileKeys <= pmax_w && t * kTileKeys + kTileKeys - 1 >= lo_first; };
   float c = a.c;
   if constexpr (FP8) c = c * a.k_scale[kvh];
   const int S = a.split_tokens;
 
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
-  const int T = pmax_wg / kTileKeys;  // last tile
-  auto buf = [&](int t) { return lds_raw + (t % 3) * kTileBytes; };
-  // Pipeline.  LDS holds three tiles in a ring.  In step t the waves take
-  // the scores of tile t+1 (MFMA) while running the softmax of tile t (VALU),
-  // then the value product of tile t; meanwhile the workgroup's global loads
-  // of tile t+2 are in flight and land in the ring slot that tile t-1 freed.
-  // One barrier per step.  Block-table entries run one tile ahead of the
-  // loads.
+  const int T = pmax_wg / kTileKeys;                                   // last tile
+  const int T0 = first_key(n - ql + i0, a.window) / kTileKeys;         // first tile
+  auto buf = [&](int t) { return lds_raw + (t & 1) * kTileBytes; };
+  // Pipeline.  LDS holds two tiles.  While the waves compute tile t from one
+  // slot, the workgroup's global loads of tile t+1 are in flight; they are
+  // written to the other slot after the compute, and one barrier per tile
+  // publishes them.  Block-table entries run one tile ahead of the loads.
   auto bt_of = [&](int t) { return load_tile_bt(bt_row, kTileKeys * (t < T ? t : T), nblk, lane); };
   Stage<D, FP8> stg;
-  stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_of(0), 0, n, a.num_pages, kvh, a.Hkv, tid);
-  int bt_next = bt_of(1);
-  stage_store<D, FP8>(buf(0), stg, tid);
-  if (T >= 1) {
-    stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-    bt_next = bt_of(2);
-    stage_store<D, FP8>(buf(1), stg, tid);
-  }
+  stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_of(T0), T0 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+  int bt_next = bt_of(T0 + 1);
+  stage_store<D, FP8>(buf(T0), stg, tid);
   __syncthreads();
 
   RowState<D> st;
@@ -248,23 +255,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 sc[4];
-  if (0 <= pmax_w) lds_tile_scores<D>(buf(0), q, r, g, sc);
-  for (int t = 0; t <= T; ++t) {
+  for (int t = T0; t <= T; ++t) {
     const int t0 = t * kTileKeys;
-    const bool more = t + 2 <= T;
-    const int bt_after = bt_of(t + 3);
-    f32x4 sc_next[4];
-    // Steady state: tile t is whole for every stored row of the wave, the wave
-    // needs tile t+1, and tile t+2 is staged.  One straight-line block, so the
-    // scores of tile t+1 (MFMA) can issue under the softmax of tile t (VALU)
-    // and the value product of tile t under the staging of tile t+2.
-    if (more && t0 + kTileKeys - 1 <= p_first && t0 + kTileKeys <= pmax_w) {
-      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + 2 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-      __builtin_amdgcn_sched_barrier(0);  // the loads of tile t+2 go out first
-      const TileStep ts = tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g);
-      lds_tile_scores<D>(buf(t + 1), q, r, g, sc_next);
-      const uint8_t* tile = buf(t);
+    const bool more = t < T;
+    const int bt_after = bt_of(t + 2);
+    const uint8_t* tile = buf(t);
+    // The tile is whole for the wave when all its keys are visible to every
+    // stored row: its last key to the first position, its first key to the
+    // last position's window.
+    const bool whole = t0 + kTileKeys - 1 <= p_first && t0 >= lo_last;
+    if (more && whole) {
+      // Steady state, one straight-line block: the loads of tile t+1 go out
+      // first, then tile t's scores, softmax and value product, then the
+      // staging of tile t+1.
+      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 sc[4];
+      lds_tile_scores<D>(tile, q, r, g, sc);
+      const TileStep ts = tile_softmax<false>(st.m, st.z, sc, c, t0, lo, limit, g);
 #pragma unroll
       for (int mb = 0; mb < D / 16; ++mb) {
         bf16x8 vf[2];
@@ -272,17 +280,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         st.u[mb] = pv_block(st.u[mb], vf, ts);
       }
       commit_scalars(st.m, st.z, ts);
-      stage_store<D, FP8>(buf(t + 2), stg, tid);
+      stage_store<D, FP8>(buf(t + 1), stg, tid);
     } else {
-      if (more) stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + 2 * kTileKeys, n, a.num_pages, kvh,
-                                   a.Hkv, tid);
-      if (t + 1 <= T && t0 + kTileKeys <= pmax_w) lds_tile_scores<D>(buf(t + 1), q, r, g, sc_next);
-      if (t0 <= pmax_w) {
-        // The tile is whole for the wave when its last key is visible to the
-        // wave's first position (and so to every stored row of the wave).
-        const TileStep ts = t0 + kTileKeys - 1 <= p_first ? tile_softmax<false>(st.m, st.z, sc, c, t0, limit, g)
-                                                          : tile_softmax<true>(st.m, st.z, sc, c, t0, limit, g);
-        const uint8_t* tile = buf(t);
+      if (more) stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv,
+                                   tid);
+      if (needs(t)) {
+        f32x4 sc[4];
+        lds_tile_scores<D>(tile, q, r, g, sc);
+        const TileStep ts = whole ? tile_softmax<false>(st.m, st.z, sc, c, t0, lo, limit, g)
+                                  : tile_softmax<true>(st.m, st.z, sc, c, t0, lo, limit, g);
 #pragma unroll
         for (int mb = 0; mb < D / 16; ++mb) {
           bf16x8 vf[2];
@@ -291,13 +297,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         }
         commit_scalars(st.m, st.z, ts);
       }
-      if (more) stage_store<D, FP8>(buf(t + 2), stg, tid);
+      if (more) stage_store<D, FP8>(buf(t + 1), stg, tid);
     }
-    // Split end: fold this split's state into the rows that reach into it.
+    // Split end: fold this split's state into the rows that see a key of it;
+    // a row's first such split seeds its merge.
     const int s = t0 / S;
     if (t == T || (t0 + kTileKeys) % S == 0) {
-      if (limit >= s * S) {
-        if (s == 0) {
+      if (limit >= s * S && lo < s * S + S) {
+        if (s == lo / S) {
           M = st.m;
           Z = st.z;
 #pragma unroll
@@ -313,9 +320,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       }
       st.init();
     }
-    if (t < T) __syncthreads();
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) sc[blk] = sc_next[blk];
+    if (more) __syncthreads();
     bt_next = bt_after;
   }
   if (!row_ok) return;
@@ -335,7 +340,7 @@ template <int D, bool FP8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (a.B == 0 || a.max_q_len == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.max_row_blocks * a.Hkv;
-  const int lds = 3 * tile_lds_bytes<D>();  // the three-tile ring (96 KiB at head_dim 128)
+  const int lds = 2 * tile_lds_bytes<D>();  // two tile slots (64 KiB at head_dim 128)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
