@@ -205,6 +205,8 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 // The value half of the update for one dim block mb of a row:
 //   U^ = U * alpha, then per key k-step ks2 (ascending) U^ += V^T A_hi, U^ += V^T A_lo
 // (one MFMA each, hi first); the block keeps U when the tile is fully masked.
+// MASK = false: a tile every stored row sees, so the update always applies.
+template <bool MASK = true>
 __device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2], const TileStep& ts) {
   f32x4 un;
 #pragma unroll
@@ -214,12 +216,14 @@ __device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2],
     un = mfma(vf[ks2], ts.phi[ks2], un);
     un = mfma(vf[ks2], ts.plo[ks2], un);
   }
-  return ts.any_visible ? un : u;
+  if constexpr (MASK) return ts.any_visible ? un : u;
+  return un;
 }
 
 // Commits the scalar half of a tile step.
+template <bool MASK = true>
 __device__ __forceinline__ void commit_scalars(float& m, float& z, const TileStep& ts) {
-  if (ts.any_visible) {
+  if (!MASK || ts.any_visible) {
     m = ts.m_new;
     z = ts.z_new;
   }

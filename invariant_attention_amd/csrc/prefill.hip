@@ -12,15 +12,19 @@
 // positions are skipped, which is the identity on its rows' states.
 //
 // Staging.  Tiles pass through two LDS slots: while the waves compute tile t,
-// the workgroup's global loads of tile t+1 are in flight; they are then zero
-// filled past the sequence end (and, for e4m3 pages, converted to bf16,
-// exactly) and written to the other slot; one barrier per tile.
+// the workgroup's loads of tile t+1 are in flight into the other slot; one
+// barrier per tile.  bf16 pages go from memory straight into LDS
+// (global_load_lds: K in 1 KiB runs, V dword by dword into its slot layout),
+// with a zero fill of the keys past the sequence end only in a tile that has
+// them; e4m3 pages go through registers, where they are zero filled and
+// converted to bf16 (exactly).
 //   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B   (the pages' own layout)
-//   LDS V: [2 key halves][D dims][4 quads][2 blocks] x 8 B
-// so every MFMA operand fragment is one 16-byte LDS read and every LDS write
-// of a wave is one contiguous run.
+//   LDS V: [2 key halves][D dims][4 quads, swizzled][2 blocks] x 8 B
+// so every MFMA operand fragment is one 16-byte LDS read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "arith.hpp"
 #include "launch.hpp"
@@ -30,6 +34,7 @@ namespace ia {
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
 // First key position p sees: 0, or p - w + 1 under a sliding window of w keys
 // (Vosti App. A.5).
@@ -43,6 +48,14 @@ template <int D>
 constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
+
+// LDS V slots are 16 bytes: slot (ks2, dim, g) holds tokens 4g..4g+3 of dim
+// `dim` from page blocks 2 ks2 and 2 ks2 + 1.  The four quads of a dim sit in
+// 4 consecutive positions, swizzled: quad g of dim d is at position
+// 4 (ks2 D + d) + (g ^ ((d / 4) % 4)).  A fragment read takes dims r = 0..15
+// of one quad; without the swizzle lanes r, r + 4, r + 8, r + 12 would hit
+// the same banks.  v_quad_at gives the quad stored at position x of dim d.
+__device__ __forceinline__ int v_quad_at(int x, int dim) { return x ^ ((dim >> 2) & 3); }
 
 // Staging registers of one thread for one tile.
 //  K: the tile's K is 4 page blocks of D * 16 elements in the pages' own
@@ -95,7 +108,7 @@ __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc,
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = c % 4;
+    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = v_quad_at(c % 4, dim);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int blk = 2 * ks2 + hb;
@@ -158,6 +171,88 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
   }
 }
 
+// ---- bf16 tiles: direct global -> LDS loads (global_load_lds) --------------
+// The data moves from the pages to LDS without passing through registers.
+// Each instruction of a wave fills a contiguous LDS run in lane order: 16
+// bytes per lane for K (the LDS K layout is the pages' own, so a page block
+// is four 1 KiB copies), 4 bytes per lane for V (each lane picks the dword its
+// position in the V slot layout needs, from either of the slot's two pages).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+template <int D>
+__device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
+                                             int kvh, int Hkv, int w, int lane) {
+  constexpr size_t kHeadBytes = (size_t)D * 16 * 2;          // one (page, kv head) block
+  constexpr int kKChunks = kTileKeys * D * 2 / 1024;          // 1 KiB K chunks per tile
+  constexpr int kVChunks = kTileKeys * D * 2 / 256;           // 256 B V chunks per tile (one dword per lane)
+  constexpr int kKBytes = kTileKeys * D * 2;
+  constexpr int kVHalf = kVChunks / kPrefillWaves / 2;        // V loads of a wave per key half
+  static_assert(kKChunks % kPrefillWaves == 0 && kVChunks % (2 * kPrefillWaves) == 0, "chunks must divide over waves");
+  static_assert(kVHalf * 1024 <= 4096, "V load offsets must fit the instruction offset");
+  auto head = [&](const uint8_t* pool, int pg) { return pool + ((size_t)pg * Hkv + kvh) * kHeadBytes; };
+#pragma unroll
+  for (int i = 0; i < kKChunks / kPrefillWaves; ++i) {
+    const int ch = i * kPrefillWaves + w;  // wave-uniform
+    const int blk = ch / (kKChunks / 4), part = ch % (kKChunks / 4);
+    const int pg = blk == 0 ? tp.page[0] : (blk == 1 ? tp.page[1] : (blk == 2 ? tp.page[2] : tp.page[3]));
+    const uint8_t* src = head(kc, pg) + part * 1024 + lane * 16;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
+  }
+  // V: load il of key half ks2 fills chunk ch = (ks2 * kVHalf + il) * 8 + w, whose
+  // dword `lane` is in position 16 ch + lane / 4 of the LDS V layout: dim
+  // 32 il + 4 w + lane / 16, quad g = ((lane / 4) % 4) ^ (w % 4) (the swizzle,
+  // as dim / 4 = ch = w mod 4), page block 2 ks2 + hb with hb = (lane / 2) % 2,
+  // tokens 4 g + 2 (lane % 2) and the next one.  The lane's source is its
+  // block's head plus a fixed offset, + 1 KiB per il.
+  const int hb = (lane >> 1) & 1;
+  const uint32_t voff =
+      (uint32_t)(((4 * w + (lane >> 4)) * 16 + 4 * (((lane >> 2) & 3) ^ (w & 3)) + 2 * (lane & 1)) * 2);
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    const uint8_t* src = (hb ? head(vc, tp.page[2 * ks2 + 1]) : head(vc, tp.page[2 * ks2])) + voff;
+#pragma unroll
+    for (int il = 0; il < kVHalf; ++il) {
+      const int ch = (ks2 * kVHalf + il) * kPrefillWaves + w;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + il * 1024), (lds_void_t*)(slot + kKBytes + ch * 256), 4, 0,
+                                       0);
+    }
+  }
+}
+
+// Zero fills the K and V of tokens past each block's key count in a landed
+// tile (only tiles that reach past the sequence end, or hold an invalid page),
+// as the register path does.
+template <int D>
+__device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp, int tid) {
+  constexpr int kKBytes = kTileKeys * D * 2;
+  constexpr int kKUnits = kKBytes / 16;
+  constexpr int kVSlots = 2 * D * 4;
+  static_assert(kKUnits % kPrefillThreads == 0, "K units must divide over the threads");
+#pragma unroll
+  for (int i = 0; i < kKUnits / kPrefillThreads; ++i) {
+    const int c = tid + kPrefillThreads * i;
+    // unit c = block c / (units per block), chunk, token c % 16
+    if ((c & 15) >= select4(c / (kKUnits / 4), tp.valid))
+      *reinterpret_cast<uint4*>(slot + (size_t)c * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < kVSlots / kPrefillThreads; ++i) {
+    const int c = tid + kPrefillThreads * i;
+    const int ks2 = c / (4 * D), g = v_quad_at(c % 4, (c / 4) % D);
+    uint4* p = reinterpret_cast<uint4*>(slot + kKBytes + (size_t)c * 16);
+    uint4 v = *p;
+    const bf16x4 lo = v_to_bf16(make_uint2(v.x, v.y), select4(2 * ks2, tp.valid) - 4 * g);
+    const bf16x4 hi = v_to_bf16(make_uint2(v.z, v.w), select4(2 * ks2 + 1, tp.valid) - 4 * g);
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    *p = make_uint4(l.x, l.y, h.x, h.y);
+  }
+}
+
+__device__ __forceinline__ bool tile_partial(const TilePages& tp) {
+  return (tp.valid[0] & tp.valid[1] & tp.valid[2] & tp.valid[3]) != 16;
+}
+
 // Operand fragments of one tile from LDS.
 template <int D>
 __device__ __forceinline__ void lds_k_block(const uint8_t* lds, int blk, int r, int g, bf16x8 (&kf)[D / 32]) {
@@ -172,7 +267,7 @@ __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, i
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2)
     vf[ks2] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + g) * 16));
+        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + (g ^ (r >> 2))) * 16));
 }
 
 // Scores of one tile for the wave's rows, from the LDS copy of its K.
@@ -195,11 +290,26 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  // Heaviest row blocks first: block index -> (row block from the end, b, kvh).
-  const int unit = blockIdx.x;
-  const int kvh = unit % a.Hkv;
-  const int b = (unit / a.Hkv) % a.B;
-  const int rb = a.max_row_blocks - 1 - unit / a.Hkv / a.B;
+  // Block index -> (sequence b, kv head, row block).  Workgroups go to the 8
+  // XCDs round robin (block i to XCD i mod 8), each XCD with its own L2.  The
+  // (b, kvh) pairs are dealt to the XCDs, and each XCD runs its pairs one
+  // after another, every pair's row blocks heaviest (last) first: the
+  // workgroups resident on an XCD at a time are mostly row blocks of one pair
+  // and walk the same K/V tiles, which its L2 then serves.  When the pair count
+  // is not a multiple of 8 the order is simply row block (from the end), b, kvh.
+  const int pairs = a.B * a.Hkv;
+  int pair, rbi;
+  if (pairs % kXcds == 0) {
+    const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    pair = xcd + kXcds * (k / a.max_row_blocks);
+    rbi = k % a.max_row_blocks;
+  } else {
+    pair = blockIdx.x % pairs;
+    rbi = blockIdx.x / pairs;
+  }
+  const int kvh = pair % a.Hkv;
+  const int b = pair / a.Hkv;
+  const int rb = a.max_row_blocks - 1 - rbi;
   const int q0 = a.cu_q_lens[b];
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   int ql = a.cu_q_lens[b + 1] - q0;
@@ -236,17 +346,38 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int nblk = (n + 15) >> 4;
   const int T = pmax_wg / kTileKeys;                                   // last tile
   const int T0 = first_key(n - ql + i0, a.window) / kTileKeys;         // first tile
-  auto buf = [&](int t) { return lds_raw + (t & 1) * kTileBytes; };
   // Pipeline.  LDS holds two tiles.  While the waves compute tile t from one
-  // slot, the workgroup's global loads of tile t+1 are in flight; they are
-  // written to the other slot after the compute, and one barrier per tile
-  // publishes them.  Block-table entries run one tile ahead of the loads.
+  // slot, tile t+1 loads into the other: bf16 pages straight from memory into
+  // LDS, e4m3 pages through registers (converted to bf16 after the compute).
+  // One barrier per tile publishes the next tile; a tile reaching past the
+  // sequence end gets its K and V zero filled between two barriers.
+  // Block-table entries run one tile ahead of the loads.
+  auto buf = [&](int t) { return lds_raw + (t & 1) * kTileBytes; };
   auto bt_of = [&](int t) { return load_tile_bt(bt_row, kTileKeys * (t < T ? t : T), nblk, lane); };
+  auto pages_of = [&](int btv, int t) {
+    const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
+                             __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
+    return tile_pages_of(e, t * kTileKeys, n, a.num_pages);
+  };
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   Stage<D, FP8> stg;
-  stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_of(T0), T0 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+  {
+    const int bt0 = bt_of(T0);
+    const TilePages tp0 = pages_of(bt0, T0);
+    if constexpr (FP8) {
+      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt0, T0 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+      stage_store<D, FP8>(buf(T0), stg, tid);
+      __syncthreads();
+    } else {
+      direct_issue<D>(buf(T0), a.k_cache, a.v_cache, tp0, kvh, a.Hkv, wu, lane);
+      __syncthreads();
+      if (tile_partial(tp0)) {
+        direct_fixup<D>(buf(T0), tp0, tid);
+        __syncthreads();
+      }
+    }
+  }
   int bt_next = bt_of(T0 + 1);
-  stage_store<D, FP8>(buf(T0), stg, tid);
-  __syncthreads();
 
   RowState<D> st;
   st.init();
@@ -259,44 +390,48 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const int t0 = t * kTileKeys;
     const bool more = t < T;
     const int bt_after = bt_of(t + 2);
+    const TilePages tpn = pages_of(bt_next, t + 1);
     const uint8_t* tile = buf(t);
+    if (more) {
+      if constexpr (FP8)
+        stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+      else
+        direct_issue<D>(buf(t + 1), a.k_cache, a.v_cache, tpn, kvh, a.Hkv, wu, lane);
+    }
     // The tile is whole for the wave when all its keys are visible to every
     // stored row: its last key to the first position, its first key to the
     // last position's window.
     const bool whole = t0 + kTileKeys - 1 <= p_first && t0 >= lo_last;
-    if (more && whole) {
-      // Steady state, one straight-line block: the loads of tile t+1 go out
-      // first, then tile t's scores, softmax and value product, then the
-      // staging of tile t+1.
-      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-      __builtin_amdgcn_sched_barrier(0);
+    // One tile step of the wave's rows; MASK = false for a whole tile.  LDS
+    // reads run one block ahead of the MFMAs that use them; the first V block
+    // is read before the softmax.
+    auto step = [&](auto mask) {
+      constexpr bool MASK = decltype(mask)::value;
       f32x4 sc[4];
-      lds_tile_scores<D>(tile, q, r, g, sc);
-      const TileStep ts = tile_softmax<false>(st.m, st.z, sc, c, t0, lo, limit, g);
+      bf16x8 kf[2][D / 32];
+      lds_k_block<D>(tile, 0, r, g, kf[0]);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        if (blk < 3) lds_k_block<D>(tile, blk + 1, r, g, kf[(blk + 1) & 1]);
+        sc[blk] = block_scores<D>(kf[blk & 1], q);
+      }
+      bf16x8 vf[2][2];
+      lds_v_block<D>(tile, 0, r, g, vf[0]);
+      const TileStep ts = tile_softmax<MASK>(st.m, st.z, sc, c, t0, lo, limit, g);
 #pragma unroll
       for (int mb = 0; mb < D / 16; ++mb) {
-        bf16x8 vf[2];
-        lds_v_block<D>(tile, mb, r, g, vf);
-        st.u[mb] = pv_block(st.u[mb], vf, ts);
+        if (mb + 1 < D / 16) lds_v_block<D>(tile, mb + 1, r, g, vf[(mb + 1) & 1]);
+        st.u[mb] = pv_block<MASK>(st.u[mb], vf[mb & 1], ts);
       }
-      commit_scalars(st.m, st.z, ts);
-      stage_store<D, FP8>(buf(t + 1), stg, tid);
-    } else {
-      if (more) stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv,
-                                   tid);
-      if (needs(t)) {
-        f32x4 sc[4];
-        lds_tile_scores<D>(tile, q, r, g, sc);
-        const TileStep ts = whole ? tile_softmax<false>(st.m, st.z, sc, c, t0, lo, limit, g)
-                                  : tile_softmax<true>(st.m, st.z, sc, c, t0, lo, limit, g);
-#pragma unroll
-        for (int mb = 0; mb < D / 16; ++mb) {
-          bf16x8 vf[2];
-          lds_v_block<D>(tile, mb, r, g, vf);
-          st.u[mb] = pv_block(st.u[mb], vf, ts);
-        }
-        commit_scalars(st.m, st.z, ts);
-      }
+      commit_scalars<MASK>(st.m, st.z, ts);
+    };
+    if (needs(t)) {
+      if (whole)
+        step(std::false_type{});
+      else
+        step(std::true_type{});
+    }
+    if constexpr (FP8) {
       if (more) stage_store<D, FP8>(buf(t + 1), stg, tid);
     }
     // Split end: fold this split's state into the rows that see a key of it;
@@ -320,7 +455,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       }
       st.init();
     }
-    if (more) __syncthreads();
+    if (more) {
+      __syncthreads();
+      if constexpr (!FP8) {
+        if (tile_partial(tpn)) {
+          direct_fixup<D>(buf(t + 1), tpn, tid);
+          __syncthreads();
+        }
+      }
+    }
     bt_next = bt_after;
   }
   if (!row_ok) return;
