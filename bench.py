@@ -54,6 +54,8 @@ DEV = "cuda"
 SEED = 0
 COPY_PROBE_BYTES = 1 << 30
 PROFILE_MD = os.path.join(ROOT, "profiles", "decode_split_kernel_llama3-8b_b256.md")
+PREFILL_PROFILE_MD = os.path.join(ROOT, "profiles", "prefill_kernel_qwen3-8b_8x4096.md")
+MFMA_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 of one wave
 KERNEL_SOURCES = ["decode.hip", "arith.hpp", "pages.hpp", "launch.hpp"]
 
 
@@ -111,6 +113,16 @@ def _csv_rows(pattern):
     return rows
 
 
+def _pmc_mean(pmc_dir, kind, counter, kernel):
+    """Mean per dispatch of one counter for one kernel, from the run in <pmc_dir>/pmc_<kind>_<counter>
+    (a run may hold several counters; the directory is named for the first)."""
+    rows = _csv_rows(os.path.join(pmc_dir, f"pmc_{kind}_{counter}", "**", "*counter_collection.csv"))
+    if not rows:
+        rows = _csv_rows(os.path.join(pmc_dir, f"pmc_{kind}_*", "**", "*counter_collection.csv"))
+    vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (float(np.mean(vals)) if vals else float("nan")), len(vals)
+
+
 def summarize_profile(trace_dir, pmc_dir):
     """Writes the decode profile summary (rocprofv3 kernel-trace stats + calibrated FETCH/WRITE)."""
     stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
@@ -119,9 +131,7 @@ def summarize_profile(trace_dir, pmc_dir):
     avg_ns = float(split[0]["AverageNs"])
 
     def pmc_mean(kind, counter, kernel):
-        rows = _csv_rows(os.path.join(pmc_dir, f"pmc_{kind}_{counter}", "**", "*counter_collection.csv"))
-        vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
-        return float(np.mean(vals)), len(vals)
+        return _pmc_mean(pmc_dir, kind, counter, kernel)
 
     fetch_kib, nf = pmc_mean("decode", "FETCH_SIZE", "decode_split_kernel<128, false>")
     write_kib, nw = pmc_mean("decode", "WRITE_SIZE", "decode_split_kernel<128, false>")
@@ -179,6 +189,26 @@ def summarize_profile(trace_dir, pmc_dir):
         f"| HBM bytes written per launch | {write_b:.4e} |",
         f"| traffic / algorithmic bytes | {tr / alg:.4f} |",
         "",
+    ]
+    hit, nh = pmc_mean("decode", "TCC_HIT_sum", "decode_split_kernel<128, false>")
+    miss, _ = pmc_mean("decode", "TCC_MISS_sum", "decode_split_kernel<128, false>")
+    if nh:
+        lines += [
+            "## L2 (rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum, one run)",
+            "",
+            f"    {cmd_pmc.format(C='TCC_HIT_sum TCC_MISS_sum')}",
+            "",
+            "| quantity | value |",
+            "|---|---|",
+            f"| TCC_HIT_sum per dispatch (mean of {nh}) | {hit:.4e} |",
+            f"| TCC_MISS_sum per dispatch | {miss:.4e} |",
+            f"| L2 hit rate | {hit / (hit + miss):.4f} |",
+            "",
+            "The K/V stream is read once and a wave's 16-byte lane loads coalesce into whole lines, so "
+            "nearly every L2 request misses; the few hits are block-table, query and split-partial reads.",
+            "",
+        ]
+    lines += [
         f"traffic_record: source_sha={kernel_source_hash()} bytes_per_launch={tr} read={int(fetch_b)} "
         f"write={int(write_b)} algorithmic={alg}",
         "",
@@ -187,6 +217,99 @@ def summarize_profile(trace_dir, pmc_dir):
     with open(PROFILE_MD, "w") as f:
         f.write("\n".join(lines))
     print(PROFILE_MD)
+
+
+PREFILL_KERNEL = "prefill_kernel<128, false>"
+PREFILL_SQ = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+              "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES"]
+
+
+def summarize_prefill_profile(trace_dir, pmc_dir):
+    """Writes the prefill profile summary: kernel-trace stats, executed MFMA work from SQ counters and
+    calibrated FETCH/WRITE bytes."""
+    stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    rows = [r for r in stats if PREFILL_KERNEL in r["Name"]]
+    avg_ns = float(rows[0]["AverageNs"])
+    shape = wl.QWEN3_8B
+    lens = [4096] * 8
+    flops = 4.0 * shape.d * shape.Hq * sum(n * (n + 1) / 2 for n in lens)
+    kv_unique = sum(lens) * shape.Hkv * shape.d * 2 * 2
+    pm = {c: _pmc_mean(pmc_dir, "prefill", c, PREFILL_KERNEL) for c in PREFILL_SQ}
+    fetch_kib, nf = _pmc_mean(pmc_dir, "prefill", "FETCH_SIZE", PREFILL_KERNEL)
+    write_kib, nw = _pmc_mean(pmc_dir, "prefill", "WRITE_SIZE", PREFILL_KERNEL)
+    copy_fetch, _ = _pmc_mean(pmc_dir, "copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    copy_write, _ = _pmc_mean(pmc_dir, "copy", "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    f_scale = COPY_PROBE_BYTES / (copy_fetch * 1024)
+    w_scale = COPY_PROBE_BYTES / (copy_write * 1024)
+    mfma_flops = pm["SQ_INSTS_MFMA"][0] * MFMA_FLOPS
+    cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o prefill -- "
+                 "python3 bench.py --prefill-only --steps 10 --warmup 2")
+    cmd_sq = ("rocprofv3 --pmc " + " ".join(PREFILL_SQ) + " --output-format csv -d <out> -o pmc -- "
+              "python3 bench.py --prefill-only --steps 3 --warmup 1")
+    cmd_pmc = ("rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- "
+               "python3 bench.py --prefill-only --steps 3 --warmup 1")
+    cmd_copy = "rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- python3 bench.py --copy-probe --steps 3"
+    tf = flops / avg_ns / 1e3
+    lines = [
+        "# prefill_kernel<128, bf16> -- Qwen3-8B-shaped whole prefill, 8 prompts x 4096 tokens, causal",
+        "",
+        "32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits; algorithmic "
+        f"flops per launch {flops:.6e} (4 x d x Hq x sum over rows of the p + 1 visible keys).",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)",
+        "",
+        f"    {cmd_trace}",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    lines += [
+        "",
+        f"Achieved from the trace: {tf:.1f} TFLOP/s = {tf / BF16_PEAK_TFLOPS:.4f} of the 2.5 PFLOP/s dense bf16 peak.",
+        "",
+        "## MFMA work and issue (rocprofv3 --pmc, SQ counters, one run)",
+        "",
+        f"    {cmd_sq}",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+    ]
+    for c in PREFILL_SQ:
+        lines.append(f"| {c} per dispatch (mean of {pm[c][1]}) | {pm[c][0]:.4e} |")
+    lines += [
+        f"| executed MFMA flops (SQ_INSTS_MFMA x {MFMA_FLOPS}) | {mfma_flops:.4e} |",
+        f"| executed / algorithmic flops | {mfma_flops / flops:.4f} |",
+        f"| MFMA pipe busy (executed flops / (duration x peak)) | {mfma_flops / (avg_ns * 1e-9) / 2.5e15:.4f} |",
+        f"| LDS bank-conflict cycles / LDS active cycles | "
+        f"{pm['SQ_LDS_BANK_CONFLICT'][0] / pm['SQ_LDS_IDX_ACTIVE'][0]:.4f} |",
+        "",
+        "Executed over algorithmic flops is 1.5 plus masking waste: each weight is carried as a bf16 hi/lo "
+        "pair, so the value product runs two MFMAs per k-step.",
+        "",
+        "## HBM traffic (rocprofv3 --pmc, one counter per run)",
+        "",
+        f"    {cmd_pmc.format(C='FETCH_SIZE')}",
+        f"    {cmd_pmc.format(C='WRITE_SIZE')}",
+        f"    {cmd_copy.format(C='FETCH_SIZE')}",
+        f"    {cmd_copy.format(C='WRITE_SIZE')}",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| FETCH_SIZE per dispatch (KiB, mean of {nf}) | {fetch_kib:.1f} |",
+        f"| WRITE_SIZE per dispatch (KiB, mean of {nw}) | {write_kib:.1f} |",
+        f"| fetch / write scale (1 GiB device copy) | {f_scale:.4f} / {w_scale:.4f} |",
+        f"| HBM bytes read per launch | {fetch_kib * 1024 * f_scale:.4e} |",
+        f"| HBM bytes written per launch | {write_kib * 1024 * w_scale:.4e} |",
+        f"| distinct K/V bytes (read at least once) | {kv_unique:.4e} |",
+        f"| Q bytes read + O bytes written | {2 * sum(lens) * shape.Hq * shape.d * 2:.4e} |",
+        "",
+    ]
+    os.makedirs(os.path.dirname(PREFILL_PROFILE_MD), exist_ok=True)
+    with open(PREFILL_PROFILE_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(PREFILL_PROFILE_MD)
 
 
 def make_ctx(shape, by_count=False, fp8=False):
@@ -465,10 +588,15 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--suite", action="store_true", help="also time the long-context and shared-prefix points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time the prefill workload only (for profilers)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
+    ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile)
+        return
+    if args.summarize_prefill_profile:
+        summarize_prefill_profile(*args.summarize_prefill_profile)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; there is no multi-GPU path (run with --gpus 1)",
@@ -478,6 +606,9 @@ def main():
     ia.load()
     if args.copy_probe:
         print(json.dumps({"copy_probe": copy_gbs(reps=args.steps)}), flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_tflops(args.steps, args.warmup)}), flush=True)
         return
     shape = wl.LLAMA3_8B
     lens = wl.uniform_lens(SEED, args.batch, 512, 8192)
