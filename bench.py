@@ -312,11 +312,12 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
     print(PREFILL_PROFILE_MD)
 
 
-def make_ctx(shape, by_count=False, fp8=False):
+def make_ctx(shape, by_count=False, fp8=False, decode_kernel=None):
     return ia.Context(ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P, split_tokens=shape.S,
                                      kv_dtype=ia.IA_KV_FP8_E4M3 if fp8 else ia.IA_KV_BF16,
                                      split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
-                                     sm_scale=shape.scale))
+                                     sm_scale=shape.scale,
+                                     decode_kernel=ia.IA_DECODE_AUTO if decode_kernel is None else decode_kernel))
 
 
 class DecodeWorld:
@@ -652,6 +653,15 @@ def main():
             log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
         result["batches"] = batches
         result["split_by_count"] = by_count
+        # The second, bitwise-equivalent decode kernel at the small batches it was built for.
+        wide_ctx = make_ctx(shape, decode_kernel=ia.IA_DECODE_WIDE)
+        wide = {}
+        for B in (1, 8, 64):
+            s_ms, d_ms = time_steps(DecodeRunner(world, range(B), wide_ctx), args.steps, args.warmup)
+            wide[str(B)] = {"step_ms": round(s_ms, 4), "decode_ms": round(d_ms, 4),
+                            "gbs": round(world.kv_bytes(range(B)) / (s_ms * 1e-3) / 1e9, 1)}
+            log(f"B={B}: wide decode kernel {wide[str(B)]['gbs']} GB/s")
+        result["wide_kernel"] = wide
         probes = [0, 1, 37, 100, 200, args.batch - 1]
         eq, tot = invariance_pairs(world, world.ctx, probes)
         eq_c, tot_c = invariance_pairs(world, bc_ctx, probes)

@@ -79,6 +79,22 @@ typedef enum { IA_KV_BF16 = 0, IA_KV_FP8_E4M3 = 1 } ia_kv_dtype;
  * fixed split. */
 typedef enum { IA_SPLIT_FIXED = 0, IA_SPLIT_BY_COUNT = 1 } ia_split_policy;
 
+/* Which decode kernel runs the splits.  Both produce bit-identical partial
+ * states and outputs (the same operations on the same operands in the same
+ * order) and differ only in schedule.  IA_DECODE_SPLIT walks each split's
+ * tiles as one chain of steps (4 waves per split).  IA_DECODE_WIDE lets 8
+ * waves score and weight 8 tiles of a split at once -- the running maximum
+ * before each tile is an exact fmaxf fold of the earlier tiles' maxima -- and
+ * keeps only the z and value updates as a chain.  This is the pages' open
+ * item of dispatch among bitwise-equivalent kernels (Vosti, Discussion,
+ * "Cross-kernel relational verification": one decode kernel for full waves,
+ * one for partially filled waves, with the same accumulation order).  On
+ * MI355X the split's K/V stream through one compute unit bounds both kernels
+ * alike at small batches, so IA_DECODE_AUTO runs SPLIT; WIDE is selectable
+ * and verified bit for bit against SPLIT.  WIDE takes splits of at most
+ * 16384 keys; longer ones run on SPLIT (same bits). */
+typedef enum { IA_DECODE_AUTO = 0, IA_DECODE_SPLIT = 1, IA_DECODE_WIDE = 2 } ia_decode_kernel;
+
 typedef struct {
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads, Hq / Hkv <= 16 */
   int32_t num_kv_heads;  /* Hkv */
@@ -96,6 +112,7 @@ typedef struct {
                              are skipped, which is the identity on a row's state,
                              so decode = prefill and batch invariance hold as for
                              full attention. */
+  int32_t decode_kernel;  /* ia_decode_kernel (0 = AUTO) */
 } ia_config;
 
 typedef struct ia_ctx ia_ctx;

@@ -147,14 +147,23 @@ __device__ __forceinline__ void split_hi_lo(float w0, float w1, bf16x2& hi, bf16
   lo = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
 }
 
+// The row maximum half of a tile step: x = masked scaled scores, mx = their
+// maximum over the row's 64 keys (lane values first, then the butterfly).
+struct TileMax {
+  float x[4][4];
+  float mx;
+  bool any_visible;  // the tile holds a key the row sees
+};
+
+__device__ __forceinline__ bool key_visible(int key, int lo, int limit) { return key <= limit && key >= lo; }
+
 // MASK = false is the same computation for a tile whose keys are all visible
 // to every row that will be stored (the selects below are then identities);
 // rows that are never stored may compute anything there.
 template <bool MASK>
-__device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (&s)[4], float c, int tile_key0,
-                                                 int lo, int limit, int lane_group) {
-  TileStep ts;
-  float x[4][4];
+__device__ __forceinline__ TileMax tile_max(const f32x4 (&s)[4], float c, int tile_key0, int lo, int limit,
+                                            int lane_group) {
+  TileMax tm;
   float mx = neg_inf();
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
@@ -162,13 +171,36 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
       const float g = s[blk][j] * c;
-      x[blk][j] = (!MASK || (key <= limit && key >= lo)) ? g : neg_inf();
-      mx = fmaxf(mx, x[blk][j]);
+      tm.x[blk][j] = (!MASK || key_visible(key, lo, limit)) ? g : neg_inf();
+      mx = fmaxf(mx, tm.x[blk][j]);
     }
   }
-  mx = row_max(mx);
-  ts.any_visible = !MASK || (tile_key0 <= limit && tile_key0 + kTileKeys - 1 >= lo);
-  ts.m_new = fmaxf(m, mx);
+  tm.mx = row_max(mx);
+  tm.any_visible = !MASK || (tile_key0 <= limit && tile_key0 + kTileKeys - 1 >= lo);
+  return tm;
+}
+
+// The running maximum after a tile: unchanged by a tile the row does not see.
+__device__ __forceinline__ float max_update(float m, float mx, bool any_visible) {
+  return any_visible ? fmaxf(m, mx) : m;
+}
+
+// The running sum after a tile: z^ = z * alpha + sum_b A (two roundings).
+__device__ __forceinline__ float z_update(float z, float alpha, float sum) {
+  const float t = z * alpha;
+  return t + sum;
+}
+
+// The weight half of a tile step, given the running maximum m before the
+// tile: m^, alpha, the weights (as hi/lo bf16 B operands) and their row sum.
+// z_new is left to the caller (z_update), so a kernel that has m before each
+// tile but not yet z can form the weights of many tiles at once.
+template <bool MASK>
+__device__ __forceinline__ TileStep tile_weights(float m, const TileMax& tm, int tile_key0, int lo, int limit,
+                                                 int lane_group, float& row_sum_out) {
+  TileStep ts;
+  ts.any_visible = tm.any_visible;
+  ts.m_new = fmaxf(m, tm.mx);
   ts.alpha = ia_exp2(m - ts.m_new);
   float a[4][4];
   float sum = 0.f;
@@ -177,28 +209,37 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
-      a[blk][j] = (!MASK || (key <= limit && key >= lo)) ? ia_exp2(x[blk][j] - ts.m_new) : 0.f;
+      a[blk][j] = (!MASK || key_visible(key, lo, limit)) ? ia_exp2(tm.x[blk][j] - ts.m_new) : 0.f;
       sum = sum + a[blk][j];
     }
   }
-  sum = row_sum(sum);
-  const float t = z * ts.alpha;
-  ts.z_new = t + sum;
+  row_sum_out = row_sum(sum);
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        bf16x2 hi, lo;
-        split_hi_lo(a[2 * ks2 + hb][j], a[2 * ks2 + hb][j + 1], hi, lo);
+        bf16x2 hi, lo2;
+        split_hi_lo(a[2 * ks2 + hb][j], a[2 * ks2 + hb][j + 1], hi, lo2);
         ts.phi[ks2][4 * hb + j] = hi[0];
         ts.phi[ks2][4 * hb + j + 1] = hi[1];
-        ts.plo[ks2][4 * hb + j] = lo[0];
-        ts.plo[ks2][4 * hb + j + 1] = lo[1];
+        ts.plo[ks2][4 * hb + j] = lo2[0];
+        ts.plo[ks2][4 * hb + j + 1] = lo2[1];
       }
     }
   }
+  return ts;
+}
+
+// The whole softmax half of a tile step for one row (the two halves above).
+template <bool MASK>
+__device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (&s)[4], float c, int tile_key0,
+                                                 int lo, int limit, int lane_group) {
+  const TileMax tm = tile_max<MASK>(s, c, tile_key0, lo, limit, lane_group);
+  float sum;
+  TileStep ts = tile_weights<MASK>(m, tm, tile_key0, lo, limit, lane_group, sum);
+  ts.z_new = z_update(z, ts.alpha, sum);
   return ts;
 }
 

@@ -120,6 +120,8 @@ ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "sm_scale must be finite and positive");
   if (c.sliding_window < 0)
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "sliding_window must be >= 0 (got %d)", c.sliding_window);
+  if (c.decode_kernel != IA_DECODE_AUTO && c.decode_kernel != IA_DECODE_SPLIT && c.decode_kernel != IA_DECODE_WIDE)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown decode_kernel %d", c.decode_kernel);
   ia_ctx* ctx = new (std::nothrow) ia_ctx;
   if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
   ctx->cfg = c;
@@ -221,6 +223,7 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.split_tokens = ctx->cfg.split_tokens;
   a.policy = ctx->cfg.split_policy;
   a.window = ctx->cfg.sliding_window;
+  a.wide = ctx->cfg.decode_kernel == IA_DECODE_WIDE;
   return hip_status(ia::launch_decode(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
                                       static_cast<hipStream_t>(stream)),
                     "decode launch");

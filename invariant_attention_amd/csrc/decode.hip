@@ -231,6 +231,258 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The wide decode kernel: bitwise equal to decode_split_kernel, for launches
+// with few units.
+//
+// Within a split the split kernel is one chain of tile steps, and with few
+// units the machine waits on that chain.  Most of a step does not need the
+// chain's state: the scores of a tile, its row maximum, and -- given the
+// running maximum before the tile -- its weights and their row sum.  The
+// running maximum before tile t is a fold of fmaxf over the earlier tiles'
+// row maxima, which every wave can form exactly in the same order.  So here
+// the 8 waves of a unit take a chunk of 8 tiles at a time:
+//   A. wave i scores tile i of the chunk and forms its row maxima;
+//   B. after a barrier, wave i folds the running maximum up to its tile and
+//      forms the tile's weights (hi/lo B operands) and row sum, into LDS;
+//   C. after a barrier, wave w runs the value chain of dim block w over the
+//      chunk's tiles (U * alpha, then the four MFMAs of pv_block) and every
+//      wave folds z = z * alpha + sum.
+// Every operation on a row's values is the split kernel's, with the same
+// operands in the same order (tile_max, max_update, tile_weights, z_update
+// and pv_block are the functions tile_softmax and the split kernel use), so
+// the partial (m, z, U) of each split and hence the output bits are the same;
+// only the schedule differs.  The partials go to the same workspace and the
+// same merge kernel folds them.
+constexpr int kWideWaves = 8;
+constexpr int kWideChunk = kWideWaves;  // tiles per chunk: one per wave in A and B
+constexpr int kWideMaxTiles = 256;      // longest split the wide kernel takes: 16384 keys
+
+template <int D, bool FP8>
+struct WideK {  // K of one tile: 4 key blocks x D/32 k-steps
+  typename Raw<FP8>::K k[4][D / 32];
+};
+template <int D, bool FP8>
+struct WideV {  // V^T of one dim block of one tile: [ks2][hb] key quads
+  typename Raw<FP8>::V v[2][2];
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int EB = Raw<FP8>::kElemBytes;
+  constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
+  constexpr int kDimBlocks = D / 16;
+  __shared__ __attribute__((aligned(16))) uint4 pw[kWideChunk][4][64];  // weights of each tile, per lane
+  __shared__ float mxs[kWideChunk][16];                                   // row maxima
+  __shared__ __attribute__((aligned(16))) float als[16][kWideChunk];     // alpha per row and tile
+  __shared__ __attribute__((aligned(16))) float sms[16][kWideChunk];     // row sums per row and tile
+  __shared__ __attribute__((aligned(16))) int bts[4 * kWideMaxTiles];    // the split's block-table entries
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  // The dim block whose V the wave loads: its own (waves past the last dim
+  // block at head_dim 64 load a copy they never use, so that every wave
+  // issues the same loads and each wait covers exactly the loads it needs).
+  const int wd = w % kDimBlocks;
+  const int unit = blockIdx.x;  // the split kernel's unit order
+  const int kvh = unit % a.Hkv;
+  const int b = (unit / a.Hkv) % a.B;
+  const int s = unit / a.Hkv / a.B;
+  const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int S = split_len(a.policy, a.split_tokens, n, a.B);
+  const int nsplit = (n + S - 1) / S;
+  const int p = n - 1;
+  const int lo = first_key(p, a.window);
+  if (s >= nsplit || (s + 1) * S <= lo) return;  // uniform over the workgroup
+  const bool row_ok = r < a.group;
+  const int limit = row_ok ? p : -1;
+  const int hq = kvh * a.group + (row_ok ? r : 0);
+  const QFrag<D> q = load_q<D>(a.q + ((size_t)b * a.Hq + hq) * D, row_ok, g);
+  float c = a.c;
+  if constexpr (FP8) c = c * a.k_scale[kvh];
+  const int k_begin = max(s * S, lo & ~(kTileKeys - 1));
+  const int k_end = min(s * S + S, n);
+  const int ntiles = (k_end - k_begin + kTileKeys - 1) / kTileKeys;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  const int nblk = (n + 15) >> 4;
+  const uint8_t* kc = a.k_cache;
+  const uint8_t* vc = a.v_cache;
+  // A tile takes the masked step unless all its keys exist and lie in the
+  // window (the split kernel's rule), and a masked tile with no visible key
+  // leaves the row's state as it is.
+  auto full = [&](int t0) { return t0 >= lo && t0 + kTileKeys <= n; };
+  auto visible = [&](int t0) { return full(t0) || (t0 <= limit && t0 + kTileKeys - 1 >= lo); };
+  // The split's block-table entries, staged in LDS once (clamped to the
+  // sequence's last block); a tile index past the split reads the last tile's.
+  {
+    const int e0 = k_begin >> 4;
+    // (The host launches this kernel only for splits of at most
+    // kWideMaxTiles tiles; the bound keeps LDS in range regardless.)
+    for (int i = threadIdx.x; i < 4 * min(ntiles, kWideMaxTiles); i += 64 * kWideWaves) {
+      const int e = e0 + i < nblk ? e0 + i : nblk - 1;
+      bts[i] = bt_row[e];
+    }
+  }
+  __syncthreads();
+  auto pages = [&](int t) {
+    t = t < ntiles ? t : ntiles - 1;
+    t = t < kWideMaxTiles ? t : kWideMaxTiles - 1;
+    const int4 e = *reinterpret_cast<const int4*>(&bts[4 * t]);
+    const int4 eu = make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                              __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+    return tile_pages_of(eu, k_begin + kTileKeys * t, n, a.num_pages);
+  };
+
+  // Loads run one chunk ahead: the K of a wave's tile in the next chunk is
+  // issued once this chunk's scores are formed, the V of its dim block once
+  // this chunk's value chain is done.  A tile past the split re-reads the
+  // split's last tile, which stays in bounds and is never used.
+  // vv[i] packs the key counts of tile i's 4 page blocks, 5 bits each.
+  auto load_v = [&](WideV<D, FP8> (&vr)[kWideChunk], int (&vv)[kWideChunk], int c0) {
+#pragma unroll
+    for (int i = 0; i < kWideChunk; ++i) {
+      const TilePages tp = pages(c0 + i);
+      vv[i] = tp.valid[0] | (tp.valid[1] << 5) | (tp.valid[2] << 10) | (tp.valid[3] << 15);
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const uint8_t* base = vc + ((size_t)tp.page[2 * ks2 + hb] * a.Hkv + kvh) * kHeadBytes;
+          vr[i].v[ks2][hb] = load_v_raw<FP8>(base, (size_t)(16 * wd + r) * 16 + 4 * g);
+        }
+    }
+  };
+  auto load_k = [&](WideK<D, FP8>& kr, int c0) {
+    const TilePages kp = pages(c0 + w);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const uint8_t* base = kc + ((size_t)kp.page[blk] * a.Hkv + kvh) * kHeadBytes;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) kr.k[blk][ks] = load_k_raw<FP8>(base, (size_t)((4 * ks + g) * 16 + r) * 8);
+    }
+  };
+
+  float m = neg_inf(), z = 0.f;  // the running state after the chunks so far
+  f32x4 u = {0.f, 0.f, 0.f, 0.f};  // dim block w (waves w < D/16)
+  WideV<D, FP8> vr[kWideChunk];
+  int vvalid[kWideChunk];
+  WideK<D, FP8> kr;
+  // (K before V, the order of the loop's own prefetches, so the wait for a
+  // chunk's K never has to drain its V.)
+  load_k(kr, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(vr, vvalid, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c0 = 0; c0 < ntiles; c0 += kWideChunk) {
+    const int nt = min(kWideChunk, ntiles - c0);
+    // A: scores and row maxima of tile w of the chunk.
+    const bool mine = w < nt;
+    const int tw0 = k_begin + kTileKeys * (c0 + (mine ? w : 0));
+    TileMax tm = {};
+    if (mine) {
+      f32x4 sc[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        bf16x8 kf[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(kr.k[blk][ks], true);
+        sc[blk] = block_scores<D>(kf, q);
+      }
+      tm = full(tw0) ? tile_max<false>(sc, c, tw0, lo, limit, g) : tile_max<true>(sc, c, tw0, lo, limit, g);
+      if (g == 0) mxs[w][r] = tm.mx;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kr, c0 + kWideChunk);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // B: the running maximum before tile w, then its weights and row sum.
+    if (mine) {
+      float mp = m;
+      for (int i = 0; i < w; ++i) mp = max_update(mp, mxs[i][r], visible(k_begin + kTileKeys * (c0 + i)));
+      float sum;
+      const TileStep ts = full(tw0) ? tile_weights<false>(mp, tm, tw0, lo, limit, g, sum)
+                                    : tile_weights<true>(mp, tm, tw0, lo, limit, g, sum);
+      pw[w][0][lane] = __builtin_bit_cast(uint4, ts.phi[0]);
+      pw[w][1][lane] = __builtin_bit_cast(uint4, ts.plo[0]);
+      pw[w][2][lane] = __builtin_bit_cast(uint4, ts.phi[1]);
+      pw[w][3][lane] = __builtin_bit_cast(uint4, ts.plo[1]);
+      if (g == 0) {
+        als[r][w] = ts.alpha;
+        sms[r][w] = sum;
+      }
+    }
+    for (int i = 0; i < nt; ++i) m = max_update(m, mxs[i][r], visible(k_begin + kTileKeys * (c0 + i)));
+    // Zero fill of the chunk's V past the sequence end, in place (only a tile
+    // that is not full has such keys: a uniform branch).
+#pragma unroll
+    for (int i = 0; i < kWideChunk; ++i) {
+      if (!full(k_begin + kTileKeys * (c0 + i))) {
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            vr[i].v[ks2][hb] = v_keep(vr[i].v[ks2][hb], ((vvalid[i] >> (5 * (2 * ks2 + hb))) & 31) - 4 * g);
+      }
+    }
+    __syncthreads();
+    // C: the z chain and the value chain of dim block w, tile by tile, with
+    // no branch: a slot past the chunk (i >= nt) is a step with no visible
+    // key, which pv_block and the z update turn into the identity.
+    float alv[kWideChunk], smv[kWideChunk];
+#pragma unroll
+    for (int i = 0; i < kWideChunk; i += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&als[r][i]);
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sms[r][i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        alv[i + j] = a4[j];
+        smv[i + j] = s4[j];
+      }
+    }
+    bool vis[kWideChunk];
+#pragma unroll
+    for (int i = 0; i < kWideChunk; ++i) {
+      const int t0 = k_begin + kTileKeys * (c0 + i);
+      vis[i] = (i < nt) & (full(t0) | ((t0 <= limit) & (t0 + kTileKeys - 1 >= lo)));
+      z = vis[i] ? z_update(z, alv[i], smv[i]) : z;
+    }
+    if (w < kDimBlocks) {
+#pragma unroll
+      for (int i = 0; i < kWideChunk; ++i) {
+        TileStep ts;
+        ts.alpha = alv[i];
+        ts.any_visible = vis[i];
+        ts.phi[0] = __builtin_bit_cast(bf16x8, pw[i][0][lane]);
+        ts.plo[0] = __builtin_bit_cast(bf16x8, pw[i][1][lane]);
+        ts.phi[1] = __builtin_bit_cast(bf16x8, pw[i][2][lane]);
+        ts.plo[1] = __builtin_bit_cast(bf16x8, pw[i][3][lane]);
+        bf16x8 vf[2];
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const bf16x4 v4 = v_to_bf16(vr[i].v[ks2][hb], 4);  // already zero filled
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
+          }
+        // The masked form's final select is the identity where every key is
+        // visible, so one form serves full and masked tiles.
+        u = pv_block<true>(u, vf, ts);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(vr, vvalid, c0 + kWideChunk);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the next chunk rewrites the LDS tables
+  }
+
+  if (row_ok) {
+    const size_t row = ((size_t)b * a.max_splits + s) * a.Hq + hq;
+    if (w < kDimBlocks) *reinterpret_cast<f32x4*>(a.ws_u + row * D + 16 * w + 4 * g) = u;
+    if (w == 0 && g == 0) *reinterpret_cast<f32x2*>(a.ws_ml + row * 2) = f32x2{m, z};
+  }
+}
+
 // One wave per (sequence, query head): folds the split partials in ascending
 // split order and writes the bf16 output row.
 template <int D, bool FP8>
@@ -269,11 +521,26 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int k = 0; k < kPer; ++k) out[k] = finalize(U[k], vs, rz);
 }
 
+// Whether every split of the launch is at most kWideMaxTiles tiles long (the
+// split kernel, with the same bits, runs the others).
+static bool wide_fits(const DecodeArgs& a) {
+  int64_t len = a.split_tokens;
+  if (a.policy != 0) {
+    int k = 256 / (a.B > 0 ? a.B : 1);
+    k = k < 1 ? 1 : (k > 64 ? 64 : k);
+    len = ((a.max_seq_len + k - 1) / k + 63) / 64 * 64;
+  }
+  return len <= (int64_t)kWideMaxTiles * kTileKeys;
+}
+
 template <int D, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.Hkv * a.max_splits;
-  hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, a);
+  if (a.wide && wide_fits(a))
+    hipLaunchKernelGGL((decode_wide_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kWideWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, FP8>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, st, a);

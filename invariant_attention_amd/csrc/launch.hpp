@@ -36,6 +36,7 @@ struct DecodeArgs {
   int max_seq_len, max_splits;
   int split_tokens, policy;
   int window;                  // 0: full causal attention; w > 0: keys p - w < j <= p
+  int wide;                    // 1: decode_wide_kernel, 0: decode_split_kernel (same bits)
 };
 
 struct PrefillArgs {

@@ -64,15 +64,22 @@ __device__ __forceinline__ bf16x8 k_to_bf16(uint2 w, bool keep) {
   return r;
 }
 
-// V quad -> bf16x4; only the first nv of the 4 tokens are keys (nv may be
-// <= 0 or >= 4), the rest become +0.
-__device__ __forceinline__ bf16x4 v_to_bf16(uint2 w, int nv) {
+// V quad with only the first nv of its 4 tokens kept (nv may be <= 0 or
+// >= 4); the others become zero bits.
+__device__ __forceinline__ uint2 v_keep(uint2 w, int nv) {
   w.x = nv >= 2 ? w.x : (nv == 1 ? (w.x & 0xFFFFu) : 0u);
   w.y = nv >= 4 ? w.y : (nv == 3 ? (w.y & 0xFFFFu) : 0u);
-  return __builtin_bit_cast(bf16x4, w);
+  return w;
 }
+__device__ __forceinline__ uint32_t v_keep(uint32_t w, int nv) {
+  return nv >= 4 ? w : (nv <= 0 ? 0u : (w & ((1u << (8 * nv)) - 1u)));
+}
+
+// V quad -> bf16x4; only the first nv of the 4 tokens are keys (nv may be
+// <= 0 or >= 4), the rest become +0.
+__device__ __forceinline__ bf16x4 v_to_bf16(uint2 w, int nv) { return __builtin_bit_cast(bf16x4, v_keep(w, nv)); }
 __device__ __forceinline__ bf16x4 v_to_bf16(uint32_t w, int nv) {
-  w = nv >= 4 ? w : (nv <= 0 ? 0u : (w & ((1u << (8 * nv)) - 1u)));
+  w = v_keep(w, nv);
   const bf16x2 a = fp8x2_to_bf16(w, false), b = fp8x2_to_bf16(w, true);
   bf16x4 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];

@@ -19,7 +19,7 @@
 // them; e4m3 pages go through registers, where they are zero filled and
 // converted to bf16 (exactly).
 //   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B   (the pages' own layout)
-//   LDS V: [2 key halves][D dims][4 quads, swizzled][2 blocks] x 8 B
+//   LDS V: [2 key halves][D dims][4 quads][2 blocks] x 8 B
 // so every MFMA operand fragment is one 16-byte LDS read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,14 +48,6 @@ template <int D>
 constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
-
-// LDS V slots are 16 bytes: slot (ks2, dim, g) holds tokens 4g..4g+3 of dim
-// `dim` from page blocks 2 ks2 and 2 ks2 + 1.  The four quads of a dim sit in
-// 4 consecutive positions, swizzled: quad g of dim d is at position
-// 4 (ks2 D + d) + (g ^ ((d / 4) % 4)).  A fragment read takes dims r = 0..15
-// of one quad; without the swizzle lanes r, r + 4, r + 8, r + 12 would hit
-// the same banks.  v_quad_at gives the quad stored at position x of dim d.
-__device__ __forceinline__ int v_quad_at(int x, int dim) { return x ^ ((dim >> 2) & 3); }
 
 // Staging registers of one thread for one tile.
 //  K: the tile's K is 4 page blocks of D * 16 elements in the pages' own
@@ -108,7 +100,7 @@ __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc,
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = v_quad_at(c % 4, dim);
+    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = c % 4;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int blk = 2 * ks2 + hb;
@@ -200,14 +192,12 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
     __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
   }
   // V: load il of key half ks2 fills chunk ch = (ks2 * kVHalf + il) * 8 + w, whose
-  // dword `lane` is in position 16 ch + lane / 4 of the LDS V layout: dim
-  // 32 il + 4 w + lane / 16, quad g = ((lane / 4) % 4) ^ (w % 4) (the swizzle,
-  // as dim / 4 = ch = w mod 4), page block 2 ks2 + hb with hb = (lane / 2) % 2,
-  // tokens 4 g + 2 (lane % 2) and the next one.  The lane's source is its
-  // block's head plus a fixed offset, + 1 KiB per il.
+  // dword `lane` is in slot 16 ch + lane / 4 of the LDS V layout: dim
+  // 32 il + 4 w + lane / 16, quad g = (lane / 4) % 4, page block 2 ks2 + hb with
+  // hb = (lane / 2) % 2, tokens 4 g + 2 (lane % 2) and the next one.  The
+  // lane's source is its block's head plus a fixed offset, + 1 KiB per il.
   const int hb = (lane >> 1) & 1;
-  const uint32_t voff =
-      (uint32_t)(((4 * w + (lane >> 4)) * 16 + 4 * (((lane >> 2) & 3) ^ (w & 3)) + 2 * (lane & 1)) * 2);
+  const uint32_t voff = (uint32_t)(((4 * w + (lane >> 4)) * 16 + 4 * ((lane >> 2) & 3) + 2 * (lane & 1)) * 2);
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
     const uint8_t* src = (hb ? head(vc, tp.page[2 * ks2 + 1]) : head(vc, tp.page[2 * ks2])) + voff;
@@ -239,7 +229,7 @@ __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp,
 #pragma unroll
   for (int i = 0; i < kVSlots / kPrefillThreads; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int ks2 = c / (4 * D), g = v_quad_at(c % 4, (c / 4) % D);
+    const int ks2 = c / (4 * D), g = c % 4;
     uint4* p = reinterpret_cast<uint4*>(slot + kKBytes + (size_t)c * 16);
     uint4 v = *p;
     const bf16x4 lo = v_to_bf16(make_uint2(v.x, v.y), select4(2 * ks2, tp.valid) - 4 * g);
@@ -267,7 +257,7 @@ __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, i
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2)
     vf[ks2] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + (g ^ (r >> 2))) * 16));
+        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + g) * 16));
 }
 
 // Scores of one tile for the wave's rows, from the LDS copy of its K.

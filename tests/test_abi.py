@@ -46,6 +46,8 @@ def test_version_and_clean_error_state():
     (dict(Hq=32, Hkv=8, d=128, kv_dtype=7), "kv_dtype"),
     (dict(Hq=32, Hkv=8, d=128, split_policy=3), "split_policy"),
     (dict(Hq=32, Hkv=8, d=128, sm_scale=-1.0), "sm_scale"),
+    (dict(Hq=32, Hkv=8, d=128, sliding_window=-1), "sliding_window"),
+    (dict(Hq=32, Hkv=8, d=128, decode_kernel=3), "decode_kernel"),
 ])
 def test_unsupported_configs_are_rejected(kw, msg):
     Hq, Hkv, d = kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d")
@@ -113,3 +115,11 @@ def test_append_and_prefill_argument_errors():
                None) == ia.IA_ERR_INVALID_ARG
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 0, 100, FAKE, None, 0,
                None) == ia.IA_ERR_INVALID_ARG  # rows but max_q_len 0
+
+
+def test_binding_constants_match_header():
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "invattn.h")).read()
+    for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT"):
+        m = re.search(name + r" = (\d+)", hdr)
+        assert m and int(m.group(1)) == getattr(ia, name), name
