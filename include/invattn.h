@@ -206,6 +206,39 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
                                 size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Batch-invariant layer operators: the other reductions of a layer, each
+ * computing an output row from its own input row in one fixed order, so a
+ * row's bits do not depend on how many rows share the call ("Deterministic
+ * inference: results independent of the batch", "Batch invariance: fixed
+ * splits": normalisation reduced by one block per row in a fixed order, and
+ * matrix multiplication without split-K; Vosti, Figure 3, the matmul
+ * contract).  Neither needs a context.  On error nothing is launched.
+ */
+
+/*
+ * RMSNorm: y[m][i] = bf16((x[m][i] * r_m) * w[i]), r_m = 1 / sqrt(mean_i
+ * x[m][i]^2 + eps), fp32 arithmetic; the sum of squares of a row runs in one
+ * workgroup in a fixed order.
+ *   x       dev [M][H] bf16, 16-byte aligned
+ *   weight  dev [H] bf16
+ *   out     dev [M][H] bf16 (may not alias x)
+ *   H       a multiple of 8, 8 <= H <= 16384; eps finite, >= 0
+ */
+ia_status ia_rmsnorm(const void* x, const void* weight, int32_t M, int32_t H, float eps, void* out, void* stream);
+
+/*
+ * C = A W^T: c[m][n] = bf16(sum_k a[m][k] w[n][k]), fp32 accumulation.  One
+ * tile shape for every call (256 x 128 outputs, 64-wide K steps) and no
+ * split-K: each output is one accumulation over k in ascending order, so a
+ * row of C depends on its row of A and on W only, never on M.
+ *   a  dev [M][K] bf16 (row-major activations, one row per token)
+ *   w  dev [N][K] bf16 (a linear layer's weight, one row per output feature)
+ *   c  dev [M][N] bf16
+ *   N  a positive multiple of 128; K a positive multiple of 64; M >= 0
+ */
+ia_status ia_gemm_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, void* c, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host page table with prefix sharing (host memory only; one pool is not
  * thread safe).  Vosti §4.1-4.3, Figure 2:
  *  - a cached page is reused only for the token prefix that produced it: a

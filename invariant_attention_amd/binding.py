@@ -36,7 +36,7 @@ EXPORTS = [
     "ia_prefill_workspace_bytes", "ia_kv_append", "ia_paged_attn_decode", "ia_paged_attn_prefill",
     "ia_pool_create", "ia_pool_destroy", "ia_seq_begin", "ia_seq_append_tokens", "ia_seq_reserve",
     "ia_seq_commit", "ia_seq_block_table", "ia_seq_len", "ia_seq_end", "ia_pool_evict", "ia_pool_page_refs",
-    "ia_pool_page_published", "ia_pool_num_free",
+    "ia_pool_page_published", "ia_pool_num_free", "ia_rmsnorm", "ia_gemm_bf16",
 ]
 
 
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
         "ia_pool_page_refs": ([vp, i32], i32),
         "ia_pool_page_published": ([vp, i32], i32),
         "ia_pool_num_free": ([vp], i32),
+        "ia_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp, vp], ctypes.c_int),
+        "ia_gemm_bf16": ([vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -193,6 +195,21 @@ def ia_paged_attn_prefill(ctx: Context, q, cu_q_lens, seq_lens, k_cache, v_cache
                                         int(k_cache.shape[0]), _p(k_scale), _p(v_scale), _p(block_table),
                                         int(block_table.shape[1]), B, int(q.shape[0]), int(max_q_len),
                                         int(max_seq_len), _p(out), _p(workspace), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------- layer operators
+
+def ia_rmsnorm(x, weight, eps: float, out, stream=None) -> None:
+    """out[m] = RMSNorm(x[m]) * weight for x, out [M][H] bf16 and weight [H] bf16."""
+    M, H = int(x.shape[0]), int(x.shape[1])
+    _check(load().ia_rmsnorm(_p(x), _p(weight), M, H, float(eps), _p(out), _stream(stream)))
+
+
+def ia_gemm_bf16(a, w, out, stream=None) -> None:
+    """out = a @ w^T for a [M][K], w [N][K], out [M][N] (bf16)."""
+    M, K = int(a.shape[0]), int(a.shape[1])
+    N = int(w.shape[0])
+    _check(load().ia_gemm_bf16(_p(a), _p(w), M, N, K, _p(out), _stream(stream)))
 
 
 # --------------------------------------------------------------- page pool

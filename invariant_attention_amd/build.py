@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libinvattn.so")
-SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "capi.hip", "pool.cpp"]
+SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "layer_ops.hip", "capi.hip", "pool.cpp"]
 HEADERS = ["arith.hpp", "pages.hpp", "launch.hpp", "errors.hpp"]
 
 # -ffp-contract=off: no implicit FMA contraction -- the arithmetic order is the one

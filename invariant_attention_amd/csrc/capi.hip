@@ -282,4 +282,35 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
                     "prefill launch");
 }
 
+ia_status ia_rmsnorm(const void* x, const void* weight, int32_t M, int32_t H, float eps, void* out, void* stream) {
+  if (M < 0) return fail(IA_ERR_INVALID_ARG, "M must be >= 0 (got %d)", M);
+  if (H < 8 || H % 8 != 0 || H > ia::rmsnorm_max_h())
+    return fail(IA_ERR_INVALID_ARG, "H must be a multiple of 8 in [8, %d] (got %d)", ia::rmsnorm_max_h(), H);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(IA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (M == 0) return ok();
+  if (!x || !weight || !out) return fail(IA_ERR_INVALID_ARG, "x/weight/out is NULL");
+  if (!aligned(x, 16) || !aligned(weight, 16) || !aligned(out, 16))
+    return fail(IA_ERR_INVALID_ARG, "x, weight and out must be 16-byte aligned");
+  return hip_status(ia::launch_rmsnorm(static_cast<const __bf16*>(x), static_cast<const __bf16*>(weight),
+                                       static_cast<__bf16*>(out), M, H, eps, static_cast<hipStream_t>(stream)),
+                    "rmsnorm launch");
+}
+
+ia_status ia_gemm_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, void* c, void* stream) {
+  if (M < 0) return fail(IA_ERR_INVALID_ARG, "M must be >= 0 (got %d)", M);
+  if (N <= 0 || N % ia::gemm_tile_n() != 0)
+    return fail(IA_ERR_INVALID_ARG, "N must be a positive multiple of %d (got %d)", ia::gemm_tile_n(), N);
+  if (K <= 0 || K % ia::gemm_tile_k() != 0)
+    return fail(IA_ERR_INVALID_ARG, "K must be a positive multiple of %d (got %d)", ia::gemm_tile_k(), K);
+  if (M == 0) return ok();
+  if (!a || !w || !c) return fail(IA_ERR_INVALID_ARG, "a/w/c is NULL");
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16))
+    return fail(IA_ERR_INVALID_ARG, "a, w and c must be 16-byte aligned");
+  if ((int64_t)(N / ia::gemm_tile_n()) * ceil_div(M, ia::gemm_tile_m()) >= ((int64_t)1 << 31))
+    return fail(IA_ERR_INVALID_ARG, "grid too large");
+  return hip_status(ia::launch_gemm(static_cast<const __bf16*>(a), static_cast<const __bf16*>(w),
+                                    static_cast<__bf16*>(c), M, N, K, static_cast<hipStream_t>(stream)),
+                    "gemm launch");
+}
+
 }  // extern "C"

@@ -65,4 +65,12 @@ hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st)
 // ceil(max_q_len / this) row blocks per (sequence, kv head)).
 int prefill_positions_per_block(int group);
 
+// Layer operators (layer_ops.hip).
+hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, int H, float eps, hipStream_t st);
+hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st);
+int gemm_tile_m();
+int gemm_tile_n();
+int gemm_tile_k();
+int rmsnorm_max_h();
+
 }  // namespace ia

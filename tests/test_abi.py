@@ -123,3 +123,27 @@ def test_binding_constants_match_header():
     for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT"):
         m = re.search(name + r" = (\d+)", hdr)
         assert m and int(m.group(1)) == getattr(ia, name), name
+
+
+@pytest.mark.parametrize("M,H,eps,msg", [(4, 12, 1e-5, "multiple of 8"), (4, 0, 1e-5, "multiple of 8"),
+                                         (4, 16392, 1e-5, "multiple of 8"), (4, 64, -1.0, "eps"),
+                                         (4, 64, float("inf"), "eps"), (-1, 64, 1e-5, "M must"),
+                                         (4, 64, 1e-5, "NULL")])
+def test_rmsnorm_argument_errors_launch_nothing(M, H, eps, msg):
+    lib = ia.load()
+    st = lib.ia_rmsnorm(None, None, M, H, eps, None, None)
+    assert st == ia.IA_ERR_INVALID_ARG and msg in lib.ia_last_error().decode()
+
+
+@pytest.mark.parametrize("M,N,K,msg", [(4, 100, 64, "N must"), (4, 0, 64, "N must"), (4, 128, 96, "K must"),
+                                       (4, 128, 0, "K must"), (-2, 128, 64, "M must"), (4, 128, 64, "NULL")])
+def test_gemm_argument_errors_launch_nothing(M, N, K, msg):
+    lib = ia.load()
+    st = lib.ia_gemm_bf16(None, None, M, N, K, None, None)
+    assert st == ia.IA_ERR_INVALID_ARG and msg in lib.ia_last_error().decode()
+
+
+def test_layer_ops_empty_batch_is_a_noop_without_pointers():
+    lib = ia.load()
+    assert lib.ia_rmsnorm(None, None, 0, 64, 1e-5, None, None) == ia.IA_OK
+    assert lib.ia_gemm_bf16(None, None, 0, 128, 64, None, None) == ia.IA_OK
