@@ -228,13 +228,13 @@ ia_status ia_rmsnorm(const void* x, const void* weight, int32_t M, int32_t H, fl
 
 /*
  * C = A W^T: c[m][n] = bf16(sum_k a[m][k] w[n][k]), fp32 accumulation.  One
- * tile shape for every call (256 x 128 outputs, 64-wide K steps) and no
+ * tile shape for every call (256 x 256 outputs, 32-wide K steps) and no
  * split-K: each output is one accumulation over k in ascending order, so a
  * row of C depends on its row of A and on W only, never on M.
  *   a  dev [M][K] bf16 (row-major activations, one row per token)
  *   w  dev [N][K] bf16 (a linear layer's weight, one row per output feature)
  *   c  dev [M][N] bf16
- *   N  a positive multiple of 128; K a positive multiple of 64; M >= 0
+ *   N  a positive multiple of 256; K a positive multiple of 32; M >= 0
  */
 ia_status ia_gemm_bf16(const void* a, const void* w, int32_t M, int32_t N, int32_t K, void* c, void* stream);
 

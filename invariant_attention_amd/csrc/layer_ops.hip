@@ -12,12 +12,12 @@
 // depend on nothing but the row.
 //
 // GEMM.  C[M][N] = A[M][K] W[N][K]^T, bf16 in, fp32 accumulation, bf16 out.
-// One tile shape for every call: 256 x 128 outputs per workgroup, 64-wide
-// K steps, 4 waves of 128 x 64, v_mfma_f32_32x32x16_bf16.  Every output
-// element is one MFMA accumulator chain over k = 0, 16, 32, ... in order, so
-// its bits depend on its row of A and its row of W only -- not on M, on the
-// row's place in a tile, or on the other rows.  K/W tiles go from memory
-// straight into a 3-slot LDS ring (global_load_lds), two K steps ahead.
+// One tile shape for every call: 256 x 256 outputs per workgroup, 32-wide
+// K steps, 8 waves of 128 x 64 (two per SIMD), v_mfma_f32_32x32x16_bf16.  Every output element is one MFMA accumulator chain
+// over k = 0, 16, 32, ... in order, so its bits depend on its row of A and
+// its row of W only -- not on M, on the row's place in a tile, or on the
+// other rows.  A/W tiles go from memory straight into a 4-slot LDS ring
+// (global_load_lds), three K steps ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,43 +88,45 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const __bf16* __r
 
 // --------------------------------------------------------------------- GEMM
 
-constexpr int kBM = 256, kBN = 128, kBK = 64;
-constexpr int kGemmWaves = 4;
-constexpr int kStages = 3;
-constexpr int kRowBytes = kBK * 2;                   // one tile row: 64 bf16 = 8 chunks of 16 B
-constexpr int kATileBytes = kBM * kRowBytes;         // 32 KiB
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kGemmWaves = 8;
+constexpr int kStages = 4;
+constexpr int kChunks = kBK / 8;                     // 16-byte chunks (8 k) per tile row
+constexpr int kRowBytes = kBK * 2;                   // 64 B
+constexpr int kRowsPerCopy = 1024 / kRowBytes;       // rows one 1 KiB copy fills: 16
+constexpr int kATileBytes = kBM * kRowBytes;         // 16 KiB
 constexpr int kBTileBytes = kBN * kRowBytes;         // 16 KiB
 constexpr int kStageBytes = kATileBytes + kBTileBytes;
-constexpr int kALoads = kBM / 8 / kGemmWaves;       // 1 KiB copies per wave per stage (8 rows each)
-constexpr int kBLoads = kBN / 8 / kGemmWaves;
-constexpr int kLoadsPerStage = kALoads + kBLoads;    // 12
+constexpr int kALoads = kBM / kRowsPerCopy / kGemmWaves;  // copies per wave per stage
+constexpr int kBLoads = kBN / kRowsPerCopy / kGemmWaves;
+constexpr int kLoadsPerStage = kALoads + kBLoads;         // 4
 
-// A tile row holds its 8 chunks (16 B = 8 k) at positions c ^ ((row >> 1) & 7),
-// so the 16 rows a quarter-wave reads for one chunk fall on 16 distinct bank
-// groups.
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+// A tile row holds its 4 chunks at positions c ^ ((row >> 2) & 3), so the 16
+// rows a quarter-wave reads for one chunk fall on 16 distinct bank groups
+// (rows are 64 B: 4 rows span the 64 banks).
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
-// Copy i of wave w fills tile rows 8 (i * 4 + w) .. +7; lane l writes row
-// + l / 8, position l % 8, from chunk swz(row, l % 8) of that row.  Rows past
+// Copy i of wave w fills tile rows 16 (i * 4 + w) .. +15; lane l writes row
+// + l / 4, position l % 4, from chunk swz(row, l % 4) of that row.  Rows past
 // M read row M - 1 (never stored).
 __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const __bf16* wt, int M, int K, int m0,
                                            int n0, int kt, int w, int lane) {
   const int k0 = kt * kBK;
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
-    const int r0 = (i * kGemmWaves + w) * 8;
-    const int row = r0 + (lane >> 3);
+    const int r0 = (i * kGemmWaves + w) * kRowsPerCopy;
+    const int row = r0 + lane / kChunks;
     int m = m0 + row;
     m = m < M ? m : M - 1;
-    const __bf16* src = a + (size_t)m * K + k0 + 8 * swz(row, lane & 7);
+    const __bf16* src = a + (size_t)m * K + k0 + 8 * swz(row, lane % kChunks);
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + r0 * kRowBytes), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < kBLoads; ++i) {
-    const int r0 = (i * kGemmWaves + w) * 8;
-    const int row = r0 + (lane >> 3);
-    const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * swz(row, lane & 7);
+    const int r0 = (i * kGemmWaves + w) * kRowsPerCopy;
+    const int row = r0 + lane / kChunks;
+    const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * swz(row, lane % kChunks);
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + kATileBytes + r0 * kRowBytes), 16, 0, 0);
   }
 }
@@ -133,21 +135,23 @@ __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const
 // copies of later steps may stay in flight), then meets the other waves.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(N == 0 || N == kLoadsPerStage, "wait counts");
+  static_assert(kLoadsPerStage == 4 && (N == 0 || N == 4 || N == 8), "wait counts");
   if constexpr (N == 0)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4)
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
-    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(64 * kGemmWaves, 1) void gemm_kernel(const __bf16* __restrict__ a,
+__global__ __launch_bounds__(64 * kGemmWaves) void gemm_kernel(const __bf16* __restrict__ a,
                                                                   const __bf16* __restrict__ wt,
                                                                   __bf16* __restrict__ c, int M, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;  // the wave's 128 x 64 block of the tile
+  const int wm = w >> 2, wn = w & 3;  // the wave's 128 x 64 block of the tile
   const int ntn = N / kBN;
   const int n0 = (blockIdx.x % ntn) * kBN;
   const int m0 = (blockIdx.x / ntn) * kBM;
@@ -160,21 +164,24 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void gemm_kernel(const __bf16* 
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = lf32x16{};
 
-  gemm_issue(slot(0), a, wt, M, K, m0, n0, 0, w, lane);
-  if (KT > 1) gemm_issue(slot(1), a, wt, M, K, m0, n0, 1, w, lane);
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) gemm_issue(slot(s), a, wt, M, K, m0, n0, s, w, lane);
   const int r32 = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT)
+    // Copies in flight after this step's: those of steps kt+1 and kt+2.
+    if (kt + 2 < KT)
+      stage_barrier<2 * kLoadsPerStage>();
+    else if (kt + 1 < KT)
       stage_barrier<kLoadsPerStage>();
     else
       stage_barrier<0>();
-    if (kt + 2 < KT) gemm_issue(slot(kt + 2), a, wt, M, K, m0, n0, kt + 2, w, lane);
+    if (kt + 3 < KT) gemm_issue(slot(kt + 3), a, wt, M, K, m0, n0, kt + 3, w, lane);
     const uint8_t* sa = slot(kt);
     const uint8_t* sb = sa + kATileBytes;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = 2 * ks + kh;  // the lane's 8 k of this 16-k step
-      lbf16x8 af[4], bf[2];
+    // Operand fragments of the lane's 8 k of each 16-k step; the reads of
+    // step ks + 1 are issued before the MFMAs of step ks.
+    auto frags = [&](int ks, lbf16x8 (&af)[4], lbf16x8 (&bf)[2]) {
+      const int ch = 2 * ks + kh;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int row = wm * 128 + mi * 32 + r32;
@@ -185,25 +192,48 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void gemm_kernel(const __bf16* 
         const int row = wn * 64 + ni * 32 + r32;
         bf[ni] = *reinterpret_cast<const lbf16x8*>(sb + row * kRowBytes + swz(row, ch) * 16);
       }
+    };
+    lbf16x8 af[2][4], bf[2][2];
+    frags(0, af[0], bf[0]);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (ks + 1 < kBK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bf[ks & 1][ni], acc[mi][ni], 0, 0, 0);
+      if (ks + 1 < kBK / 16) {
+        // One LDS read after each of the first 6 MFMAs of this step.
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
     }
   }
   // Output element (row, col) of a 32 x 32 accumulator sits in lane col +
-  // 32 * ((row / 4) % 2), register 4 * (row / 8) + row % 4.
+  // 32 * ((row / 4) % 2), register 4 * (row / 8) + row % 4.  A wave whose
+  // 128 rows all exist stores without row checks.
+  const int mw = m0 + wm * 128;
+  auto store = [&](bool check) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
-        const int n = n0 + wn * 64 + ni * 32 + r32;
-        if (m < M) c[(size_t)m * N + n] = (__bf16)acc[mi][ni][i];
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int m = mw + mi * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
+          const int n = n0 + wn * 64 + ni * 32 + r32;
+          if (!check || m < M) c[(size_t)m * N + n] = (__bf16)acc[mi][ni][i];
+        }
+  };
+  if (mw + 128 <= M)
+    store(false);
+  else
+    store(true);
 }
 
 }  // namespace
@@ -221,7 +251,7 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
 
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const int lds = kStages * kStageBytes;  // 144 KiB
+  const int lds = kStages * kStageBytes;  // 128 KiB
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;

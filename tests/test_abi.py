@@ -135,8 +135,9 @@ def test_rmsnorm_argument_errors_launch_nothing(M, H, eps, msg):
     assert st == ia.IA_ERR_INVALID_ARG and msg in lib.ia_last_error().decode()
 
 
-@pytest.mark.parametrize("M,N,K,msg", [(4, 100, 64, "N must"), (4, 0, 64, "N must"), (4, 128, 96, "K must"),
-                                       (4, 128, 0, "K must"), (-2, 128, 64, "M must"), (4, 128, 64, "NULL")])
+@pytest.mark.parametrize("M,N,K,msg", [(4, 100, 64, "N must"), (4, 0, 64, "N must"), (4, 128, 64, "N must"),
+                                       (4, 256, 48, "K must"), (4, 256, 0, "K must"), (-2, 256, 64, "M must"),
+                                       (4, 256, 64, "NULL")])
 def test_gemm_argument_errors_launch_nothing(M, N, K, msg):
     lib = ia.load()
     st = lib.ia_gemm_bf16(None, None, M, N, K, None, None)
@@ -146,4 +147,4 @@ def test_gemm_argument_errors_launch_nothing(M, N, K, msg):
 def test_layer_ops_empty_batch_is_a_noop_without_pointers():
     lib = ia.load()
     assert lib.ia_rmsnorm(None, None, 0, 64, 1e-5, None, None) == ia.IA_OK
-    assert lib.ia_gemm_bf16(None, None, 0, 128, 64, None, None) == ia.IA_OK
+    assert lib.ia_gemm_bf16(None, None, 0, 256, 64, None, None) == ia.IA_OK

@@ -60,8 +60,8 @@ def test_rmsnorm_row_alone_equals_row_in_batch():
         assert np.array_equal(_bits(one), _bits(full[r:r + 1]))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (7, 256, 128), (300, 384, 4096), (257, 1024, 1024),
-                                   (256, 128, 14336), (513, 6144, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 32), (3, 256, 64), (7, 256, 128), (300, 512, 4096),
+                                   (257, 1024, 1024), (256, 256, 14336), (513, 6144, 4096)])
 def test_gemm_matches_oracle(M, N, K):
     a = li.activations(3, 0, M, K)
     w = li.gemm_weight(3, N, K)
@@ -87,7 +87,7 @@ def test_gemm_row_alone_equals_row_in_batch(N, K):
 
 def test_gemm_row_bits_do_not_depend_on_its_neighbours():
     # The same row placed among different neighbours at different slots gives the same bits.
-    K, N = 512, 384
+    K, N = 512, 512
     w = li.gemm_weight(5, N, K).to(DEV)
     probe = li.activations(5, 0, 1, K)
     ref = None
