@@ -88,18 +88,32 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const __bf16* __r
 
 // --------------------------------------------------------------------- GEMM
 
-constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kGemmWaves = 8;
-constexpr int kStages = 4;
-constexpr int kChunks = kBK / 8;                     // 16-byte chunks (8 k) per tile row
-constexpr int kRowBytes = kBK * 2;                   // 64 B
-constexpr int kRowsPerCopy = 1024 / kRowBytes;       // rows one 1 KiB copy fills: 16
-constexpr int kATileBytes = kBM * kRowBytes;         // 16 KiB
-constexpr int kBTileBytes = kBN * kRowBytes;         // 16 KiB
-constexpr int kStageBytes = kATileBytes + kBTileBytes;
-constexpr int kALoads = kBM / kRowsPerCopy / kGemmWaves;  // copies per wave per stage
-constexpr int kBLoads = kBN / kRowsPerCopy / kGemmWaves;
-constexpr int kLoadsPerStage = kALoads + kBLoads;         // 4
+constexpr int kComputeUnits = 256;              // MI355X
+constexpr int kBK = 32;                          // K step
+constexpr int kStages = 4;                       // LDS ring slots
+constexpr int kChunks = kBK / 8;                 // 16-byte chunks (8 k) per tile row
+constexpr int kRowBytes = kBK * 2;               // 64 B
+constexpr int kRowsPerCopy = 1024 / kRowBytes;   // rows one 1 KiB copy fills: 16
+
+// A workgroup tile of BM x BN outputs over WM x WN waves; each wave owns a
+// (BM / WM) x (BN / WN) block as 32 x 32 MFMA tiles.  Every configuration
+// computes each output with the same MFMA chain over k in ascending order,
+// so the choice of tile never changes a bit.
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kMI = BM / WM / 32, kNI = BN / WN / 32;
+  static constexpr int kATileBytes = BM * kRowBytes;
+  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr int kALoads = BM / kRowsPerCopy / kWaves;  // 1 KiB copies per wave per stage
+  static constexpr int kBLoads = BN / kRowsPerCopy / kWaves;
+  static constexpr int kLoadsPerStage = kALoads + kBLoads;
+  static_assert(kMI >= 1 && kNI >= 1 && kALoads >= 1 && kBLoads >= 1, "tile must divide over the waves");
+  static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BN % (kRowsPerCopy * kWaves) == 0, "copies per wave");
+};
+using BigTile = Tile<256, 256, 2, 4>;   // 8 waves of 128 x 64
+using SmallTile = Tile<64, 64, 2, 2>;   // 4 waves of 32 x 32, for calls with few big tiles
 
 // A tile row holds its 4 chunks at positions c ^ ((row >> 2) & 3), so the 16
 // rows a quarter-wave reads for one chunk fall on 16 distinct bank groups
@@ -107,15 +121,16 @@ constexpr int kLoadsPerStage = kALoads + kBLoads;         // 4
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
-// Copy i of wave w fills tile rows 16 (i * 4 + w) .. +15; lane l writes row
-// + l / 4, position l % 4, from chunk swz(row, l % 4) of that row.  Rows past
-// M read row M - 1 (never stored).
+// Copy i of wave w fills tile rows 16 (i * waves + w) .. +15; lane l writes
+// row + l / 4, position l % 4, from chunk swz(row, l % 4) of that row.  Rows
+// past M read row M - 1 (never stored).
+template <class T>
 __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const __bf16* wt, int M, int K, int m0,
                                            int n0, int kt, int w, int lane) {
   const int k0 = kt * kBK;
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int r0 = (i * kGemmWaves + w) * kRowsPerCopy;
+  for (int i = 0; i < T::kALoads; ++i) {
+    const int r0 = (i * T::kWaves + w) * kRowsPerCopy;
     const int row = r0 + lane / kChunks;
     int m = m0 + row;
     m = m < M ? m : M - 1;
@@ -123,123 +138,135 @@ __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + r0 * kRowBytes), 16, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int r0 = (i * kGemmWaves + w) * kRowsPerCopy;
+  for (int i = 0; i < T::kBLoads; ++i) {
+    const int r0 = (i * T::kWaves + w) * kRowsPerCopy;
     const int row = r0 + lane / kChunks;
     const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * swz(row, lane % kChunks);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + kATileBytes + r0 * kRowBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + T::kATileBytes + r0 * kRowBytes), 16, 0,
+                                     0);
   }
 }
 
 // Waits until this wave's copies of the step to be consumed have landed (N
-// copies of later steps may stay in flight), then meets the other waves.
+// copies of later steps may stay in flight), then meets the other waves.  The
+// copies write LDS behind the compiler's back, so the wait is explicit.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(kLoadsPerStage == 4 && (N == 0 || N == 4 || N == 8), "wait counts");
-  if constexpr (N == 0)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 4)
-    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__global__ __launch_bounds__(64 * kGemmWaves) void gemm_kernel(const __bf16* __restrict__ a,
-                                                                  const __bf16* __restrict__ wt,
-                                                                  __bf16* __restrict__ c, int M, int N, int K) {
+template <class T>
+__global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __restrict__ a,
+                                                               const __bf16* __restrict__ wt,
+                                                               __bf16* __restrict__ c, int M, int N, int K) {
+  constexpr int MI = T::kMI, NI = T::kNI, L = T::kLoadsPerStage;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 2, wn = w & 3;  // the wave's 128 x 64 block of the tile
-  const int ntn = N / kBN;
-  const int n0 = (blockIdx.x % ntn) * kBN;
-  const int m0 = (blockIdx.x / ntn) * kBM;
+  const int wm = w / T::WN, wn = w % T::WN;  // the wave's block of the tile
+  const int ntn = N / T::BN;
+  const int n0 = (blockIdx.x % ntn) * T::BN;
+  const int m0 = (blockIdx.x / ntn) * T::BM;
   const int KT = K / kBK;
-  auto slot = [&](int kt) { return lds + (kt % kStages) * kStageBytes; };
+  auto slot = [&](int kt) { return lds + (kt % kStages) * T::kStageBytes; };
 
-  lf32x16 acc[4][2];
+  lf32x16 acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = lf32x16{};
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = lf32x16{};
 
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < KT) gemm_issue(slot(s), a, wt, M, K, m0, n0, s, w, lane);
+    if (s < KT) gemm_issue<T>(slot(s), a, wt, M, K, m0, n0, s, w, lane);
   const int r32 = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
     // Copies in flight after this step's: those of steps kt+1 and kt+2.
     if (kt + 2 < KT)
-      stage_barrier<2 * kLoadsPerStage>();
+      stage_barrier<2 * L>();
     else if (kt + 1 < KT)
-      stage_barrier<kLoadsPerStage>();
+      stage_barrier<L>();
     else
       stage_barrier<0>();
-    if (kt + 3 < KT) gemm_issue(slot(kt + 3), a, wt, M, K, m0, n0, kt + 3, w, lane);
+    if (kt + 3 < KT) gemm_issue<T>(slot(kt + 3), a, wt, M, K, m0, n0, kt + 3, w, lane);
     const uint8_t* sa = slot(kt);
-    const uint8_t* sb = sa + kATileBytes;
+    const uint8_t* sb = sa + T::kATileBytes;
     // Operand fragments of the lane's 8 k of each 16-k step; the reads of
     // step ks + 1 are issued before the MFMAs of step ks.
-    auto frags = [&](int ks, lbf16x8 (&af)[4], lbf16x8 (&bf)[2]) {
+    auto frags = [&](int ks, lbf16x8 (&af)[MI], lbf16x8 (&bf)[NI]) {
       const int ch = 2 * ks + kh;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 128 + mi * 32 + r32;
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * (32 * MI) + mi * 32 + r32;
         af[mi] = *reinterpret_cast<const lbf16x8*>(sa + row * kRowBytes + swz(row, ch) * 16);
       }
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int row = wn * 64 + ni * 32 + r32;
+      for (int ni = 0; ni < NI; ++ni) {
+        const int row = wn * (32 * NI) + ni * 32 + r32;
         bf[ni] = *reinterpret_cast<const lbf16x8*>(sb + row * kRowBytes + swz(row, ch) * 16);
       }
     };
-    lbf16x8 af[2][4], bf[2][2];
+    lbf16x8 af[2][MI], bf[2][NI];
     frags(0, af[0], bf[0]);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       if (ks + 1 < kBK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bf[ks & 1][ni], acc[mi][ni], 0, 0, 0);
-      if (ks + 1 < kBK / 16) {
-        // One LDS read after each of the first 6 MFMAs of this step.
+      if constexpr (MI * NI >= MI + NI) {
+        if (ks + 1 < kBK / 16) {
+          // One LDS read after each of the first MFMAs of this step.
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int i = 0; i < MI + NI; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
   }
   // Output element (row, col) of a 32 x 32 accumulator sits in lane col +
   // 32 * ((row / 4) % 2), register 4 * (row / 8) + row % 4.  A wave whose
-  // 128 rows all exist stores without row checks.
-  const int mw = m0 + wm * 128;
+  // rows all exist stores without row checks.
+  const int mw = m0 + wm * (32 * MI);
   auto store = [&](bool check) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int m = mw + mi * 32 + 8 * (i / 4) + 4 * kh + (i % 4);
-          const int n = n0 + wn * 64 + ni * 32 + r32;
+          const int n = n0 + wn * (32 * NI) + ni * 32 + r32;
           if (!check || m < M) c[(size_t)m * N + n] = (__bf16)acc[mi][ni][i];
         }
   };
-  if (mw + 128 <= M)
+  if (mw + 32 * MI <= M)
     store(false);
   else
     store(true);
 }
 
+template <class T>
+hipError_t launch_gemm_t(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
+  const int lds = kStages * T::kStageBytes;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<T>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = (int64_t)(N / T::BN) * ((M + T::BM - 1) / T::BM);
+  hipLaunchKernelGGL(gemm_kernel<T>, dim3((unsigned)tiles), dim3(64 * T::kWaves), lds, st, a, wt, c, M, N, K);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int gemm_tile_m() { return kBM; }
-int gemm_tile_n() { return kBN; }
+int gemm_tile_m() { return BigTile::BM; }
+int gemm_tile_n() { return BigTile::BN; }
 int gemm_tile_k() { return kBK; }
 int rmsnorm_max_h() { return kNormThreads * kNormMaxChunks * 8; }
 
@@ -249,15 +276,13 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
   return hipGetLastError();
 }
 
+// The big tile when it gives at least one workgroup per compute unit, else the
+// small one (same bits either way).
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const int lds = kStages * kStageBytes;  // 128 KiB
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  const int64_t tiles = (int64_t)(N / kBN) * ((M + kBM - 1) / kBM);
-  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(64 * kGemmWaves), lds, st, a, wt, c, M, N, K);
-  return hipGetLastError();
+  const int64_t big = (int64_t)(N / BigTile::BN) * ((M + BigTile::BM - 1) / BigTile::BM);
+  if (big >= kComputeUnits) return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
+  return launch_gemm_t<SmallTile>(a, wt, c, M, N, K, st);
 }
 
 }  // namespace ia

@@ -61,7 +61,8 @@ def test_rmsnorm_row_alone_equals_row_in_batch():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 32), (3, 256, 64), (7, 256, 128), (300, 512, 4096),
-                                   (257, 1024, 1024), (256, 256, 14336), (513, 6144, 4096)])
+                                   (257, 1024, 1024), (256, 256, 14336), (513, 6144, 4096),
+                                   (3000, 6144, 256)])
 def test_gemm_matches_oracle(M, N, K):
     a = li.activations(3, 0, M, K)
     w = li.gemm_weight(3, N, K)
@@ -72,12 +73,13 @@ def test_gemm_matches_oracle(M, N, K):
     assert ok, f"max abs err {err}, worst err/bound {ratio}"
 
 
-@pytest.mark.parametrize("N,K", [(256, 1024), (6144, 4096)])
-def test_gemm_row_alone_equals_row_in_batch(N, K):
-    # Rows at every position class of the 256-row tile (first, last, both halves of a 32-row
-    # MFMA block, a ragged last tile), computed alone and inside batches of 300 and 1000 rows.
+@pytest.mark.parametrize("N,K,Ms", [(256, 1024, (300, 1000)), (6144, 4096, (300, 4096))])
+def test_gemm_row_alone_equals_row_in_batch(N, K, Ms):
+    # Rows at every position class of a tile (first, last, both halves of a 32-row MFMA block, a
+    # ragged last tile), computed alone and inside larger batches.  A lone row runs on the small
+    # 64 x 64 tile; the 4096-row call at N = 6144 runs on the 256 x 256 tile.
     w = li.gemm_weight(4, N, K).to(DEV)
-    for M in (300, 1000):
+    for M in Ms:
         a = li.activations(4, 0, M, K)
         full = _gemm(a.to(DEV), w)
         for r in sorted({0, 1, 3, 4, 7, 8, 31, 32, 127, 128, 255, 256, 257, M - 1}):
