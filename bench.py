@@ -509,6 +509,64 @@ def prefill_tflops(steps: int, warmup: int):
             "algorithmic_flops": flops}
 
 
+def layer_ops(steps: int, warmup: int):
+    """The batch-invariant layer operators against torch's (vendor library) kernels on Llama-3-8B /
+    Qwen3-8B layer shapes: the fixed-tile GEMM at a prefill chunk (M = 8192) and a decode batch
+    (M = 256), RMSNorm at hidden 4096; plus whether torch's matmul keeps a row's bits when the
+    batch changes."""
+    from synth import layer_inputs as li
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = {"gemm": {}}
+    shapes = {"qkv_proj": (6144, 4096), "down_proj": (4096, 14336)}
+    for M in (8192, 256):
+        for name, (N, K) in shapes.items():
+            a = li.activations(SEED, 0, M, K).to(DEV)
+            w = li.gemm_weight(SEED, N, K).to(DEV)
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+            ms = timed(lambda: ia.ia_gemm_bf16(a, w, c))
+            ms_t = timed(lambda: torch.matmul(a, w.t()))
+            fl = 2.0 * M * N * K
+            key = f"{name}_M{M}"
+            out["gemm"][key] = {"M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                                "frac_of_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                                "torch_ms": round(ms_t, 4), "torch_tflops": round(fl / ms_t / 1e9, 1),
+                                "time_vs_torch": round(ms / ms_t, 3)}
+            log(f"gemm {key}: {out['gemm'][key]}")
+    # Row 0 alone vs inside the 8192-row batch: ours by construction, torch's as it happens.
+    N, K = shapes["qkv_proj"]
+    a = li.activations(SEED, 0, 8192, K).to(DEV)
+    w = li.gemm_weight(SEED, N, K).to(DEV)
+    c_full = torch.empty((8192, N), dtype=torch.bfloat16, device=DEV)
+    c_one = torch.empty((1, N), dtype=torch.bfloat16, device=DEV)
+    ia.ia_gemm_bf16(a, w, c_full)
+    ia.ia_gemm_bf16(a[:1].contiguous(), w, c_one)
+    t_full = torch.matmul(a, w.t())
+    t_one = torch.matmul(a[:1].contiguous(), w.t())
+    torch.cuda.synchronize()
+    out["row0_alone_equals_in_batch"] = {"ours": bool(torch.equal(c_full[:1].view(torch.int16), c_one.view(torch.int16))),
+                                         "torch": bool(torch.equal(t_full[:1].view(torch.int16), t_one.view(torch.int16)))}
+    x = li.activations(SEED, 0, 8192, 4096).to(DEV)
+    g = li.norm_weight(SEED, 4096).to(DEV)
+    y = torch.empty_like(x)
+    ms = timed(lambda: ia.ia_rmsnorm(x, g, 1e-5, y))
+    out["rmsnorm"] = {"M": 8192, "H": 4096, "ms": round(ms, 4), "gbs": round(2 * x.numel() * 2 / ms / 1e6, 1),
+                      "frac_of_hbm_peak": round(2 * x.numel() * 2 / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    log(f"rmsnorm: {out['rmsnorm']}; row 0 alone = in batch: {out['row0_alone_equals_in_batch']}")
+    return out
+
+
 def cpu_baseline(lens, shape, target_s=10.0, sample=32):
     """The fp64 oracle, as it stands, on a bounded sample of the headline workload: the first
     `sample` sequences' decode rows (all query heads), on all host threads, repeated until about
@@ -590,6 +648,7 @@ def main():
     ap.add_argument("--suite", action="store_true", help="also time the long-context and shared-prefix points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time the prefill workload only (for profilers)")
+    ap.add_argument("--layer-only", action="store_true", help="time the layer operators only (for profilers)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     args = ap.parse_args()
@@ -610,6 +669,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_tflops(args.steps, args.warmup)}), flush=True)
+        return
+    if args.layer_only:
+        print(json.dumps({"layer_ops": layer_ops(args.steps, args.warmup)}), flush=True)
         return
     shape = wl.LLAMA3_8B
     lens = wl.uniform_lens(SEED, args.batch, 512, 8192)
@@ -673,6 +735,7 @@ def main():
         torch.cuda.empty_cache()
         result["prefill"] = prefill_tflops(max(3, args.steps // 4), 1)
         log(f"prefill: {result['prefill']}")
+        result["layer_ops"] = layer_ops(max(3, args.steps // 4), 2)
         if args.suite:
             result["suite"] = suite(args)
     if not args.no_cpu_baseline:
