@@ -14,13 +14,16 @@
 // Staging.  Tiles pass through two LDS slots: while the waves compute tile t,
 // the workgroup's loads of tile t+1 are in flight into the other slot; one
 // barrier per tile.  bf16 pages go from memory straight into LDS
-// (global_load_lds: K in 1 KiB runs, V dword by dword into its slot layout),
-// with a zero fill of the keys past the sequence end only in a tile that has
-// them; e4m3 pages go through registers, where they are zero filled and
-// converted to bf16 (exactly).
-//   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B   (the pages' own layout)
-//   LDS V: [2 key halves][D dims][4 quads][2 blocks] x 8 B
-// so every MFMA operand fragment is one 16-byte LDS read.
+// (global_load_lds, 1 KiB runs of K and V), with a zero fill of the keys past
+// the sequence end only in a tile that has them; e4m3 pages go through
+// registers, where they are zero filled and converted to bf16 (exactly).
+// Both tensors keep the pages' own layout:
+//   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B
+//   LDS V: [4 blocks][D dims][2 halves] x 16 B   (8 tokens per half)
+// except that in V the two halves of a dim row trade places when bit 3 of
+// the dim is set, so a wave's 8-byte fragment reads hit 64 distinct banks.
+// A K operand fragment is one 16-byte LDS read; a V fragment is two 8-byte
+// reads (tokens 4g..4g+3 of two page blocks).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,24 +52,26 @@ constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
 
-// Staging registers of one thread for one tile.
+// LDS position of V half `half` of dim `dim` in a page block's copy: halves
+// swap when bit 3 of the dim is set (and the map is its own inverse).
+__device__ __forceinline__ int v_half_pos(int dim, int half) { return half ^ ((dim >> 3) & 1); }
+
+// Staging registers of one thread for one tile (e4m3 pages).
 //  K: the tile's K is 4 page blocks of D * 16 elements in the pages' own
 //     order; 16-byte units of it are copied as they are (kKUnits units).
-//  V: slot (ks2, dim, g) of the LDS layout holds tokens 4g..4g+3 of dim `dim`
-//     from page block 2 ks2 (8 bytes as bf16) followed by the same tokens of
-//     block 2 ks2 + 1; a thread gathers both quads and writes the slot whole,
-//     so every LDS write of a wave is one contiguous run.
+//  V: LDS unit c of the V region (16 bytes of bf16 = 8 tokens of one dim)
+//     comes from the 8 codes of the same tokens in the page.
 template <int D, bool FP8>
 struct Stage {
   static constexpr int kKUnits = kTileKeys * D * Raw<FP8>::kElemBytes / 16;
   static constexpr int kKPer = (kKUnits + kPrefillThreads - 1) / kPrefillThreads;
-  static constexpr int kVSlots = 2 * D * 4;
-  static constexpr int kVPer = kVSlots / kPrefillThreads;
-  static_assert(kKUnits % 64 == 0 && kVSlots % kPrefillThreads == 0, "tile must divide over the waves");
+  static constexpr int kVUnits = 4 * D * 2;
+  static constexpr int kVPer = kVUnits / kPrefillThreads;
+  static_assert(kKUnits % 64 == 0 && kVUnits % kPrefillThreads == 0, "tile must divide over the waves");
   uint4 k[kKPer];
   int knv[kKPer];                  // keys in the unit's page block
   typename Raw<FP8>::V v[kVPer][2];
-  int vnv[kVPer][2];               // keys among each quad's 4 tokens
+  int vnv[kVPer];                  // keys among the unit's 8 tokens
 };
 
 // x[blk] for a lane-varying blk in 0..3, as two levels of selects on its bits
@@ -100,14 +105,13 @@ __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc,
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int ks2 = c / (4 * D), dim = (c / 4) % D, g = c % 4;
+    const int blk = c / (2 * D), dim = (c % (2 * D)) >> 1, half = v_half_pos(dim, c & 1);
+    st.vnv[i] = select4(blk, tp.valid) - 8 * half;
+    const uint8_t* base = vc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int blk = 2 * ks2 + hb;
-      st.vnv[i][hb] = select4(blk, tp.valid) - 4 * g;
-      const uint8_t* base = vc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
-      st.v[i][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(base + (uint32_t)((dim * 16 + 4 * g) * EB));
-    }
+    for (int q4 = 0; q4 < 2; ++q4)
+      st.v[i][q4] =
+          *reinterpret_cast<const typename Raw<FP8>::V*>(base + (uint32_t)((dim * 16 + 8 * half + 4 * q4) * EB));
   }
 }
 
@@ -156,8 +160,8 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const bf16x4 lo = v_to_bf16(st.v[i][0], st.vnv[i][0]);
-    const bf16x4 hi = v_to_bf16(st.v[i][1], st.vnv[i][1]);
+    const bf16x4 lo = v_to_bf16(st.v[i][0], st.vnv[i]);
+    const bf16x4 hi = v_to_bf16(st.v[i][1], st.vnv[i] - 4);
     const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
     *reinterpret_cast<uint4*>(lds + kKBytes + (size_t)c * 16) = make_uint4(l.x, l.y, h.x, h.y);
   }
@@ -165,10 +169,10 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
 
 // ---- bf16 tiles: direct global -> LDS loads (global_load_lds) --------------
 // The data moves from the pages to LDS without passing through registers.
-// Each instruction of a wave fills a contiguous LDS run in lane order: 16
-// bytes per lane for K (the LDS K layout is the pages' own, so a page block
-// is four 1 KiB copies), 4 bytes per lane for V (each lane picks the dword its
-// position in the V slot layout needs, from either of the slot's two pages).
+// Each instruction of a wave fills a contiguous 1 KiB LDS run, 16 bytes per
+// lane in lane order.  A page block's K or V (D x 16 values) is contiguous in
+// its page, so a tile is 4 blocks x D/32 such copies per tensor; the lanes of
+// a V copy fetch their 16 bytes from the position v_half_pos maps them to.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
@@ -176,37 +180,22 @@ template <int D>
 __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
                                              int kvh, int Hkv, int w, int lane) {
   constexpr size_t kHeadBytes = (size_t)D * 16 * 2;          // one (page, kv head) block
-  constexpr int kKChunks = kTileKeys * D * 2 / 1024;          // 1 KiB K chunks per tile
-  constexpr int kVChunks = kTileKeys * D * 2 / 256;           // 256 B V chunks per tile (one dword per lane)
+  constexpr int kChunks = kTileKeys * D * 2 / 1024;           // 1 KiB copies per tile and tensor
   constexpr int kKBytes = kTileKeys * D * 2;
-  constexpr int kVHalf = kVChunks / kPrefillWaves / 2;        // V loads of a wave per key half
-  static_assert(kKChunks % kPrefillWaves == 0 && kVChunks % (2 * kPrefillWaves) == 0, "chunks must divide over waves");
-  static_assert(kVHalf * 1024 <= 4096, "V load offsets must fit the instruction offset");
+  static_assert(kChunks % kPrefillWaves == 0, "chunks must divide over waves");
   auto head = [&](const uint8_t* pool, int pg) { return pool + ((size_t)pg * Hkv + kvh) * kHeadBytes; };
 #pragma unroll
-  for (int i = 0; i < kKChunks / kPrefillWaves; ++i) {
+  for (int i = 0; i < kChunks / kPrefillWaves; ++i) {
     const int ch = i * kPrefillWaves + w;  // wave-uniform
-    const int blk = ch / (kKChunks / 4), part = ch % (kKChunks / 4);
+    const int blk = ch / (kChunks / 4), part = ch % (kChunks / 4);
     const int pg = blk == 0 ? tp.page[0] : (blk == 1 ? tp.page[1] : (blk == 2 ? tp.page[2] : tp.page[3]));
-    const uint8_t* src = head(kc, pg) + part * 1024 + lane * 16;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
-  }
-  // V: load il of key half ks2 fills chunk ch = (ks2 * kVHalf + il) * 8 + w, whose
-  // dword `lane` is in slot 16 ch + lane / 4 of the LDS V layout: dim
-  // 32 il + 4 w + lane / 16, quad g = (lane / 4) % 4, page block 2 ks2 + hb with
-  // hb = (lane / 2) % 2, tokens 4 g + 2 (lane % 2) and the next one.  The
-  // lane's source is its block's head plus a fixed offset, + 1 KiB per il.
-  const int hb = (lane >> 1) & 1;
-  const uint32_t voff = (uint32_t)(((4 * w + (lane >> 4)) * 16 + 4 * ((lane >> 2) & 3) + 2 * (lane & 1)) * 2);
-#pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2) {
-    const uint8_t* src = (hb ? head(vc, tp.page[2 * ks2 + 1]) : head(vc, tp.page[2 * ks2])) + voff;
-#pragma unroll
-    for (int il = 0; il < kVHalf; ++il) {
-      const int ch = (ks2 * kVHalf + il) * kPrefillWaves + w;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + il * 1024), (lds_void_t*)(slot + kKBytes + ch * 256), 4, 0,
-                                       0);
-    }
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(kc, pg) + part * 1024 + lane * 16),
+                                     (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
+    // V: LDS unit u = 64 part + lane of the block = dim u / 2, position u % 2.
+    const int u = part * 64 + lane;
+    const int dim = u >> 1;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, pg) + dim * 32 + v_half_pos(dim, u & 1) * 16),
+                                     (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
   }
 }
 
@@ -217,7 +206,7 @@ template <int D>
 __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp, int tid) {
   constexpr int kKBytes = kTileKeys * D * 2;
   constexpr int kKUnits = kKBytes / 16;
-  constexpr int kVSlots = 2 * D * 4;
+  constexpr int kVUnits = 4 * D * 2;
   static_assert(kKUnits % kPrefillThreads == 0, "K units must divide over the threads");
 #pragma unroll
   for (int i = 0; i < kKUnits / kPrefillThreads; ++i) {
@@ -227,15 +216,14 @@ __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp,
       *reinterpret_cast<uint4*>(slot + (size_t)c * 16) = make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
-  for (int i = 0; i < kVSlots / kPrefillThreads; ++i) {
+  for (int i = 0; i < kVUnits / kPrefillThreads; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int ks2 = c / (4 * D), g = c % 4;
+    const int blk = c / (2 * D), dim = (c % (2 * D)) >> 1;
+    const int nv = select4(blk, tp.valid) - 8 * v_half_pos(dim, c & 1);
     uint4* p = reinterpret_cast<uint4*>(slot + kKBytes + (size_t)c * 16);
-    uint4 v = *p;
-    const bf16x4 lo = v_to_bf16(make_uint2(v.x, v.y), select4(2 * ks2, tp.valid) - 4 * g);
-    const bf16x4 hi = v_to_bf16(make_uint2(v.z, v.w), select4(2 * ks2 + 1, tp.valid) - 4 * g);
-    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
-    *p = make_uint4(l.x, l.y, h.x, h.y);
+    const uint4 v = *p;
+    const uint2 lo = v_keep(make_uint2(v.x, v.y), nv), hi = v_keep(make_uint2(v.z, v.w), nv - 4);
+    *p = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
@@ -251,13 +239,19 @@ __device__ __forceinline__ void lds_k_block(const uint8_t* lds, int blk, int r, 
     kf[ks] = __builtin_bit_cast(
         bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + r) * 16));
 }
+// V^T fragment of dim block mb for key half ks2: tokens 4g..4g+3 of page
+// blocks 2 ks2 and 2 ks2 + 1 for dim 16 mb + r (8 bytes from each).
 template <int D>
 __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, int g, bf16x8 (&vf)[2]) {
   constexpr int kKBytes = kTileKeys * D * 2;
+  const int dim = 16 * mb + r;
+  const uint8_t* base = lds + kKBytes + dim * 32 + v_half_pos(dim, g >> 1) * 16 + 8 * (g & 1);
 #pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2)
-    vf[ks2] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + ((size_t)(ks2 * D + 16 * mb + r) * 4 + g) * 16));
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(base + (2 * ks2) * D * 32);
+    const uint2 hi = *reinterpret_cast<const uint2*>(base + (2 * ks2 + 1) * D * 32);
+    vf[ks2] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
 }
 
 // Scores of one tile for the wave's rows, from the LDS copy of its K.

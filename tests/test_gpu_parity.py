@@ -158,3 +158,35 @@ def test_fp8_prefill_matches_oracle():
     out = gs.prefill(ctx, pages, q, cu, layout, lens)
     ok, err, ratio = gs.within_tolerance(out, ref)
     assert ok, f"max abs err {err}, worst err/bound {ratio}"
+
+# ------------------------------------------------- unwritten page slots
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_unwritten_slots_never_reach_the_output(fp8):
+    # Keys past a sequence's end read as zero values and masked scores (Vosti App. A.2,
+    # zero-padded out-of-range loads): slots of the pool that no kv_append wrote may hold
+    # anything, here NaN, and decode and prefill must give the same bits as on a zeroed pool.
+    shape = wl.LLAMA3_8B if not fp8 else wl.LLAMA31_70B
+    lens = [2300, 600, 37, 1, 65]
+    q_lens = [300, 600, 37, 1, 1]
+    scales = wl.fp8_scales(5, shape.Hkv, False) if fp8 else (None, None)
+    seqs = wl.make_sequences(lens)
+    layout = wl.layout_pages(3, lens, shape.P)
+    ctx = gs.make_ctx(shape, fp8=fp8)
+    outs = []
+    for poison in (False, True):
+        pages = gs.DevicePages(shape, layout.num_pages, fp8, *scales)
+        if poison:
+            for pool in (pages.k, pages.v):
+                if fp8:
+                    pool.fill_(0x7F)  # e4m3 NaN
+                else:
+                    pool.view(torch.int16).fill_(0x7FC0)  # bf16 quiet NaN
+        gs.fill_sequences(ctx, pages, seqs, layout, 0)
+        q, cu = osd.queries(shape, seqs, 0, q_lens)
+        dq, _ = osd.queries(shape, seqs, 0, [1] * len(lens))
+        outs.append((gs.prefill(ctx, pages, q, cu, layout, lens), gs.decode(ctx, pages, dq, layout, lens)))
+    (p0, d0), (p1, d1) = outs
+    assert np.isfinite(p1.float().cpu().numpy()).all() and np.isfinite(d1.float().cpu().numpy()).all()
+    assert np.array_equal(gs.bits(p0), gs.bits(p1))
+    assert np.array_equal(gs.bits(d0), gs.bits(d1))
