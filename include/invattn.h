@@ -134,7 +134,9 @@ const char* ia_version(void);
 
 /* Device workspace (bytes) that ia_paged_attn_decode needs for `batch`
  * sequences of at most max_seq_len keys: one fp32 partial state
- * (max, sum, head_dim accumulators) per (sequence, split, query head). */
+ * (max, sum, head_dim accumulators) per (sequence, split, query head), and
+ * one int32 per (sequence, split) for the order in which the split units are
+ * dispatched (longest first; the order never changes a result bit). */
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
 /* Device workspace for ia_paged_attn_prefill (0: prefill folds its split

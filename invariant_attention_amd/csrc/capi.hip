@@ -59,12 +59,15 @@ int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len)
   return k < by_tile ? k : by_tile;
 }
 
-// Bytes of the two workspace arrays (U accumulators, then (m, z) pairs).
-void decode_ws_parts(const ia_ctx* ctx, int64_t B, int64_t max_seq_len, size_t* u_bytes, size_t* ml_bytes) {
+// Bytes of the three workspace arrays (U accumulators, (m, z) pairs, then the
+// dispatch order of the split units).
+void decode_ws_parts(const ia_ctx* ctx, int64_t B, int64_t max_seq_len, size_t* u_bytes, size_t* ml_bytes,
+                     size_t* order_bytes) {
   const int64_t ms = decode_max_splits(ctx, B, max_seq_len);
   const int64_t rows = B * ms * ctx->cfg.num_q_heads;
   *u_bytes = align_up((size_t)rows * ctx->cfg.head_dim * sizeof(float));
   *ml_bytes = align_up((size_t)rows * 2 * sizeof(float));
+  *order_bytes = align_up((size_t)(B * ms) * sizeof(int32_t));
 }
 
 ia_status hip_status(hipError_t e, const char* what) {
@@ -135,9 +138,9 @@ void ia_destroy(ia_ctx* ctx) { delete ctx; }
 
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len) {
   if (!ctx || batch <= 0 || max_seq_len <= 0) return 0;
-  size_t u, ml;
-  decode_ws_parts(ctx, batch, max_seq_len, &u, &ml);
-  return u + ml;
+  size_t u, ml, ord;
+  decode_ws_parts(ctx, batch, max_seq_len, &u, &ml, &ord);
+  return u + ml + ord;
 }
 
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
@@ -192,10 +195,11 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   if (max_seq_len <= 0) return fail(IA_ERR_INVALID_ARG, "max_seq_len must be positive (got %d)", max_seq_len);
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  size_t u_bytes, ml_bytes;
-  decode_ws_parts(ctx, B, max_seq_len, &u_bytes, &ml_bytes);
-  if (!workspace || ws_bytes < u_bytes + ml_bytes)
-    return fail(IA_ERR_WORKSPACE_TOO_SMALL, "decode workspace needs %zu bytes (got %zu)", u_bytes + ml_bytes, ws_bytes);
+  size_t u_bytes, ml_bytes, order_bytes;
+  decode_ws_parts(ctx, B, max_seq_len, &u_bytes, &ml_bytes, &order_bytes);
+  const size_t need = u_bytes + ml_bytes + order_bytes;
+  if (!workspace || ws_bytes < need)
+    return fail(IA_ERR_WORKSPACE_TOO_SMALL, "decode workspace needs %zu bytes (got %zu)", need, ws_bytes);
   if (!aligned(workspace, 16)) return fail(IA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const int64_t ms = decode_max_splits(ctx, B, max_seq_len);
   if ((int64_t)B * ctx->cfg.num_kv_heads * ms >= ((int64_t)1 << 31))
@@ -211,6 +215,7 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.out = static_cast<__bf16*>(out);
   a.ws_u = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes);
+  a.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + u_bytes + ml_bytes);
   a.c = ctx->c;
   a.B = B;
   a.Hq = ctx->cfg.num_q_heads;

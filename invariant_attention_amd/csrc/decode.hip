@@ -143,14 +143,22 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  // Split-major order: every sequence's first split is dispatched before any
-  // second split, and so on.  Early splits are whole (S keys) while last
-  // splits are partial, so the longest units start first and the short ones
-  // fill the tail (longest-first list scheduling).
+  // Which (sequence, split) the workgroup runs: the order list of
+  // decode_order_kernel when the launch has one (longest units first), else
+  // split-major (every sequence's first split before any second split, and
+  // so on).  The choice moves work between workgroups, never changes it.
   const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
-  const int b = (unit / a.Hkv) % a.B;
-  const int s = unit / a.Hkv / a.B;
+  int b, s;
+  if (a.order) {
+    const int e = a.order[unit / a.Hkv];
+    if (e < 0) return;  // past the listed units; uniform over the workgroup
+    b = e / a.max_splits;
+    s = e % a.max_splits;
+  } else {
+    b = (unit / a.Hkv) % a.B;
+    s = unit / a.Hkv / a.B;
+  }
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int S = split_len(a.policy, a.split_tokens, n, a.B);
   const int nsplit = (n + S - 1) / S;
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
   // block at head_dim 64 load a copy they never use, so that every wave
   // issues the same loads and each wait covers exactly the loads it needs).
   const int wd = w % kDimBlocks;
-  const int unit = blockIdx.x;  // the split kernel's unit order
+  const int unit = blockIdx.x;  // split-major, as the split kernel without an order list
   const int kvh = unit % a.Hkv;
   const int b = (unit / a.Hkv) % a.B;
   const int s = unit / a.Hkv / a.B;
@@ -521,6 +529,59 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int k = 0; k < kPer; ++k) out[k] = finalize(U[k], vs, rz);
 }
 
+// ---------------------------------------------------------------------------
+// Longest-first dispatch of the split units.
+//
+// A launch's units are whole splits (S keys) except each sequence's last
+// split, which holds the remaining n mod S keys.  Workgroups start in grid
+// order as compute units free up, so a long unit that starts late sets the
+// end of the launch.  This one-workgroup kernel writes the list the split
+// kernel takes its units from: every whole split first, then the last splits
+// by decreasing length in 64-key tiles, then -1 for the unused grid entries.
+// Entry = b * max_splits + s.  Places inside the list are claimed with LDS
+// atomics, so the order among sequences may differ between calls; it decides
+// only which workgroup runs a unit, never what the unit computes.  Batches
+// above kOrderMaxB, and launches with fewer than kOrderMinUnits units (where
+// most units start at once), keep the split-major grid order.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxB = kOrderThreads;
+constexpr int kOrderMinUnits = 2048;
+constexpr int kOrderBuckets = 64;  // last-split lengths, in tiles; longer ones share bucket 0
+
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a) {
+  __shared__ int full_next;             // next free place in the whole-split part
+  __shared__ int next[kOrderBuckets];   // last splits per bucket, then each bucket's next place
+  __shared__ int listed;
+  const int tid = threadIdx.x;
+  if (tid == 0) full_next = 0;
+  if (tid < kOrderBuckets) next[tid] = 0;
+  __syncthreads();
+  int nf = 0, q = -1;  // q: bucket of the last split (0 = longest), -1 = none
+  if (tid < a.B) {
+    const int n = clamp_len(a.seq_lens[tid], a.max_seq_len);
+    const int S = split_len(a.policy, a.split_tokens, n, a.B);
+    nf = n / S;
+    const int tiles = (n - nf * S + kTileKeys - 1) / kTileKeys;
+    if (tiles > 0) q = kOrderBuckets - (tiles < kOrderBuckets ? tiles : kOrderBuckets);
+  }
+  const int f0 = nf > 0 ? atomicAdd(&full_next, nf) : 0;
+  if (q >= 0) atomicAdd(&next[q], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = full_next;
+    for (int i = 0; i < kOrderBuckets; ++i) {
+      const int c = next[i];
+      next[i] = run;
+      run += c;
+    }
+    listed = run;
+  }
+  __syncthreads();
+  for (int s = 0; s < nf; ++s) a.order[f0 + s] = tid * a.max_splits + s;
+  if (q >= 0) a.order[atomicAdd(&next[q], 1)] = tid * a.max_splits + nf;
+  for (int i = listed + tid; i < a.B * a.max_splits; i += kOrderThreads) a.order[i] = -1;
+}
+
 // Whether every split of the launch is at most kWideMaxTiles tiles long (the
 // split kernel, with the same bits, runs the others).
 static bool wide_fits(const DecodeArgs& a) {
@@ -537,10 +598,19 @@ template <int D, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.Hkv * a.max_splits;
-  if (a.wide && wide_fits(a))
+  if (a.wide && wide_fits(a)) {
     hipLaunchKernelGGL((decode_wide_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kWideWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, a);
+  } else {
+    DecodeArgs sa = a;
+    if (a.order && a.B <= kOrderMaxB && units >= kOrderMinUnits) {
+      hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, st, a);
+      const hipError_t oe = hipGetLastError();
+      if (oe != hipSuccess) return oe;
+    } else {
+      sa.order = nullptr;
+    }
+    hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, sa);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, FP8>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, st, a);

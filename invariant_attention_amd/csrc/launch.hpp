@@ -30,6 +30,7 @@ struct DecodeArgs {
   __bf16* out;                 // [B][Hq][D]
   float* ws_u;                 // [B][max_splits][Hq][D]
   float* ws_ml;                // [B][max_splits][Hq][2]
+  int32_t* order;              // [B * max_splits] dispatch order of the split units (workspace)
   float c;                     // fp32(sm_scale * log2 e)
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;

@@ -58,16 +58,18 @@ def test_unsupported_configs_are_rejected(kw, msg):
 
 def test_workspace_size_formula():
     ctx = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048))
-    # B * ceil(max_len / S) * Hq rows of (d + 2) floats, each array rounded up to 256 bytes
+    # B * ceil(max_len / S) * Hq rows of (d + 2) floats, plus one int32 per (sequence, split) for
+    # the dispatch order, each array rounded up to 256 bytes
     got = ia.ia_decode_workspace_bytes(ctx, 256, 8192)
     rows = 256 * 4 * 32
     up = lambda x: (x + 255) // 256 * 256
-    assert got == up(rows * 128 * 4) + up(rows * 2 * 4)
+    assert got == up(rows * 128 * 4) + up(rows * 2 * 4) + up(256 * 4 * 4)
     assert ia.ia_decode_workspace_bytes(ctx, 0, 8192) == 0
     bc = ia.Context(ia.make_config(32, 8, 128, split_policy=ia.IA_SPLIT_BY_COUNT))
     # split-by-count: at most min(64, 256 // B) pieces, and no more than one per 64-key tile
-    assert ia.ia_decode_workspace_bytes(bc, 1, 64) == up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4)
-    assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
+    assert ia.ia_decode_workspace_bytes(bc, 1, 64) == up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4) + up(4)
+    assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
+                                                          + up(4 * 64 * 4))
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
