@@ -128,6 +128,7 @@ def summarize_profile(trace_dir, pmc_dir):
     stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     split = [r for r in stats if "decode_split_kernel<128, false>" in r["Name"]]
     merge = [r for r in stats if "decode_merge_kernel<128, false>" in r["Name"]]
+    order = [r for r in stats if "decode_order_kernel" in r["Name"]]
     avg_ns = float(split[0]["AverageNs"])
 
     def pmc_mean(kind, counter, kernel):
@@ -163,12 +164,13 @@ def summarize_profile(trace_dir, pmc_dir):
         "| kernel | calls | average ns | min ns | max ns |",
         "|---|---|---|---|---|",
     ]
-    for r in split + merge:
+    for r in order + split + merge:
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
     lines += [
         "",
         f"Achieved from the trace: {alg / avg_ns:.1f} GB/s = {alg / avg_ns / HBM_PEAK_GBS:.4f} of the 8 TB/s HBM peak "
-        "(split kernel alone; the split merge adds about 6 us per call).",
+        "(split kernel alone; the dispatch-order kernel before it and the split merge after it add a few us "
+        "each per call).",
         "",
         "## HBM traffic (rocprofv3 --pmc, one counter per run)",
         "",
