@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from invariant_attention_amd import binding as ia
 from synth import workloads as wl
 from tests import gpu_side as gs
 from tests import oracle_side as osd
@@ -200,3 +201,40 @@ def test_split_by_count_breaks_batch_invariance():
     full_c = w.decode_rows()
     w.ctx = keep
     assert not _eq(full_c[0:1], alone_c), "split-by-count unexpectedly batch invariant"
+
+
+# ------------------------------------------------- dispatch order of the units
+# Large launches take their units from a longest-first list built on the device
+# (at least 2048 units, at most 1024 sequences); smaller ones, larger batches and
+# the wide kernel use split-major grid order.  Which workgroup runs a unit must
+# never change a bit.
+
+ORDER_SHAPE = wl.AttnShape(Hq=16, Hkv=8, d=64, P=16, S=256)
+
+
+@pytest.mark.parametrize("by_count,window", [(False, 0), (False, 700), (True, 0)],
+                         ids=["fixed", "fixed-window", "by-count"])
+def test_ordered_dispatch_changes_no_bit(by_count, window):
+    shape = ORDER_SHAPE
+    lens = wl.uniform_lens(31, 300, 1, 2048)  # 300 x 8 kv heads x up to 8 splits: an ordered launch
+    w = World(shape, lens, by_count=by_count)
+    w.ctx = gs.make_ctx(shape, by_count=by_count, window=window)
+    ordered = w.decode_rows()
+    w_wide = object.__new__(World)
+    w_wide.__dict__.update(w.__dict__)
+    w_wide.ctx = gs.make_ctx(shape, by_count=by_count, window=window, decode_kernel=ia.IA_DECODE_WIDE)
+    assert _eq(w_wide.decode_rows(), ordered)  # same splits, split-major order
+    if not by_count:  # by-count splits depend on the batch size by design
+        for b in (0, 7, 150, 299):  # each alone: 8 units or fewer, split-major order
+            assert _eq(w.decode_rows([b]), ordered[[b]]), f"row {b}"
+
+
+def test_batches_above_the_order_limit_keep_their_bits():
+    shape = wl.AttnShape(Hq=4, Hkv=2, d=64, P=16, S=64)
+    lens = wl.uniform_lens(32, 1100, 1, 700)  # 1100 sequences: above the order list's batch limit
+    w = World(shape, lens)
+    full = w.decode_rows()
+    idx = list(range(0, 1100, 2))  # 550 sequences x 2 kv heads x up to 11 splits: an ordered launch
+    assert _eq(w.decode_rows(idx), full[idx])
+    for b in (0, 549, 1099):
+        assert _eq(w.decode_rows([b]), full[[b]]), f"row {b}"
