@@ -209,6 +209,9 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
     };
     lbf16x8 af[2][MI], bf[2][NI];
     frags(0, af[0], bf[0]);
+    // The two waves of a SIMD meet at every stage barrier; a wave issuing its
+    // MFMAs takes precedence over the other's fragment reads and copies.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       if (ks + 1 < kBK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
@@ -229,6 +232,7 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   // Output element (row, col) of a 32 x 32 accumulator sits in lane col +
   // 32 * ((row / 4) % 2), register 4 * (row / 8) + row % 4.  A wave whose
