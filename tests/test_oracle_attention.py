@@ -18,6 +18,7 @@ import torch.nn.functional as F
 from oracle import oracle
 from synth import workloads as wl
 from tests import oracle_side as osd
+from tests import golden
 
 SHAPES = [
     wl.AttnShape(Hq=8, Hkv=2, d=64, P=16, S=128),   # the tiny decode shape
@@ -172,18 +173,29 @@ def test_fixed_split_merge_agrees_with_plain(oracle_lib, split):
 
 
 def test_vosti_figure4_prefill_row_equals_decode(oracle_lib):
-    # Vosti, Figure 4: prefill with q_len = k_len = 6 on pages P7, P9, P2 (two tokens a page) and
-    # decode with q_len = 1, k_len = 4 on pages P4, P8 both compute logical position p = 3.
-    shape = wl.AttnShape(Hq=2, Hkv=1, d=16, P=2, S=64)
+    # Vosti, Figure 4 (tests/golden/vosti_figure4_positions.txt): a prefill invocation on pages
+    # P7, P9, P2 and a decode invocation on pages P4, P8 (two tokens a page) reach the same logical
+    # position, and their selected rows are bitwise equal.
+    fix = golden.load("vosti_figure4_positions.txt")
+    pre_f, dec_f = golden.one(fix, "prefill"), golden.one(fix, "decode")
+    P, pos = int(golden.one(fix, "page_size")), int(golden.one(fix, "position"))
+    for f in (pre_f, dec_f):
+        assert int(f["k_len"]) - int(f["q_len"]) + int(f["row"]) == pos
+        assert len(golden.ints(f["pages"])) == -(-int(f["k_len"]) // P)
+    shape = wl.AttnShape(Hq=2, Hkv=1, d=16, P=P, S=64)
+    n_pre, n_dec = int(pre_f["k_len"]), int(dec_f["k_len"])
     rng = np.random.default_rng(4)
-    K = _bf16(rng.standard_normal((6, 1, 16)))
-    V = _bf16(rng.standard_normal((6, 1, 16)))
-    Q = _bf16(rng.standard_normal((6, 2, 16)))
-    pre = _oracle_on_rows(shape, K, V, Q, q_len=6, pages=np.array([7, 9, 2]))
-    dec = _oracle_on_rows(shape, K[:4], V[:4], Q[3:4], q_len=1, pages=np.array([4, 8]))
-    assert np.array_equal(pre[3], dec[0])
+    K = _bf16(rng.standard_normal((n_pre, 1, 16)))
+    V = _bf16(rng.standard_normal((n_pre, 1, 16)))
+    Q = _bf16(rng.standard_normal((n_pre, 2, 16)))
+    pre = _oracle_on_rows(shape, K, V, Q, q_len=int(pre_f["q_len"]), pages=np.array(golden.ints(pre_f["pages"])))
+    q_dec = Q[pos - int(dec_f["row"]):pos - int(dec_f["row"]) + int(dec_f["q_len"])]
+    dec = _oracle_on_rows(shape, K[:n_dec], V[:n_dec], q_dec, q_len=int(dec_f["q_len"]),
+                          pages=np.array(golden.ints(dec_f["pages"])))
+    equal = np.array_equal(pre[int(pre_f["row"])], dec[int(dec_f["row"])])
+    assert equal == golden.flag(golden.one(fix, "outputs")["bitwise_equal"])
     # and a wrong position rule (p = i) would have given row 0 instead:
-    assert not np.array_equal(pre[0], dec[0])
+    assert not np.array_equal(pre[0], dec[int(dec_f["row"])])
 
 
 @pytest.mark.parametrize("pow2", [True, False])

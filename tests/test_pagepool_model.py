@@ -6,6 +6,7 @@ import random
 import pytest
 
 from oracle.pagepool import ERR_OUT_OF_PAGES, OK, PagePool
+from tests import golden
 
 a, b, c, d, e, f = 1, 2, 3, 4, 5, 6
 
@@ -19,34 +20,60 @@ def _run(pool, tokens):
     return seq, cached, slots
 
 
+def _refs(text):
+    return {k: int(v) for k, v in (kv.split(":") for kv in text.split(","))}
+
+
 def test_vosti_figure2_share_retain_evict_reuse():
-    pool = PagePool(num_pages=8, page_size=2)
-    A, cached_a, _ = _run(pool, [a, b, c, d])
+    # Stage by stage against the reference counts Vosti Figure 2 prints
+    # (tests/golden/vosti_figure2_page_states.txt).  The pool hands out its own page ids, so the
+    # figure's pages are matched by role: the shared [a, b] page and the two suffix pages.
+    fix = golden.load("vosti_figure2_page_states.txt")
+    P = int(golden.one(fix, "page_size"))
+    tok = {ch: i + 1 for i, ch in enumerate("abcdef")}
+    req = {k: [tok[t] for t in v.split(",")] for r in fix["request"] for k, v in r.items()}
+    stages = {int(st[""]): st for st in fix["stage"]}
+    pool = PagePool(num_pages=8, page_size=P)
+    A, cached_a, _ = _run(pool, req["A"])
     assert cached_a == 0
-    B, cached_b, slots_b = _run(pool, [a, b, e, f])
-    # 1: A and B live, sharing the [a, b] page (refs 2) with private suffix pages (refs 1)
+    B, cached_b, slots_b = _run(pool, req["B"])
     shared, a_suffix = pool.seq_block_table(A)
     shared_b, b_suffix = pool.seq_block_table(B)
-    assert cached_b == 2 and shared_b == shared
-    assert pool.page_refs(shared) == 2 and pool.page_refs(a_suffix) == 1 and pool.page_refs(b_suffix) == 1
-    assert all(s // 2 == b_suffix for s in slots_b)  # B writes only its private page
+    role = {"shared": shared, "A_suffix": a_suffix, "B_suffix": b_suffix}
+    fig = {}
+    for pg in fix["page"]:
+        name = next(k for k in pg if k != "role")
+        fig[name] = role[pg["role"]]
+
+    def check(stage):
+        for name, refs in _refs(stages[stage]["refs"]).items():
+            assert pool.page_refs(fig[name]) == refs, (stage, name)
+            assert pool.is_published(fig[name]), (stage, name)
+        if "free" in stages[stage]:
+            assert not pool.is_published(fig[stages[stage]["free"]]), stage
+
+    # 1: A and B live, sharing the [a, b] page with private suffix pages
+    assert cached_b == P and shared_b == shared
+    check(1)
+    assert all(s // P == b_suffix for s in slots_b)  # B writes only its private page
     # 2: both finish; pages are retained with refs 0
     pool.seq_end(A)
     pool.seq_end(B)
-    for pg in (shared, a_suffix, b_suffix):
-        assert pool.page_refs(pg) == 0 and pool.is_published(pg)
+    check(2)
     # 3: evict one page -- a leaf goes (A's suffix, released first); the shared parent stays
     assert pool.evict(1) == 1
-    assert not pool.is_published(a_suffix) and pool.is_published(shared) and pool.is_published(b_suffix)
+    check(3)
     leaves = [p for p in pool.published if pool.page_refs(p) == 0 and not pool._has_published_child(p)]
     assert shared not in leaves  # cannot go while B's suffix refers to it
-    # 4: C = [a, b, c, d] reuses the shared page and recomputes [c, d] into fresh storage
-    st, C, cached_c = pool.seq_begin([a, b, c, d])
-    assert st == OK and cached_c == 2
-    assert pool.seq_block_table(C) == [shared] and pool.page_refs(shared) == 1
-    st, slots = pool.seq_reserve(C, 2)
-    assert st == OK and len(slots) == 2 and slots[0] // 2 == slots[1] // 2
-    assert not pool.is_published(slots[0] // 2)
+    # 4: C reuses the shared page and recomputes its suffix into fresh storage
+    st, C, cached_c = pool.seq_begin(req["C"])
+    assert st == OK and cached_c == int(stages[4]["cached"])
+    assert pool.seq_block_table(C) == [shared]
+    check(4)
+    n_new = len(stages[4]["recomputed"].split(","))
+    st, slots = pool.seq_reserve(C, n_new)
+    assert st == OK and len(slots) == n_new and len({s // P for s in slots}) == 1
+    assert not pool.is_published(slots[0] // P)
 
 
 def test_fully_cached_prompt_recomputes_last_page():
