@@ -617,10 +617,13 @@ def suite(args):
     # 16 decode rows at 32768 context + batch 1 vs 64.
     shape = wl.QWEN3_235B
     w = DecodeWorld(shape, [32768] * 64)
+    split_ctx = make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT)
     for B in (1, 16, 64):
         s_ms, d_ms = time_steps(DecodeRunner(w, range(B)), args.steps, args.warmup, with_append=False)
+        s2, d2 = time_steps(DecodeRunner(w, range(B), split_ctx), args.steps, args.warmup, with_append=False)
         out[f"qwen3-235b-32k-B{B}"] = {"decode_ms": round(d_ms, 4),
-                                       "gbs": round(w.kv_bytes(range(B)) / d_ms / 1e6, 1)}
+                                       "gbs": round(w.kv_bytes(range(B)) / d_ms / 1e6, 1),
+                                       "split_kernel_decode_ms": round(d2, 4)}
         log(f"qwen3-235b 32k B={B}: {out[f'qwen3-235b-32k-B{B}']}")
     del w
     torch.cuda.empty_cache()
@@ -722,15 +725,20 @@ def main():
             log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
         result["batches"] = batches
         result["split_by_count"] = by_count
-        # The second, bitwise-equivalent decode kernel at the small batches it was built for.
-        wide_ctx = make_ctx(shape, decode_kernel=ia.IA_DECODE_WIDE)
-        wide = {}
-        for B in (1, 8, 64):
-            s_ms, d_ms = time_steps(DecodeRunner(world, range(B), wide_ctx), args.steps, args.warmup)
-            wide[str(B)] = {"step_ms": round(s_ms, 4), "decode_ms": round(d_ms, 4),
-                            "gbs": round(world.kv_bytes(range(B)) / (s_ms * 1e-3) / 1e9, 1)}
-            log(f"B={B}: wide decode kernel {wide[str(B)]['gbs']} GB/s")
-        result["wide_kernel"] = wide
+        # The bitwise-equivalent decode kernels at small batches: the split kernel alone, the spread
+        # pair alone (the automatic choice runs it up to 512 split units) and the wide kernel.
+        kern = {}
+        for name, kid in (("split", ia.IA_DECODE_SPLIT), ("spread", ia.IA_DECODE_SPREAD), ("wide", ia.IA_DECODE_WIDE)):
+            kctx = make_ctx(shape, decode_kernel=kid)
+            kern[name] = {}
+            for B in (1, 8, 16, 32, 64):
+                if name == "wide" and B not in (1, 8, 64):
+                    continue
+                s_ms, d_ms = time_steps(DecodeRunner(world, range(B), kctx), args.steps, args.warmup)
+                kern[name][str(B)] = {"decode_ms": round(d_ms, 4),
+                                      "decode_gbs": round(world.kv_bytes(range(B)) / (d_ms * 1e-3) / 1e9, 1)}
+            log(f"{name} decode kernel: {kern[name]}")
+        result["decode_kernels"] = kern
         probes = [0, 1, 37, 100, 200, args.batch - 1]
         eq, tot = invariance_pairs(world, world.ctx, probes)
         eq_c, tot_c = invariance_pairs(world, bc_ctx, probes)

@@ -79,21 +79,31 @@ typedef enum { IA_KV_BF16 = 0, IA_KV_FP8_E4M3 = 1 } ia_kv_dtype;
  * fixed split. */
 typedef enum { IA_SPLIT_FIXED = 0, IA_SPLIT_BY_COUNT = 1 } ia_split_policy;
 
-/* Which decode kernel runs the splits.  Both produce bit-identical partial
+/* Which decode kernel runs the splits.  All produce bit-identical partial
  * states and outputs (the same operations on the same operands in the same
- * order) and differ only in schedule.  IA_DECODE_SPLIT walks each split's
- * tiles as one chain of steps (4 waves per split).  IA_DECODE_WIDE lets 8
- * waves score and weight 8 tiles of a split at once -- the running maximum
- * before each tile is an exact fmaxf fold of the earlier tiles' maxima -- and
- * keeps only the z and value updates as a chain.  This is the pages' open
- * item of dispatch among bitwise-equivalent kernels (Vosti, Discussion,
+ * order) and differ only in schedule.  This is the pages' open item of
+ * dispatch among bitwise-equivalent kernels (Vosti, Discussion,
  * "Cross-kernel relational verification": one decode kernel for full waves,
- * one for partially filled waves, with the same accumulation order).  On
- * MI355X the split's K/V stream through one compute unit bounds both kernels
- * alike at small batches, so IA_DECODE_AUTO runs SPLIT; WIDE is selectable
- * and verified bit for bit against SPLIT.  WIDE takes splits of at most
- * 16384 keys; longer ones run on SPLIT (same bits). */
-typedef enum { IA_DECODE_AUTO = 0, IA_DECODE_SPLIT = 1, IA_DECODE_WIDE = 2 } ia_decode_kernel;
+ * one that gives a sequence several compute units for partially filled
+ * waves, with the same accumulation order).
+ *   IA_DECODE_SPLIT walks each split's tiles as one chain of steps on one
+ *     compute unit (4 waves per split).
+ *   IA_DECODE_WIDE lets 8 waves of one compute unit score and weight 8 tiles
+ *     of a split at once (the running maximum before a tile is an exact fmaxf
+ *     fold of the earlier tiles' maxima) and keeps only the z and value
+ *     updates as a chain.  It takes splits of at most 16384 keys; longer ones
+ *     run on SPLIT.  Selectable only: it is not faster than SPLIT.
+ *   IA_DECODE_SPREAD spreads a split over many compute units in three
+ *     launches: one wave per (split, tile) forms the tile's scores and row
+ *     maxima; one wave per (split, tile) folds the running maximum before its
+ *     tile from the earlier tiles' maxima and forms the tile's weights, alpha
+ *     and row sum; one wave per (split, 16-dim block) runs the chain of z and
+ *     value updates for its dims.  The intermediate values live in the
+ *     workspace.  Launches whose buffer would exceed 32768 (split, tile)
+ *     slots run on SPLIT.
+ *   IA_DECODE_AUTO runs SPREAD for launches of at most 64 split units
+ *     (batch x kv heads x splits of max_seq_len) and SPLIT above that. */
+typedef enum { IA_DECODE_AUTO = 0, IA_DECODE_SPLIT = 1, IA_DECODE_WIDE = 2, IA_DECODE_SPREAD = 3 } ia_decode_kernel;
 
 typedef struct {
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads, Hq / Hkv <= 16 */
@@ -134,9 +144,13 @@ const char* ia_version(void);
 
 /* Device workspace (bytes) that ia_paged_attn_decode needs for `batch`
  * sequences of at most max_seq_len keys: one fp32 partial state
- * (max, sum, head_dim accumulators) per (sequence, split, query head), and
- * one int32 per (sequence, split) for the order in which the split units are
- * dispatched (longest first; the order never changes a result bit). */
+ * (max, sum, head_dim accumulators) per (sequence, split, query head), one
+ * int32 per (sequence, split) for the order in which the split units are
+ * dispatched (longest first; the order never changes a result bit), and,
+ * when the launch runs the spread kernels, one slot per (sequence, split,
+ * kv head, tile): group x 64 fp32 scores (later the weights), and 16 row
+ * maxima and 16 (alpha, row sum) pairs.  Under IA_DECODE_AUTO a workspace large enough for the split kernel
+ * but not for the score slots runs the split kernel (the same bits). */
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
 /* Device workspace for ia_paged_attn_prefill (0: prefill folds its split

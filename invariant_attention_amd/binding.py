@@ -29,6 +29,7 @@ IA_SPLIT_BY_COUNT = 1
 IA_DECODE_AUTO = 0
 IA_DECODE_SPLIT = 1
 IA_DECODE_WIDE = 2
+IA_DECODE_SPREAD = 3
 IA_POOL_CONSTANT_HASH = 1
 
 EXPORTS = [

@@ -59,15 +59,52 @@ int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len)
   return k < by_tile ? k : by_tile;
 }
 
-// Bytes of the three workspace arrays (U accumulators, (m, z) pairs, then the
-// dispatch order of the split units).
+// The spread decode pair (decode_score_kernel + decode_value_kernel) serves
+// launches with few split units, where one compute unit per split leaves the
+// chip idle; it gives the split kernel's bits, so the choice below decides
+// speed only.  Its score buffer holds one slot per (unit, tile).
+constexpr int64_t kSpreadMaxUnits = 64;        // IA_DECODE_AUTO: at most this many split units
+constexpr int64_t kSpreadMaxSlots = 1 << 15;   // score slots: <= 128 MiB of scores at 16 rows
+
+// Tiles of the longest split a launch can have: the fixed split, or the
+// split-by-count length for the longest sequence.
+int64_t decode_split_tiles(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len) {
+  if (ctx->cfg.split_policy == IA_SPLIT_FIXED) return ctx->cfg.split_tokens / kTileKeys;
+  int64_t k = 256 / (batch > 0 ? batch : 1);
+  k = k < 1 ? 1 : (k > 64 ? 64 : k);
+  const int64_t len = ceil_div(ceil_div(max_seq_len, k), kTileKeys);
+  return len < 1 ? 1 : len;
+}
+
+// Which decode kernel a launch of this size runs: 0 split, 1 wide, 2 spread.
+int decode_kernel_for(const ia_ctx* ctx, int64_t B, int64_t max_seq_len) {
+  const int64_t units = B * ctx->cfg.num_kv_heads * decode_max_splits(ctx, B, max_seq_len);
+  const bool spread_fits = units * decode_split_tiles(ctx, B, max_seq_len) <= kSpreadMaxSlots;
+  switch (ctx->cfg.decode_kernel) {
+    case IA_DECODE_WIDE: return 1;
+    case IA_DECODE_SPLIT: return 0;
+    case IA_DECODE_SPREAD: return spread_fits ? 2 : 0;
+    default: return spread_fits && units <= kSpreadMaxUnits ? 2 : 0;
+  }
+}
+
+// Bytes of the workspace arrays: U accumulators, (m, z) pairs, the dispatch
+// order of the split units, and (spread kernels only) the score / weight
+// slots, their row maxima, and their alphas and row sums.
 void decode_ws_parts(const ia_ctx* ctx, int64_t B, int64_t max_seq_len, size_t* u_bytes, size_t* ml_bytes,
-                     size_t* order_bytes) {
+                     size_t* order_bytes, size_t* x_bytes, size_t* mx_bytes) {
   const int64_t ms = decode_max_splits(ctx, B, max_seq_len);
   const int64_t rows = B * ms * ctx->cfg.num_q_heads;
   *u_bytes = align_up((size_t)rows * ctx->cfg.head_dim * sizeof(float));
   *ml_bytes = align_up((size_t)rows * 2 * sizeof(float));
   *order_bytes = align_up((size_t)(B * ms) * sizeof(int32_t));
+  *x_bytes = *mx_bytes = 0;
+  if (decode_kernel_for(ctx, B, max_seq_len) == 2) {
+    const int64_t slots = B * ms * ctx->cfg.num_kv_heads * decode_split_tiles(ctx, B, max_seq_len);
+    *x_bytes = align_up((size_t)slots * 16 * ctx->group * 4 * sizeof(float));
+    // row maxima [slot][16], then (alpha, row sum) [slot][16][2]
+    *mx_bytes = align_up((size_t)slots * 16 * sizeof(float)) + align_up((size_t)slots * 16 * 2 * sizeof(float));
+  }
 }
 
 ia_status hip_status(hipError_t e, const char* what) {
@@ -123,7 +160,8 @@ ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "sm_scale must be finite and positive");
   if (c.sliding_window < 0)
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "sliding_window must be >= 0 (got %d)", c.sliding_window);
-  if (c.decode_kernel != IA_DECODE_AUTO && c.decode_kernel != IA_DECODE_SPLIT && c.decode_kernel != IA_DECODE_WIDE)
+  if (c.decode_kernel != IA_DECODE_AUTO && c.decode_kernel != IA_DECODE_SPLIT && c.decode_kernel != IA_DECODE_WIDE &&
+      c.decode_kernel != IA_DECODE_SPREAD)
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown decode_kernel %d", c.decode_kernel);
   ia_ctx* ctx = new (std::nothrow) ia_ctx;
   if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
@@ -138,9 +176,9 @@ void ia_destroy(ia_ctx* ctx) { delete ctx; }
 
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len) {
   if (!ctx || batch <= 0 || max_seq_len <= 0) return 0;
-  size_t u, ml, ord;
-  decode_ws_parts(ctx, batch, max_seq_len, &u, &ml, &ord);
-  return u + ml + ord;
+  size_t u, ml, ord, x, mx;
+  decode_ws_parts(ctx, batch, max_seq_len, &u, &ml, &ord, &x, &mx);
+  return u + ml + ord + x + mx;
 }
 
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
@@ -195,9 +233,16 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   if (max_seq_len <= 0) return fail(IA_ERR_INVALID_ARG, "max_seq_len must be positive (got %d)", max_seq_len);
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  size_t u_bytes, ml_bytes, order_bytes;
-  decode_ws_parts(ctx, B, max_seq_len, &u_bytes, &ml_bytes, &order_bytes);
-  const size_t need = u_bytes + ml_bytes + order_bytes;
+  size_t u_bytes, ml_bytes, order_bytes, x_bytes, mx_bytes;
+  decode_ws_parts(ctx, B, max_seq_len, &u_bytes, &ml_bytes, &order_bytes, &x_bytes, &mx_bytes);
+  int kernel = decode_kernel_for(ctx, B, max_seq_len);
+  const size_t need_split = u_bytes + ml_bytes + order_bytes;
+  // Under IA_DECODE_AUTO a workspace too small for the spread kernels' score
+  // slots runs the split kernel instead (the same bits).
+  if (kernel == 2 && ctx->cfg.decode_kernel == IA_DECODE_AUTO && workspace && ws_bytes >= need_split &&
+      ws_bytes < need_split + x_bytes + mx_bytes)
+    kernel = 0;
+  const size_t need = need_split + (kernel == 2 ? x_bytes + mx_bytes : 0);
   if (!workspace || ws_bytes < need)
     return fail(IA_ERR_WORKSPACE_TOO_SMALL, "decode workspace needs %zu bytes (got %zu)", need, ws_bytes);
   if (!aligned(workspace, 16)) return fail(IA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -216,6 +261,13 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.ws_u = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes);
   a.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + u_bytes + ml_bytes);
+  a.ws_x = reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes + ml_bytes + order_bytes);
+  a.ws_mx = reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes + ml_bytes + order_bytes + x_bytes);
+  {
+    const int64_t slots = (int64_t)B * ctx->cfg.num_kv_heads * decode_max_splits(ctx, B, max_seq_len) *
+                          decode_split_tiles(ctx, B, max_seq_len);
+    a.ws_as = a.ws_mx + align_up((size_t)slots * 16 * sizeof(float)) / sizeof(float);
+  }
   a.c = ctx->c;
   a.B = B;
   a.Hq = ctx->cfg.num_q_heads;
@@ -228,7 +280,8 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.split_tokens = ctx->cfg.split_tokens;
   a.policy = ctx->cfg.split_policy;
   a.window = ctx->cfg.sliding_window;
-  a.wide = ctx->cfg.decode_kernel == IA_DECODE_WIDE;
+  a.kernel = kernel;
+  a.tps = (int)decode_split_tiles(ctx, B, max_seq_len);
   return hip_status(ia::launch_decode(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
                                       static_cast<hipStream_t>(stream)),
                     "decode launch");

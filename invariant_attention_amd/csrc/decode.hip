@@ -491,6 +491,333 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// The spread decode kernels: bitwise equal to decode_split_kernel, for
+// launches with few split units.
+//
+// A split unit of the split kernel is one chain of tile steps on one compute
+// unit, and a compute unit streams only a few tens of GB/s, so a launch of a
+// few dozen units (one sequence, or a handful) leaves most of the chip idle
+// and most of HBM unused.  Here a split's work is spread over many compute
+// units in three launches (Vosti, Discussion: a decode kernel that gives one
+// sequence several compute units for partially filled waves, with the same
+// accumulation order as the kernel for full waves):
+//   decode_score_kernel, one wave per (unit, tile): loads the tile's K and
+//     forms its scores (block_scores) and tile_max (masked scaled scores and
+//     their row maximum) for the stored rows;
+//   decode_weight_kernel, one wave per (unit, tile): folds the running
+//     maximum before its tile from the earlier tiles' row maxima (an exact
+//     fmaxf fold in tile order, the split kernel's max updates), then runs
+//     tile_weights: alpha, the weights as hi/lo bf16 B operands, and their
+//     row sum;
+//   decode_value_kernel, one wave per (unit, 16-dim block): walks the split's
+//     tiles in order running the only true chain, the z update and pv_block
+//     on its own dims' V.
+// Every value is formed by the functions the split kernel's tile step uses,
+// from the same operands, in the same order, and an fp32 or bf16 value
+// stored and read back keeps its bits; so each split partial, and the merged
+// output, is the split kernel's.  Slots are indexed
+// ((b * max_splits + s) * Hkv + kvh) * tps + tile, tps being the longest
+// split of the launch in tiles; a slot past its split's tiles is never
+// written or read.  A slot holds, per stored row, 64 fp32 scores, which the
+// weight kernel then overwrites with the row's hi/lo weights (the same 256
+// bytes); plus the row maximum, and alpha with the row sum.
+
+// (b, s, kvh) of a unit in the spread kernels' order.
+struct SpreadUnit {
+  int b, s, kvh;
+};
+__device__ __forceinline__ SpreadUnit spread_unit(const DecodeArgs& a, int us) {
+  SpreadUnit u;
+  u.kvh = us % a.Hkv;
+  const int bs = us / a.Hkv;
+  u.s = bs % a.max_splits;
+  u.b = bs / a.max_splits;
+  return u;
+}
+
+// Offset (in floats) of lane (r, g)'s 16 bytes of part `part` (a key block's
+// four scores, later one of the four weight operands) in a slot:
+// [4 parts][4 lane groups][group rows][16 bytes].
+__device__ __forceinline__ size_t spread_x_off(size_t slot, int group, int part, int g, int r) {
+  return ((slot * 16 + (size_t)(4 * part + g)) * group + r) * 4;
+}
+
+// The split geometry of one unit, as every decode kernel computes it.
+struct SpreadSplit {
+  int n, p, lo, k_begin, ntiles;
+  bool live;  // the split holds a key the row sees
+};
+__device__ __forceinline__ SpreadSplit spread_split(const DecodeArgs& a, const SpreadUnit& un) {
+  SpreadSplit sp;
+  sp.n = clamp_len(a.seq_lens[un.b], a.max_seq_len);
+  const int S = split_len(a.policy, a.split_tokens, sp.n, a.B);
+  const int nsplit = (sp.n + S - 1) / S;
+  sp.p = sp.n - 1;
+  sp.lo = first_key(sp.p, a.window);
+  sp.live = !(un.s >= nsplit || (un.s + 1) * S <= sp.lo);
+  sp.k_begin = max(un.s * S, sp.lo & ~(kTileKeys - 1));
+  const int k_end = min(un.s * S + S, sp.n);
+  sp.ntiles = sp.live ? (k_end - sp.k_begin + kTileKeys - 1) / kTileKeys : 0;
+  return sp;
+}
+
+// The split kernel's rules for a tile at t0: unmasked step when all its keys
+// exist and lie in the window; a tile holds a key the row sees.
+__device__ __forceinline__ bool tile_full(int t0, int lo, int n) { return t0 >= lo && t0 + kTileKeys <= n; }
+__device__ __forceinline__ bool tile_visible(int t0, int lo, int n, int limit) {
+  return tile_full(t0, lo, n) || (t0 <= limit && t0 + kTileKeys - 1 >= lo);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
+  constexpr int EB = Raw<FP8>::kElemBytes;
+  constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t slot = blockIdx.x;
+  const int lt = (int)(slot % a.tps);
+  const SpreadUnit un = spread_unit(a, (int)(slot / a.tps));
+  const SpreadSplit sp = spread_split(a, un);
+  if (lt >= sp.ntiles) return;  // uniform over the wave (no tile, or no live split)
+  const bool row_ok = r < a.group;
+  const int limit = row_ok ? sp.p : -1;
+  const int hq = un.kvh * a.group + (row_ok ? r : 0);
+  const QFrag<D> q = load_q<D>(a.q + ((size_t)un.b * a.Hq + hq) * D, row_ok, g);
+  float c = a.c;
+  if constexpr (FP8) c = c * a.k_scale[un.kvh];
+  const int t0 = sp.k_begin + kTileKeys * lt;
+  const int32_t* bt_row = a.block_table + (size_t)un.b * a.bt_stride;
+  const int btv = load_tile_bt(bt_row, t0, (sp.n + 15) >> 4, lane);
+  const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
+                           __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
+  const TilePages tp = tile_pages_of(e, t0, sp.n, a.num_pages);
+  // The K of all 4 key blocks, then their scores (the split kernel's k-slot
+  // mapping: lane (r, g) holds chunk 4 ks + g of token r).
+  typename Raw<FP8>::K kr[4][D / 32];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const uint8_t* base = a.k_cache + ((size_t)tp.page[blk] * a.Hkv + un.kvh) * kHeadBytes;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kr[blk][ks] = load_k_raw<FP8>(base, (size_t)((4 * ks + g) * 16 + r) * 8);
+  }
+  f32x4 sc[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    bf16x8 kf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(kr[blk][ks], true);
+    sc[blk] = block_scores<D>(kf, q);
+  }
+  TileMax tm;
+  if (tile_full(t0, sp.lo, sp.n))
+    tm = tile_max<false>(sc, c, t0, sp.lo, limit, g);
+  else
+    tm = tile_max<true>(sc, c, t0, sp.lo, limit, g);
+  if (row_ok) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+      *reinterpret_cast<f32x4*>(a.ws_x + spread_x_off(slot, a.group, blk, g, r)) =
+          f32x4{tm.x[blk][0], tm.x[blk][1], tm.x[blk][2], tm.x[blk][3]};
+    if (g == 0) a.ws_mx[slot * 16 + r] = tm.mx;
+  }
+}
+
+// The weights of one tile from its stored scores and the running maximum m
+// before it; MASK as in the split kernel's step.
+template <bool MASK>
+__device__ __forceinline__ void spread_weights(const DecodeArgs& a, size_t slot, float m, int t0, int lo, int limit,
+                                               int rr, bool row_ok, int g, int r) {
+  TileMax tm;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_x + spread_x_off(slot, a.group, blk, g, rr));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tm.x[blk][j] = x[j];
+  }
+  tm.mx = a.ws_mx[slot * 16 + rr];
+  tm.any_visible = !MASK || (t0 <= limit && t0 + kTileKeys - 1 >= lo);
+  float sum;
+  const TileStep ts = tile_weights<MASK>(m, tm, t0, lo, limit, g, sum);
+  if (row_ok) {
+    // The scores were read above into registers the weights depend on; the
+    // slot's 256 bytes per row now take the four weight operands.
+    *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 0, g, r)) = __builtin_bit_cast(uint4, ts.phi[0]);
+    *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 1, g, r)) = __builtin_bit_cast(uint4, ts.plo[0]);
+    *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 2, g, r)) = __builtin_bit_cast(uint4, ts.phi[1]);
+    *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 3, g, r)) = __builtin_bit_cast(uint4, ts.plo[1]);
+    if (g == 0) *reinterpret_cast<f32x2*>(a.ws_as + (slot * 16 + r) * 2) = f32x2{ts.alpha, sum};
+  }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) void decode_weight_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t slot = blockIdx.x;
+  const int lt = (int)(slot % a.tps);
+  const SpreadUnit un = spread_unit(a, (int)(slot / a.tps));
+  const SpreadSplit sp = spread_split(a, un);
+  if (lt >= sp.ntiles) return;  // uniform over the wave
+  const bool row_ok = r < a.group;
+  const int rr = row_ok ? r : 0;  // padding lanes read row 0's slots (never stored)
+  const int limit = row_ok ? sp.p : -1;
+  // The running maximum before this tile: the split kernel's max updates
+  // over the split's earlier tiles, in order.
+  const size_t slot0 = slot - lt;
+  float mx[kWideChunk];
+  float m = neg_inf();
+  for (int i0 = 0; i0 < lt; i0 += kWideChunk) {
+#pragma unroll
+    for (int i = 0; i < kWideChunk; ++i) mx[i] = a.ws_mx[(slot0 + min(i0 + i, lt - 1)) * 16 + rr];
+#pragma unroll
+    for (int i = 0; i < kWideChunk; ++i) {
+      const int t0 = sp.k_begin + kTileKeys * (i0 + i);
+      m = (i0 + i < lt) ? max_update(m, mx[i], tile_visible(t0, sp.lo, sp.n, limit)) : m;
+    }
+  }
+  const int t0 = sp.k_begin + kTileKeys * lt;
+  if (tile_full(t0, sp.lo, sp.n))
+    spread_weights<false>(a, slot, m, t0, sp.lo, limit, rr, row_ok, g, r);
+  else
+    spread_weights<true>(a, slot, m, t0, sp.lo, limit, rr, row_ok, g, r);
+}
+
+constexpr int kSpreadGroup = 4;  // tiles per load group; two groups alternate (up to 8 tiles in flight)
+
+template <bool FP8>
+struct SpreadFrag {  // one tile's operands for one wave of decode_value_kernel
+  uint4 w[4];                    // phi[0], plo[0], phi[1], plo[1]
+  f32x2 as;                      // alpha, row sum
+  float mx;                      // row maximum
+  typename Raw<FP8>::V v[2][2];  // V^T quads of the wave's dim block
+  int valid;                     // key counts of the tile's 4 page blocks, 5 bits each
+};
+
+// The chain half of the split kernel's tile step, for one dim block: the z
+// and running-maximum commits, and pv_block.  FULL: the unmasked step.
+template <bool FULL, bool FP8>
+__device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, bool vis, float& m, float& z, f32x4& u,
+                                             int g) {
+  TileStep ts;
+  ts.alpha = f.as[0];
+  ts.any_visible = vis;
+  ts.phi[0] = __builtin_bit_cast(bf16x8, f.w[0]);
+  ts.plo[0] = __builtin_bit_cast(bf16x8, f.w[1]);
+  ts.phi[1] = __builtin_bit_cast(bf16x8, f.w[2]);
+  ts.plo[1] = __builtin_bit_cast(bf16x8, f.w[3]);
+  ts.m_new = fmaxf(m, f.mx);
+  ts.z_new = z_update(z, f.as[0], f.as[1]);
+  bf16x8 vf[2];
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int nv = FULL ? 4 : ((f.valid >> (5 * (2 * ks2 + hb))) & 31) - 4 * g;
+      const bf16x4 v4 = v_to_bf16(f.v[ks2][hb], nv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
+    }
+  u = pv_block(u, vf, ts);
+  commit_scalars(m, z, ts);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) void decode_value_kernel(DecodeArgs a) {
+  constexpr int EB = Raw<FP8>::kElemBytes;
+  constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
+  constexpr int kDimBlocks = D / 16;
+  constexpr int G = kSpreadGroup;
+  __shared__ __attribute__((aligned(16))) int bt_lds[4 * kBtWindowTiles];
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int mb = blockIdx.x % kDimBlocks;
+  const int us = blockIdx.x / kDimBlocks;
+  const SpreadUnit un = spread_unit(a, us);
+  const SpreadSplit sp = spread_split(a, un);
+  if (!sp.live) return;  // uniform over the wave
+  const int n = sp.n, lo = sp.lo, k_begin = sp.k_begin, ntiles = sp.ntiles;
+  const bool row_ok = r < a.group;
+  const int rr = row_ok ? r : 0;  // padding lanes read row 0's slots (never stored)
+  const int limit = row_ok ? sp.p : -1;
+  const int hq = un.kvh * a.group + rr;
+  const size_t slot0 = (size_t)us * a.tps;
+  const int32_t* bt_row = a.block_table + (size_t)un.b * a.bt_stride;
+  const int nblk = (n + 15) >> 4;
+  const uint8_t* vc = a.v_cache;
+  const int np = a.num_pages;
+
+  float m = neg_inf(), z = 0.f;
+  f32x4 u = {0.f, 0.f, 0.f, 0.f};  // dims 16 mb + 4 g + j of the row
+
+  for (int w0 = 0; w0 < ntiles; w0 += kBtWindowTiles) {
+    const int wn = min(ntiles - w0, kBtWindowTiles);
+    __syncthreads();
+    const int e0 = (k_begin >> 4) + 4 * w0;
+    for (int i = lane; i < 4 * wn; i += 64) {
+      const int e = e0 + i < nblk ? e0 + i : nblk - 1;
+      bt_lds[i] = bt_row[e];
+    }
+    __syncthreads();
+    const int last = wn - 1;
+    // Issues the loads of tiles lt0 .. lt0 + G - 1 of the window; an index
+    // past the window clamps to its last tile (in bounds, never used).
+    auto load = [&](SpreadFrag<FP8> (&f)[G], int lt0) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int lt = lt0 + i < last ? lt0 + i : last;
+        const int4 e = *reinterpret_cast<const int4*>(&bt_lds[4 * lt]);
+        const int4 eu = make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                                  __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+        const TilePages tp = tile_pages_of(eu, k_begin + kTileKeys * (w0 + lt), n, np);
+        f[i].valid = tp.valid[0] | (tp.valid[1] << 5) | (tp.valid[2] << 10) | (tp.valid[3] << 15);
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const uint8_t* base = vc + ((size_t)tp.page[2 * ks2 + hb] * a.Hkv + un.kvh) * kHeadBytes;
+            f[i].v[ks2][hb] = load_v_raw<FP8>(base, (size_t)(16 * mb + r) * 16 + 4 * g);
+          }
+        const size_t slot = slot0 + w0 + lt;
+#pragma unroll
+        for (int part = 0; part < 4; ++part)
+          f[i].w[part] = *reinterpret_cast<const uint4*>(a.ws_x + spread_x_off(slot, a.group, part, g, rr));
+        f[i].as = *reinterpret_cast<const f32x2*>(a.ws_as + (slot * 16 + rr) * 2);
+        f[i].mx = a.ws_mx[slot * 16 + rr];
+      }
+    };
+    auto step = [&](const SpreadFrag<FP8>& f, int lt) {
+      const int t0 = k_begin + kTileKeys * (w0 + lt);
+      const bool vis = tile_visible(t0, lo, n, limit);
+      if (tile_full(t0, lo, n))
+        spread_chain<true, FP8>(f, vis, m, z, u, g);
+      else
+        spread_chain<false, FP8>(f, vis, m, z, u, g);
+    };
+    SpreadFrag<FP8> fa[G], fb[G];
+    load(fa, 0);
+    for (int lt = 0; lt < wn; lt += 2 * G) {
+      load(fb, lt + G);
+      __builtin_amdgcn_sched_barrier(0);  // issue the next group's loads before waiting on this one's
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        if (lt + i < wn) step(fa[i], lt + i);
+      if (lt + G >= wn) break;
+      load(fa, lt + 2 * G);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        if (lt + G + i < wn) step(fb[i], lt + G + i);
+    }
+  }
+
+  if (row_ok) {
+    const size_t row = ((size_t)un.b * a.max_splits + un.s) * a.Hq + hq;
+    *reinterpret_cast<f32x4*>(a.ws_u + row * D + 16 * mb + 4 * g) = u;
+    if (mb == 0 && g == 0) *reinterpret_cast<f32x2*>(a.ws_ml + row * 2) = f32x2{m, z};
+  }
+}
+
 // One wave per (sequence, query head): folds the split partials in ascending
 // split order and writes the bf16 output row.
 template <int D, bool FP8>
@@ -598,7 +925,15 @@ template <int D, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.Hkv * a.max_splits;
-  if (a.wide && wide_fits(a)) {
+  if (a.kernel == 2) {
+    hipLaunchKernelGGL((decode_score_kernel<D, FP8>), dim3((unsigned)(units * a.tps)), dim3(64), 0, st, a);
+    hipError_t se = hipGetLastError();
+    if (se != hipSuccess) return se;
+    hipLaunchKernelGGL((decode_weight_kernel<D, FP8>), dim3((unsigned)(units * a.tps)), dim3(64), 0, st, a);
+    se = hipGetLastError();
+    if (se != hipSuccess) return se;
+    hipLaunchKernelGGL((decode_value_kernel<D, FP8>), dim3((unsigned)(units * (D / 16))), dim3(64), 0, st, a);
+  } else if (a.kernel == 1 && wide_fits(a)) {
     hipLaunchKernelGGL((decode_wide_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kWideWaves), 0, st, a);
   } else {
     DecodeArgs sa = a;

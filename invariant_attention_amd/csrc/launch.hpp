@@ -31,13 +31,18 @@ struct DecodeArgs {
   float* ws_u;                 // [B][max_splits][Hq][D]
   float* ws_ml;                // [B][max_splits][Hq][2]
   int32_t* order;              // [B * max_splits] dispatch order of the split units (workspace)
+  float* ws_x;                 // spread: per slot [4 parts][4 lane groups][group][16 B]: scores, then weights
+  float* ws_mx;                // spread: row maxima, [slot][16]
+  float* ws_as;                // spread: alpha and row sum, [slot][16][2]
   float c;                     // fp32(sm_scale * log2 e)
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;
   int max_seq_len, max_splits;
   int split_tokens, policy;
   int window;                  // 0: full causal attention; w > 0: keys p - w < j <= p
-  int wide;                    // 1: decode_wide_kernel, 0: decode_split_kernel (same bits)
+  int kernel;                  // 0: decode_split_kernel, 1: decode_wide_kernel, 2: the spread kernels
+                               // (score, weight, value); all give the same bits
+  int tps;                     // spread: tile slots per split (the longest split of the launch, in tiles)
 };
 
 struct PrefillArgs {

@@ -47,7 +47,7 @@ def test_version_and_clean_error_state():
     (dict(Hq=32, Hkv=8, d=128, split_policy=3), "split_policy"),
     (dict(Hq=32, Hkv=8, d=128, sm_scale=-1.0), "sm_scale"),
     (dict(Hq=32, Hkv=8, d=128, sliding_window=-1), "sliding_window"),
-    (dict(Hq=32, Hkv=8, d=128, decode_kernel=3), "decode_kernel"),
+    (dict(Hq=32, Hkv=8, d=128, decode_kernel=4), "decode_kernel"),
 ])
 def test_unsupported_configs_are_rejected(kw, msg):
     Hq, Hkv, d = kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d")
@@ -66,8 +66,17 @@ def test_workspace_size_formula():
     assert got == up(rows * 128 * 4) + up(rows * 2 * 4) + up(256 * 4 * 4)
     assert ia.ia_decode_workspace_bytes(ctx, 0, 8192) == 0
     bc = ia.Context(ia.make_config(32, 8, 128, split_policy=ia.IA_SPLIT_BY_COUNT))
+    # a launch of at most 64 split units runs the spread kernels, which add one slot per
+    # (sequence, split, kv head, tile): group x 64 fp32 scores, 16 fp32 row maxima, 16 (alpha, sum)
+    slots = 1 * 4 * 8 * 32
+    assert ia.ia_decode_workspace_bytes(ctx, 1, 8192) == (up(4 * 32 * 128 * 4) + up(4 * 32 * 2 * 4) + up(4 * 4)
+                                                         + up(slots * 4 * 64 * 4) + up(slots * 16 * 4)
+                                                         + up(slots * 16 * 2 * 4))
+    split_only = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048, decode_kernel=ia.IA_DECODE_SPLIT))
+    assert ia.ia_decode_workspace_bytes(split_only, 1, 8192) == up(4 * 32 * 128 * 4) + up(4 * 32 * 2 * 4) + up(16)
     # split-by-count: at most min(64, 256 // B) pieces, and no more than one per 64-key tile
-    assert ia.ia_decode_workspace_bytes(bc, 1, 64) == up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4) + up(4)
+    assert ia.ia_decode_workspace_bytes(bc, 1, 64) == (up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4) + up(4)
+                                                       + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 2 * 4))
     assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
                                                           + up(4 * 64 * 4))
 
@@ -122,7 +131,7 @@ def test_append_and_prefill_argument_errors():
 def test_binding_constants_match_header():
     import re
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "invattn.h")).read()
-    for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT"):
+    for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_DECODE_SPREAD", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT"):
         m = re.search(name + r" = (\d+)", hdr)
         assert m and int(m.group(1)) == getattr(ia, name), name
 

@@ -1,9 +1,10 @@
-"""The two decode kernels are bitwise equivalent (dispatch among bitwise-equivalent kernels: Vosti,
+"""The decode kernels are bitwise equivalent (dispatch among bitwise-equivalent kernels: Vosti,
 Discussion, "Cross-kernel relational verification").  The wide kernel forms the scores and weights
-of 8 tiles of a split at once and keeps only the z and value updates as a chain; every row must get
-the same bits from it as from the split kernel, on every head geometry, dtype, window, split policy
-and edge length, and the automatic choice must not change a bit either.  It is also checked against
-the fp64 oracle directly."""
+of 8 tiles of a split at once and keeps only the z and value updates as a chain; the spread kernels
+scores every tile of a split in its own wave and runs the chain of each 16-dim block in its own
+wave.  Every row must get the same bits from each as from the split kernel, on every head geometry,
+dtype, window, split policy and edge length, and the automatic choice must not change a bit either.
+Both are also checked against the fp64 oracle directly."""
 import numpy as np
 import pytest
 import torch
@@ -56,34 +57,41 @@ CASES = [
 ]
 
 
+KERNELS = [ia.IA_DECODE_WIDE, ia.IA_DECODE_SPREAD]
+KIDS = ["wide", "spread"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS, ids=KIDS)
 @pytest.mark.parametrize("name,shape,lens", CASES, ids=[c[0] for c in CASES])
-def test_wide_equals_split_bitwise(name, shape, lens):
+def test_kernel_equals_split_bitwise(name, shape, lens, kernel):
     seqs, layout, pages, q = _world(shape, lens)
     split = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_SPLIT)
-    wide = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_WIDE)
-    assert _eq(wide, split)
+    other = _decode(shape, pages, q, layout, lens, kernel)
+    assert _eq(other, split)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KIDS)
 @pytest.mark.parametrize("pow2", [True, False], ids=["pow2-scales", "free-scales"])
-def test_wide_equals_split_fp8(pow2):
+def test_kernel_equals_split_fp8(pow2, kernel):
     shape = wl.LLAMA31_70B
     lens = [3000, 700, 64, 1]
     scales = wl.fp8_scales(4, shape.Hkv, power_of_two=pow2)
     seqs, layout, pages, q = _world(shape, lens, fp8=True, scales=scales)
     split = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_SPLIT)
-    wide = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_WIDE)
-    assert _eq(wide, split)
+    other = _decode(shape, pages, q, layout, lens, kernel)
+    assert _eq(other, split)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KIDS)
 @pytest.mark.parametrize("shape,lens,window", [(wl.TINY, EDGE, 17), (wl.TINY, list(wl.TINY_LENS), 100),
                                                (wl.LLAMA3_8B, [6000, 2048, 2049, 100, 4097], 2000),
                                                (wl.LLAMA3_8B, [9000, 4096], 4096)],
                          ids=["tiny-w17", "tiny-w100", "llama8b-w2000", "llama8b-w4096"])
-def test_wide_equals_split_with_window(shape, lens, window):
+def test_kernel_equals_split_with_window(shape, lens, window, kernel):
     seqs, layout, pages, q = _world(shape, lens)
     split = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_SPLIT, window=window)
-    wide = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_WIDE, window=window)
-    assert _eq(wide, split)
+    other = _decode(shape, pages, q, layout, lens, kernel, window=window)
+    assert _eq(other, split)
 
 
 def test_wide_falls_back_for_long_splits():
@@ -96,20 +104,22 @@ def test_wide_falls_back_for_long_splits():
     assert _eq(wide, split)
 
 
-def test_wide_equals_split_under_split_by_count():
+@pytest.mark.parametrize("kernel", KERNELS, ids=KIDS)
+def test_kernel_equals_split_under_split_by_count(kernel):
     shape = wl.LLAMA3_8B
     lens = [8192, 3000, 65]
     seqs, layout, pages, q = _world(shape, lens)
     split = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_SPLIT, by_count=True)
-    wide = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_WIDE, by_count=True)
-    assert _eq(wide, split)
+    other = _decode(shape, pages, q, layout, lens, kernel, by_count=True)
+    assert _eq(other, split)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KIDS)
 @pytest.mark.parametrize("name,shape,lens", [CASES[0], CASES[3], CASES[6]], ids=["tiny", "llama8b-edges", "d64-g3"])
-def test_wide_matches_oracle(name, shape, lens):
+def test_kernel_matches_oracle(name, shape, lens, kernel):
     seqs, layout, pages, q = _world(shape, lens)
     ref, *_ = osd.run_oracle(shape, seqs, layout, SEED, [1] * len(lens))
-    out = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_WIDE)
+    out = _decode(shape, pages, q, layout, lens, kernel)
     ok, err, ratio = gs.within_tolerance(out, ref)
     assert ok, f"max abs err {err}, worst err/bound {ratio}"
 
@@ -127,3 +137,36 @@ def test_kernel_choice_changes_no_bit_across_batch_sizes():
         sub = wl.PageLayout(layout.num_pages, layout.block_table[idx], [layout.pages[i] for i in idx])
         small = _decode(shape, pages, q[idx], sub, [lens[i] for i in idx], ia.IA_DECODE_WIDE)
         assert _eq(small, full_split[idx])
+
+
+def test_spread_with_grid_bounds_above_the_lengths():
+    # max_seq_len sizes the grid only.  At 4000 the spread kernels runs with most of its units and
+    # tile slots empty; at 128 * 2731 its score buffer would need 2 x 3 x 2731 x 2 = 32772 slots,
+    # above its 32768, and the split kernel runs instead.  Every call gives the same bits.
+    shape = wl.AttnShape(Hq=8, Hkv=2, d=64, P=16, S=128)
+    lens = [300, 1000, 77]
+    seqs, layout, pages, q = _world(shape, lens)
+    split = _decode(shape, pages, q, layout, lens, ia.IA_DECODE_SPLIT)
+    ctx = gs.make_ctx(shape, decode_kernel=ia.IA_DECODE_SPREAD)
+    for msl in (4000, 128 * 2731):
+        wide_layout = wl.widened(layout, -(-msl // shape.P))
+        bt = torch.as_tensor(wide_layout.block_table, device="cuda")
+        out = gs.decode(ctx, pages, q, wide_layout, lens, max_seq_len=msl, block_table=bt)
+        assert _eq(out, split), msl
+
+
+def test_auto_with_a_workspace_sized_for_the_split_kernel_only():
+    # Under AUTO a small launch runs the spread kernels; given only the split kernel's workspace it runs
+    # the split kernel instead.  Both calls give the same bits.
+    shape = wl.LLAMA3_8B
+    lens = [5000, 77]
+    seqs, layout, pages, q = _world(shape, lens)
+    ctx = gs.make_ctx(shape)
+    full = gs.decode(ctx, pages, q, layout, lens)
+    split_ctx = gs.make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT)
+    need_split = ia.ia_decode_workspace_bytes(split_ctx, len(lens), max(lens))
+    need_auto = ia.ia_decode_workspace_bytes(ctx, len(lens), max(lens))
+    assert need_auto > need_split
+    ws = torch.empty(need_split, dtype=torch.uint8, device="cuda")
+    small = gs.decode(ctx, pages, q, layout, lens, ws=ws)
+    assert _eq(small, full)
