@@ -148,9 +148,10 @@ const char* ia_version(void);
  * int32 per (sequence, split) for the order in which the split units are
  * dispatched (longest first; the order never changes a result bit), and,
  * when the launch runs the spread kernels, one slot per (sequence, split,
- * kv head, tile): group x 64 fp32 scores (later the weights), and 16 row
- * maxima and 16 (alpha, row sum) pairs.  Under IA_DECODE_AUTO a workspace large enough for the split kernel
- * but not for the score slots runs the split kernel (the same bits). */
+ * kv head, tile): group x 64 fp32 scores (later the weights), 16 row
+ * maxima, and 16 rows of (alpha, row sum, row maximum, 0).  Under
+ * IA_DECODE_AUTO a workspace large enough for the split kernel but not for
+ * the score slots runs the split kernel (the same bits). */
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
 /* Device workspace for ia_paged_attn_prefill (0: prefill folds its split

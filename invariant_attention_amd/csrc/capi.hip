@@ -64,7 +64,7 @@ int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len)
 // chip idle; it gives the split kernel's bits, so the choice below decides
 // speed only.  Its score buffer holds one slot per (unit, tile).
 constexpr int64_t kSpreadMaxUnits = 64;        // IA_DECODE_AUTO: at most this many split units
-constexpr int64_t kSpreadMaxSlots = 1 << 15;   // score slots: <= 128 MiB of scores at 16 rows
+constexpr int64_t kSpreadMaxSlots = 1 << 15;   // slots: <= 128 MiB of scores at 16 rows
 
 // Tiles of the longest split a launch can have: the fixed split, or the
 // split-by-count length for the longest sequence.
@@ -102,8 +102,8 @@ void decode_ws_parts(const ia_ctx* ctx, int64_t B, int64_t max_seq_len, size_t* 
   if (decode_kernel_for(ctx, B, max_seq_len) == 2) {
     const int64_t slots = B * ms * ctx->cfg.num_kv_heads * decode_split_tiles(ctx, B, max_seq_len);
     *x_bytes = align_up((size_t)slots * 16 * ctx->group * 4 * sizeof(float));
-    // row maxima [slot][16], then (alpha, row sum) [slot][16][2]
-    *mx_bytes = align_up((size_t)slots * 16 * sizeof(float)) + align_up((size_t)slots * 16 * 2 * sizeof(float));
+    // row maxima [slot][16], then (alpha, row sum, row maximum, 0) [slot][16][4]
+    *mx_bytes = align_up((size_t)slots * 16 * sizeof(float)) + align_up((size_t)slots * 16 * 4 * sizeof(float));
   }
 }
 

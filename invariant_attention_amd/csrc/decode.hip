@@ -609,8 +609,9 @@ __global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
     for (int ks = 0; ks < D / 32; ++ks) kf[ks] = k_to_bf16(kr[blk][ks], true);
     sc[blk] = block_scores<D>(kf, q);
   }
+  const bool full = tile_full(t0, sp.lo, sp.n);
   TileMax tm;
-  if (tile_full(t0, sp.lo, sp.n))
+  if (full)
     tm = tile_max<false>(sc, c, t0, sp.lo, limit, g);
   else
     tm = tile_max<true>(sc, c, t0, sp.lo, limit, g);
@@ -646,7 +647,7 @@ __device__ __forceinline__ void spread_weights(const DecodeArgs& a, size_t slot,
     *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 1, g, r)) = __builtin_bit_cast(uint4, ts.plo[0]);
     *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 2, g, r)) = __builtin_bit_cast(uint4, ts.phi[1]);
     *reinterpret_cast<uint4*>(a.ws_x + spread_x_off(slot, a.group, 3, g, r)) = __builtin_bit_cast(uint4, ts.plo[1]);
-    if (g == 0) *reinterpret_cast<f32x2*>(a.ws_as + (slot * 16 + r) * 2) = f32x2{ts.alpha, sum};
+    if (g == 0) *reinterpret_cast<f32x4*>(a.ws_as + (slot * 16 + r) * 4) = f32x4{ts.alpha, sum, tm.mx, 0.f};
   }
 }
 
@@ -665,13 +666,14 @@ __global__ __launch_bounds__(64) void decode_weight_kernel(DecodeArgs a) {
   // The running maximum before this tile: the split kernel's max updates
   // over the split's earlier tiles, in order.
   const size_t slot0 = slot - lt;
-  float mx[kWideChunk];
+  constexpr int kMaxChunk = 32;  // earlier tiles' maxima loaded at once
+  float mx[kMaxChunk];
   float m = neg_inf();
-  for (int i0 = 0; i0 < lt; i0 += kWideChunk) {
+  for (int i0 = 0; i0 < lt; i0 += kMaxChunk) {
 #pragma unroll
-    for (int i = 0; i < kWideChunk; ++i) mx[i] = a.ws_mx[(slot0 + min(i0 + i, lt - 1)) * 16 + rr];
+    for (int i = 0; i < kMaxChunk; ++i) mx[i] = a.ws_mx[(slot0 + min(i0 + i, lt - 1)) * 16 + rr];
 #pragma unroll
-    for (int i = 0; i < kWideChunk; ++i) {
+    for (int i = 0; i < kMaxChunk; ++i) {
       const int t0 = sp.k_begin + kTileKeys * (i0 + i);
       m = (i0 + i < lt) ? max_update(m, mx[i], tile_visible(t0, sp.lo, sp.n, limit)) : m;
     }
@@ -683,37 +685,34 @@ __global__ __launch_bounds__(64) void decode_weight_kernel(DecodeArgs a) {
     spread_weights<true>(a, slot, m, t0, sp.lo, limit, rr, row_ok, g, r);
 }
 
-constexpr int kSpreadGroup = 4;  // tiles per load group; two groups alternate (up to 8 tiles in flight)
-
 template <bool FP8>
 struct SpreadFrag {  // one tile's operands for one wave of decode_value_kernel
   uint4 w[4];                    // phi[0], plo[0], phi[1], plo[1]
-  f32x2 as;                      // alpha, row sum
-  float mx;                      // row maximum
+  f32x4 asm4;                    // alpha, row sum, row maximum, 0
   typename Raw<FP8>::V v[2][2];  // V^T quads of the wave's dim block
-  int valid;                     // key counts of the tile's 4 page blocks, 5 bits each
 };
 
 // The chain half of the split kernel's tile step, for one dim block: the z
-// and running-maximum commits, and pv_block.  FULL: the unmasked step.
+// and running-maximum commits, and pv_block.  FULL: the unmasked step (every
+// key of the tile exists); otherwise the V of keys past n is zero filled.
 template <bool FULL, bool FP8>
-__device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, bool vis, float& m, float& z, f32x4& u,
-                                             int g) {
+__device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, int valid, bool vis, float& m, float& z,
+                                             f32x4& u, int g) {
   TileStep ts;
-  ts.alpha = f.as[0];
+  ts.alpha = f.asm4[0];
   ts.any_visible = vis;
   ts.phi[0] = __builtin_bit_cast(bf16x8, f.w[0]);
   ts.plo[0] = __builtin_bit_cast(bf16x8, f.w[1]);
   ts.phi[1] = __builtin_bit_cast(bf16x8, f.w[2]);
   ts.plo[1] = __builtin_bit_cast(bf16x8, f.w[3]);
-  ts.m_new = fmaxf(m, f.mx);
-  ts.z_new = z_update(z, f.as[0], f.as[1]);
+  ts.m_new = fmaxf(m, f.asm4[2]);
+  ts.z_new = z_update(z, f.asm4[0], f.asm4[1]);
   bf16x8 vf[2];
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int nv = FULL ? 4 : ((f.valid >> (5 * (2 * ks2 + hb))) & 31) - 4 * g;
+      const int nv = FULL ? 4 : ((valid >> (5 * (2 * ks2 + hb))) & 31) - 4 * g;
       const bf16x4 v4 = v_to_bf16(f.v[ks2][hb], nv);
 #pragma unroll
       for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
@@ -722,96 +721,156 @@ __device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, bool vis,
   commit_scalars(m, z, ts);
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(64) void decode_value_kernel(DecodeArgs a) {
+// The value kernel is a workgroup of 4 waves per (unit, 16-dim block).  It
+// stages a group of up to GT tiles' operands in LDS with direct global -> LDS
+// copies (global_load_lds), each wave copying a quarter of the tiles (a wave
+// keeps at most 63 memory instructions in flight), waits for all of them, then
+// wave 0 runs the chain over the group from LDS.  GT covers a whole
+// 2048-key split at up to 4 query heads per kv head.  Copies per tile: the
+// V^T of the dim block from its 4 pages (4 x 512 B bf16 in two copies,
+// 4 x 256 B e4m3 in one), the slot's weights (group x 256 B in WC copies of
+// 1 KiB), and the rows' (alpha, sum, max) (16 x 16 B in one copy of 4 B per
+// lane).
+template <int WC>
+struct SpreadRing {
+  static constexpr int GT = WC == 1 ? 32 : 16;  // tiles per group
+  static constexpr int kWaves = 4;
+  static constexpr int TPW = GT / kWaves;       // tiles each wave copies
+};
+
+template <int D, bool FP8, int WC>
+__global__ __launch_bounds__(256) void decode_value_kernel(DecodeArgs a) {
   constexpr int EB = Raw<FP8>::kElemBytes;
   constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
   constexpr int kDimBlocks = D / 16;
-  constexpr int G = kSpreadGroup;
-  __shared__ __attribute__((aligned(16))) int bt_lds[4 * kBtWindowTiles];
-  const int lane = threadIdx.x;
+  constexpr int GT = SpreadRing<WC>::GT;
+  constexpr int TPW = SpreadRing<WC>::TPW;
+  constexpr int kVBytes = 4 * 16 * 16 * EB;         // V of one dim block of one tile
+  constexpr int kWBytes = WC * 1024;
+  constexpr int kSlotBytes = kVBytes + kWBytes + 256;
+  static_assert(4 * TPW <= 64, "a wave's block-table entries fit its lanes");
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // GT slots, then GT x 4 block-table entries
+  int* bt_lds = reinterpret_cast<int*>(ring + GT * kSlotBytes);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int mb = blockIdx.x % kDimBlocks;
   const int us = blockIdx.x / kDimBlocks;
   const SpreadUnit un = spread_unit(a, us);
   const SpreadSplit sp = spread_split(a, un);
-  if (!sp.live) return;  // uniform over the wave
+  if (!sp.live) return;  // uniform over the workgroup
   const int n = sp.n, lo = sp.lo, k_begin = sp.k_begin, ntiles = sp.ntiles;
   const bool row_ok = r < a.group;
-  const int rr = row_ok ? r : 0;  // padding lanes read row 0's slots (never stored)
+  const int rr = row_ok ? r : 0;  // padding lanes read row 0's values (never stored)
   const int limit = row_ok ? sp.p : -1;
   const int hq = un.kvh * a.group + rr;
   const size_t slot0 = (size_t)us * a.tps;
   const int32_t* bt_row = a.block_table + (size_t)un.b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
-  const uint8_t* vc = a.v_cache;
   const int np = a.num_pages;
+  const int wbytes = a.group * 256;  // one slot's weights
+  // This lane's source byte within a slot's weights for copy i (lanes past
+  // the slot's rows re-read its last 16 bytes: in bounds, never used).
+  auto w_src = [&](int i) { return min(i * 1024 + lane * 16, wbytes - 16); };
+  auto pages = [&](int j) {  // group tile j's entries, staged in LDS
+    const int4 e = *reinterpret_cast<const int4*>(&bt_lds[4 * j]);
+    return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                     __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+  };
 
   float m = neg_inf(), z = 0.f;
-  f32x4 u = {0.f, 0.f, 0.f, 0.f};  // dims 16 mb + 4 g + j of the row
-
-  for (int w0 = 0; w0 < ntiles; w0 += kBtWindowTiles) {
-    const int wn = min(ntiles - w0, kBtWindowTiles);
-    __syncthreads();
-    const int e0 = (k_begin >> 4) + 4 * w0;
-    for (int i = lane; i < 4 * wn; i += 64) {
-      const int e = e0 + i < nblk ? e0 + i : nblk - 1;
-      bt_lds[i] = bt_row[e];
+  f32x4 u = {0.f, 0.f, 0.f, 0.f};  // dims 16 mb + 4 g + j of the row (wave 0)
+  for (int g0 = 0; g0 < ntiles; g0 += GT) {
+    const int cnt = min(GT, ntiles - g0);
+    const int j0 = w * TPW;                       // this wave's first tile of the group
+    const int jn = min(TPW, cnt - j0);            // and how many (may be <= 0)
+    __syncthreads();                              // the previous group's chain is done with LDS
+    // Weights and (alpha, sum, max): they need no page.
+    for (int jj = 0; jj < jn; ++jj) {
+      const int j = j0 + jj;
+      uint8_t* dst = ring + j * kSlotBytes;
+      const size_t slot = slot0 + g0 + j;
+      const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.ws_x + spread_x_off(slot, a.group, 0, 0, 0));
+#pragma unroll
+      for (int i = 0; i < WC; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc + w_src(i)), (lds_void_t*)(dst + kVBytes + i * 1024),
+                                         16, 0, 0);
+      const uint8_t* asrc = reinterpret_cast<const uint8_t*>(a.ws_as + slot * 16 * 4);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc + lane * 4), (lds_void_t*)(dst + kVBytes + kWBytes), 4, 0,
+                                       0);
     }
-    __syncthreads();
-    const int last = wn - 1;
-    // Issues the loads of tiles lt0 .. lt0 + G - 1 of the window; an index
-    // past the window clamps to its last tile (in bounds, never used).
-    auto load = [&](SpreadFrag<FP8> (&f)[G], int lt0) {
+    // The wave's block-table entries (clamped to the sequence's last block),
+    // one per lane, then the V copies of its tiles.
+    int btv = 0;
+    if (jn > 0) {
+      const int e = (k_begin >> 4) + 4 * (g0 + j0) + (lane < 4 * jn ? lane : 4 * jn - 1);
+      btv = bt_row[e < nblk ? e : nblk - 1];
+    }
+    for (int jj = 0; jj < jn; ++jj) {
+      const int j = j0 + jj;
+      const int4 ent = make_int4(__builtin_amdgcn_readlane(btv, 4 * jj), __builtin_amdgcn_readlane(btv, 4 * jj + 1),
+                                 __builtin_amdgcn_readlane(btv, 4 * jj + 2), __builtin_amdgcn_readlane(btv, 4 * jj + 3));
+      const TilePages tp = tile_pages_of(ent, k_begin + kTileKeys * (g0 + j), n, np);
+      uint8_t* dst = ring + j * kSlotBytes;
+      const size_t vdim = (size_t)16 * mb * 16 * EB;  // the dim block's bytes inside a page block
+      if constexpr (FP8) {
+        // 4 page blocks x 256 B: lanes 16 q .. 16 q + 15 copy block q.
+        const int q = lane >> 4;
+        const int pg = q == 0 ? tp.page[0] : (q == 1 ? tp.page[1] : (q == 2 ? tp.page[2] : tp.page[3]));
+        const uint8_t* src = a.v_cache + ((size_t)pg * a.Hkv + un.kvh) * kHeadBytes + vdim + (lane & 15) * 16;
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+      } else {
+        // 4 page blocks x 512 B: copy h takes blocks 2 h (lanes 0..31) and 2 h + 1.
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const int lt = lt0 + i < last ? lt0 + i : last;
-        const int4 e = *reinterpret_cast<const int4*>(&bt_lds[4 * lt]);
-        const int4 eu = make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
-                                  __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
-        const TilePages tp = tile_pages_of(eu, k_begin + kTileKeys * (w0 + lt), n, np);
-        f[i].valid = tp.valid[0] | (tp.valid[1] << 5) | (tp.valid[2] << 10) | (tp.valid[3] << 15);
+        for (int h = 0; h < 2; ++h) {
+          const int pg = (lane < 32) ? (h == 0 ? tp.page[0] : tp.page[2]) : (h == 0 ? tp.page[1] : tp.page[3]);
+          const uint8_t* src = a.v_cache + ((size_t)pg * a.Hkv + un.kvh) * kHeadBytes + vdim + (lane & 31) * 16;
+          __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(dst + h * 1024), 16, 0, 0);
+        }
+      }
+    }
+    if (jn > 0 && lane < 4 * jn) bt_lds[4 * j0 + lane] = btv;  // for the chain's key counts
+    __syncthreads();  // (waits for every copy of this wave first) the group has landed
+    if (w != 0) continue;
+    // Wave 0: the chain over the group, operands read from LDS (no copy is
+    // in flight now, so these are ordinary LDS reads), four tiles' reads at a
+    // time ahead of their value products.
+    auto read = [&](int j, SpreadFrag<FP8>& f) {
+      const uint8_t* src = ring + j * kSlotBytes;
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
+      for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const uint8_t* base = vc + ((size_t)tp.page[2 * ks2 + hb] * a.Hkv + un.kvh) * kHeadBytes;
-            f[i].v[ks2][hb] = load_v_raw<FP8>(base, (size_t)(16 * mb + r) * 16 + 4 * g);
-          }
-        const size_t slot = slot0 + w0 + lt;
+        for (int hb = 0; hb < 2; ++hb)
+          f.v[ks2][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(src + (2 * ks2 + hb) * (kVBytes / 4) +
+                                                                         (r * 16 + 4 * g) * EB);
 #pragma unroll
-        for (int part = 0; part < 4; ++part)
-          f[i].w[part] = *reinterpret_cast<const uint4*>(a.ws_x + spread_x_off(slot, a.group, part, g, rr));
-        f[i].as = *reinterpret_cast<const f32x2*>(a.ws_as + (slot * 16 + rr) * 2);
-        f[i].mx = a.ws_mx[slot * 16 + rr];
+      for (int part = 0; part < 4; ++part)
+        f.w[part] = *reinterpret_cast<const uint4*>(src + kVBytes + ((4 * part + g) * a.group + rr) * 16);
+      f.asm4 = *reinterpret_cast<const f32x4*>(src + kVBytes + kWBytes + rr * 16);
+    };
+    auto chain = [&](int j, const SpreadFrag<FP8>& f) {
+      const int t0 = k_begin + kTileKeys * (g0 + j);
+      const bool vis = tile_visible(t0, lo, n, limit);
+      if (tile_full(t0, lo, n)) {
+        spread_chain<true, FP8>(f, 0, vis, m, z, u, g);
+      } else {
+        const TilePages tp = tile_pages_of(pages(j), t0, n, np);
+        const int valid = tp.valid[0] | (tp.valid[1] << 5) | (tp.valid[2] << 10) | (tp.valid[3] << 15);
+        spread_chain<false, FP8>(f, valid, vis, m, z, u, g);
       }
     };
-    auto step = [&](const SpreadFrag<FP8>& f, int lt) {
-      const int t0 = k_begin + kTileKeys * (w0 + lt);
-      const bool vis = tile_visible(t0, lo, n, limit);
-      if (tile_full(t0, lo, n))
-        spread_chain<true, FP8>(f, vis, m, z, u, g);
-      else
-        spread_chain<false, FP8>(f, vis, m, z, u, g);
-    };
-    SpreadFrag<FP8> fa[G], fb[G];
-    load(fa, 0);
-    for (int lt = 0; lt < wn; lt += 2 * G) {
-      load(fb, lt + G);
-      __builtin_amdgcn_sched_barrier(0);  // issue the next group's loads before waiting on this one's
+    for (int j = 0; j < cnt; j += 4) {
+      SpreadFrag<FP8> f[4];
 #pragma unroll
-      for (int i = 0; i < G; ++i)
-        if (lt + i < wn) step(fa[i], lt + i);
-      if (lt + G >= wn) break;
-      load(fa, lt + 2 * G);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i)
+        if (j + i < cnt) read(j + i, f[i]);
 #pragma unroll
-      for (int i = 0; i < G; ++i)
-        if (lt + G + i < wn) step(fb[i], lt + G + i);
+      for (int i = 0; i < 4; ++i)
+        if (j + i < cnt) chain(j + i, f[i]);
     }
   }
 
-  if (row_ok) {
+  if (w == 0 && row_ok) {
     const size_t row = ((size_t)un.b * a.max_splits + un.s) * a.Hq + hq;
     *reinterpret_cast<f32x4*>(a.ws_u + row * D + 16 * mb + 4 * g) = u;
     if (mb == 0 && g == 0) *reinterpret_cast<f32x2*>(a.ws_ml + row * 2) = f32x2{m, z};
@@ -921,6 +980,18 @@ static bool wide_fits(const DecodeArgs& a) {
   return len <= (int64_t)kWideMaxTiles * kTileKeys;
 }
 
+template <int D, bool FP8, int WC>
+static hipError_t launch_value(const DecodeArgs& a, int64_t units, hipStream_t st) {
+  constexpr int kSlotBytes = 4 * 16 * 16 * (FP8 ? 1 : 2) + WC * 1024 + 256;
+  const int lds = SpreadRing<WC>::GT * (kSlotBytes + 16);  // slots, then 4 block-table entries per tile
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&decode_value_kernel<D, FP8, WC>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((decode_value_kernel<D, FP8, WC>), dim3((unsigned)(units * (D / 16))),
+                     dim3(64 * SpreadRing<WC>::kWaves), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int D, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
@@ -932,7 +1003,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_weight_kernel<D, FP8>), dim3((unsigned)(units * a.tps)), dim3(64), 0, st, a);
     se = hipGetLastError();
     if (se != hipSuccess) return se;
-    hipLaunchKernelGGL((decode_value_kernel<D, FP8>), dim3((unsigned)(units * (D / 16))), dim3(64), 0, st, a);
+    if (a.group <= 4)
+      se = launch_value<D, FP8, 1>(a, units, st);
+    else if (a.group <= 8)
+      se = launch_value<D, FP8, 2>(a, units, st);
+    else
+      se = launch_value<D, FP8, 4>(a, units, st);
+    if (se != hipSuccess) return se;
   } else if (a.kernel == 1 && wide_fits(a)) {
     hipLaunchKernelGGL((decode_wide_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kWideWaves), 0, st, a);
   } else {

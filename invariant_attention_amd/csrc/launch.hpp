@@ -33,7 +33,7 @@ struct DecodeArgs {
   int32_t* order;              // [B * max_splits] dispatch order of the split units (workspace)
   float* ws_x;                 // spread: per slot [4 parts][4 lane groups][group][16 B]: scores, then weights
   float* ws_mx;                // spread: row maxima, [slot][16]
-  float* ws_as;                // spread: alpha and row sum, [slot][16][2]
+  float* ws_as;                // spread: (alpha, row sum, row maximum, 0), [slot][16][4]
   float c;                     // fp32(sm_scale * log2 e)
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;

@@ -17,6 +17,10 @@
 
 namespace ia {
 
+// Address-space pointer types of the direct global -> LDS copy builtin.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
 // ---------------------------------------------------------------- raw types
 
 // Raw page words of one K chunk (8 dims of one token) and of one V quad

@@ -173,9 +173,6 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
 // lane in lane order.  A page block's K or V (D x 16 values) is contiguous in
 // its page, so a tile is 4 blocks x D/32 such copies per tensor; the lanes of
 // a V copy fetch their 16 bytes from the position v_half_pos maps them to.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void gbl_void_t;
-
 template <int D>
 __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
                                              int kvh, int Hkv, int w, int lane) {

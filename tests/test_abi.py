@@ -67,16 +67,16 @@ def test_workspace_size_formula():
     assert ia.ia_decode_workspace_bytes(ctx, 0, 8192) == 0
     bc = ia.Context(ia.make_config(32, 8, 128, split_policy=ia.IA_SPLIT_BY_COUNT))
     # a launch of at most 64 split units runs the spread kernels, which add one slot per
-    # (sequence, split, kv head, tile): group x 64 fp32 scores, 16 fp32 row maxima, 16 (alpha, sum)
+    # (sequence, split, kv head, tile): group x 64 fp32 scores, 16 fp32 row maxima, 16 (alpha, sum, max, 0)
     slots = 1 * 4 * 8 * 32
     assert ia.ia_decode_workspace_bytes(ctx, 1, 8192) == (up(4 * 32 * 128 * 4) + up(4 * 32 * 2 * 4) + up(4 * 4)
                                                          + up(slots * 4 * 64 * 4) + up(slots * 16 * 4)
-                                                         + up(slots * 16 * 2 * 4))
+                                                         + up(slots * 16 * 4 * 4))
     split_only = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048, decode_kernel=ia.IA_DECODE_SPLIT))
     assert ia.ia_decode_workspace_bytes(split_only, 1, 8192) == up(4 * 32 * 128 * 4) + up(4 * 32 * 2 * 4) + up(16)
     # split-by-count: at most min(64, 256 // B) pieces, and no more than one per 64-key tile
     assert ia.ia_decode_workspace_bytes(bc, 1, 64) == (up(1 * 1 * 32 * 128 * 4) + up(32 * 2 * 4) + up(4)
-                                                       + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 2 * 4))
+                                                       + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 4 * 4))
     assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
                                                           + up(4 * 64 * 4))
 
