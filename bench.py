@@ -20,6 +20,7 @@ reference, and the fp64 CPU oracle timed on a bounded sample of the same workloa
     python bench.py --copy-probe        a plain copy of known size (counter calibration)
     python bench.py --suite             also the long-context, mixed and shared-prefix workloads
     python bench.py --summarize-profile TRACE_DIR PMC_DIR   write the profile summary under profiles/
+    python bench.py --summarize-spread-profile TRACE_DIR    the batch-1 spread-kernel trace summary
 
 The roofline's `traffic` (HBM bytes per launch of the decode split kernel) comes from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters, each scaled by what the same counter reads for a plain 1 GiB
@@ -219,6 +220,49 @@ def summarize_profile(trace_dir, pmc_dir):
     with open(PROFILE_MD, "w") as f:
         f.write("\n".join(lines))
     print(PROFILE_MD)
+
+
+SPREAD_PROFILE_MD = os.path.join(ROOT, "profiles", "decode_spread_kernels_llama3-8b_b1.md")
+
+
+def summarize_spread_profile(trace_dir):
+    """Writes the kernel-trace summary of one batch-1 decode call on the spread kernels."""
+    stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    names = ["decode_score_kernel<128, false>", "decode_weight_kernel<128, false>",
+             "decode_value_kernel<128, false, 1>", "decode_merge_kernel<128, false>"]
+    rows = [r for n in names for r in stats if n in r["Name"]]
+    lens = wl.uniform_lens(SEED, 256, 512, 8192)[:1]
+    alg = int(sum(lens)) * 8 * 128 * 2 * 2
+    total = sum(float(r["AverageNs"]) for r in rows)
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o spread -- "
+           "python3 bench.py --decode-only --no-cpu-baseline --batch 1 --steps 20 --warmup 5")
+    lines = [
+        "# decode spread kernels -- Llama-3-8B-shaped decode, batch 1",
+        "",
+        f"32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits, one sequence of "
+        f"{int(sum(lens))} keys (the first of the batch-256 workload): 4 splits x 8 KV heads = 32 split units, "
+        f"which IA_DECODE_AUTO runs on the spread kernels; algorithmic KV bytes per call {alg}.",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)",
+        "",
+        f"    {cmd}",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    lines += [
+        "",
+        f"Sum of the four kernels' average durations: {total / 1e3:.1f} us per decode call "
+        f"({alg / total:.1f} GB/s of algorithmic KV bytes, {alg / total / HBM_PEAK_GBS:.4f} of the 8 TB/s peak). "
+        "Each kernel is about one round trip to memory plus its launch; the value kernel holds two round trips "
+        "(block-table entries, then the copies) and the 32-step chain of one split.",
+        "",
+    ]
+    with open(SPREAD_PROFILE_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(SPREAD_PROFILE_MD)
 
 
 PREFILL_KERNEL = "prefill_kernel<128, false>"
@@ -658,12 +702,16 @@ def main():
     ap.add_argument("--layer-only", action="store_true", help="time the layer operators only (for profilers)")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
+    ap.add_argument("--summarize-spread-profile", metavar="TRACE_DIR")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile)
         return
     if args.summarize_prefill_profile:
         summarize_prefill_profile(*args.summarize_prefill_profile)
+        return
+    if args.summarize_spread_profile:
+        summarize_spread_profile(args.summarize_spread_profile)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; there is no multi-GPU path (run with --gpus 1)",
