@@ -84,7 +84,13 @@ int decode_kernel_for(const ia_ctx* ctx, int64_t B, int64_t max_seq_len) {
     case IA_DECODE_WIDE: return 1;
     case IA_DECODE_SPLIT: return 0;
     case IA_DECODE_SPREAD: return spread_fits ? 2 : 0;
-    default: return spread_fits && units <= kSpreadMaxUnits ? 2 : 0;
+    default: {
+      // Measured: the spread kernels win for a few dozen units when a split's
+      // tiles fit one staging group of the value kernel (at most 32 tiles, up
+      // to 4 query heads per kv head); otherwise the split kernel is faster.
+      const bool one_group = ctx->group <= 4 && decode_split_tiles(ctx, B, max_seq_len) <= 32;
+      return spread_fits && one_group && units <= kSpreadMaxUnits ? 2 : 0;
+    }
   }
 }
 
