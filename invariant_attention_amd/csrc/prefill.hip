@@ -1,11 +1,14 @@
 // prefill.hip -- chunked / whole prefill (causal, grouped-query) with K/V
-// tiles staged in LDS and shared by the 8 waves of a workgroup.  All
+// tiles staged in LDS and shared by the 4 waves of a workgroup.  All
 // value-relevant arithmetic is in arith.hpp; each row runs exactly the
 // decode row's operations at its position (Vosti §5.3, App. A.1-A.5).
 //
 // Rows.  A wave owns 16 rows = 16/g consecutive positions x the g query
-// heads of one kv head; a workgroup of 8 waves owns 8 * 16/g consecutive
-// positions of one sequence.  The workgroup walks 64-key tiles 0..T of the
+// heads of one kv head; a workgroup of 4 waves owns 4 * 16/g consecutive
+// positions of one sequence.  Two workgroups share a compute unit (2 x 64 KiB
+// of LDS, 2 waves per SIMD) and run out of step with each other, so one's
+// value products overlap the other's softmax; one workgroup of 8 waves per
+// compute unit, whose waves meet at every tile's barrier, measured ~3% slower.  The workgroup walks 64-key tiles 0..T of the
 // keys its last row can see; splits of S keys start a fresh state, and at a
 // split's end every row that reaches into it folds the split's state into its
 // running merge (ascending order, as in decode).  Tiles past all of a wave's
@@ -35,7 +38,7 @@
 
 namespace ia {
 
-constexpr int kPrefillWaves = 8;
+constexpr int kPrefillWaves = 4;  // per workgroup; 2 workgroups per compute unit
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
@@ -264,7 +267,7 @@ __device__ __forceinline__ void lds_tile_scores(const uint8_t* tile, const QFrag
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   constexpr int kTileBytes = tile_lds_bytes<D>();
   const int tid = threadIdx.x;
