@@ -173,17 +173,19 @@ def test_v9_decode_entry_equals_prefill_entry_qlen1():
 
 @pytest.mark.parametrize("budget", [64, 256, 1024])
 def test_v3_chunk_budgets_equal_whole_prefill(budget):
+    # The Qwen3-8B-shaped chunked-prefill workload at its own size: 8 prompts of 4096 tokens,
+    # processed whole and in chunks (all 8 prompts' chunk k in one call).
     shape = wl.QWEN3_8B
-    n = 4096
-    w = World(shape, [n, n])
-    whole = w.prefill_rows([0, 1], [n, n])
+    n, B = 4096, 8
+    w = World(shape, [n] * B)
+    whole = w.prefill_rows(list(range(B)), [n] * B)
     outs = []
     for c0 in range(0, n, budget):
         c1 = min(n, c0 + budget)
-        # both prompts' chunk k in one call; keys beyond c1 exist in the pages but are causally masked
-        outs.append(w.prefill_rows([0, 1], [c1 - c0, c1 - c0], seq_lens=[c1, c1]))
-    chunked = torch.cat([torch.cat([o[:len(o) // 2] for o in outs]), torch.cat([o[len(o) // 2:] for o in outs])])
-    assert _eq(chunked, whole)
+        # keys beyond c1 exist in the pages but are causally masked
+        outs.append(w.prefill_rows(list(range(B)), [c1 - c0] * B, seq_lens=[c1] * B))
+    per = [torch.cat([o[b * len(o) // B:(b + 1) * len(o) // B] for o in outs]) for b in range(B)]
+    assert _eq(torch.cat(per), whole)
 
 
 # ------------------------------------------------------------ positive control
