@@ -369,13 +369,14 @@ def make_ctx(shape, by_count=False, fp8=False, decode_kernel=None):
 class DecodeWorld:
     """A decode workload resident on the GPU: pages, tables, queries, new-token rows, slots."""
 
-    def __init__(self, shape: wl.AttnShape, lens, fp8=False, shared_prefix=0, width=None, scales=None):
+    def __init__(self, shape: wl.AttnShape, lens, fp8=False, shared_prefix=0, width=None, scales=None,
+                 layout_seed=3):
         self.shape = shape
         self.lens = [int(n) for n in lens]
         self.B = len(self.lens)
         self.fp8 = fp8
         self.seqs = wl.make_sequences(self.lens, shared_prefix=shared_prefix)
-        self.layout = wl.layout_pages(3, self.lens, shape.P, shared_prefix=shared_prefix, width=width)
+        self.layout = wl.layout_pages(layout_seed, self.lens, shape.P, shared_prefix=shared_prefix, width=width)
         self.ctx = make_ctx(shape, fp8=fp8)
         dt = torch.uint8 if fp8 else torch.bfloat16
         npg = self.layout.num_pages
@@ -498,6 +499,93 @@ def invariance_pairs(world: DecodeWorld, ctx, probes):
         cmp(sub)
     cmp(list(reversed(range(B))))
     return eq, tot
+
+
+def _row_bits(t):
+    return t.view(torch.int16).cpu().numpy().reshape(t.shape[0], -1)
+
+
+def _equal_rows(a, b):
+    return int((_row_bits(a) == _row_bits(b)).all(axis=1).sum()), int(a.shape[0])
+
+
+def _prefill_world(shape, lens, layout_seed):
+    """Pages, queries and tables of whole prompts (every position's K/V appended)."""
+    seqs = wl.make_sequences(lens, first_sid=2000)
+    layout = wl.layout_pages(layout_seed, lens, shape.P)
+    ctx = make_ctx(shape)
+    k = torch.zeros((layout.num_pages, shape.Hkv, shape.d // 8, shape.P, 8), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros((layout.num_pages, shape.Hkv, shape.d, shape.P), dtype=torch.bfloat16, device=DEV)
+    for b, s in enumerate(seqs):
+        sl = torch.as_tensor(layout.slots(b, 0, s.n, shape.P), device=DEV)
+        ia.ia_kv_append(ctx, s.k(SEED, shape).to(DEV), s.v(SEED, shape).to(DEV), sl, k, v)
+    return seqs, layout, ctx, k, v
+
+
+def _prefill_rows(shape, seqs, layout, ctx, k, v, p0, p1):
+    """Rows p0 .. p1 - 1 of every prompt in one prefill call (key length p1)."""
+    q = torch.cat([s.q(SEED, shape, p0, p1) for s in seqs]).to(DEV)
+    B = len(seqs)
+    cu = torch.as_tensor(np.arange(0, B * (p1 - p0) + 1, p1 - p0, dtype=np.int32), device=DEV)
+    sl = torch.as_tensor(np.full(B, p1, np.int32), device=DEV)
+    bt = torch.as_tensor(layout.block_table, device=DEV)
+    out = torch.empty_like(q)
+    ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, p1 - p0, p1, out)
+    return out.view(B, p1 - p0, shape.Hq, shape.d)
+
+
+def invariance_variations(lens):
+    """Bitwise comparisons for the execution variations other than batch composition: the
+    Llama-3-8B decode rows of 8 sequences on a second random page placement and with a 16x wider
+    block table, decode against prefill at 16 positions of each, and the Qwen3-8B prefill of 2
+    prompts of 4096 tokens whole against chunks of 64 / 256 / 1024 and against its second half
+    served from pages written by an earlier call (a cached 2048-token prefix).  A pair is one
+    output row (all query heads).  Returns {variation: (equal, compared)}."""
+    res = {}
+    shape = wl.LLAMA3_8B
+    lens8 = [int(x) for x in lens[:8]]
+    w1 = DecodeWorld(shape, lens8)
+    w2 = DecodeWorld(shape, lens8, layout_seed=7)
+    wide = DecodeWorld(shape, lens8, width=16 * (max(lens8) // shape.P + 1))
+    r1, r2, r3 = DecodeRunner(w1, range(8)), DecodeRunner(w2, range(8)), DecodeRunner(wide, range(8))
+    for r in (r1, r2, r3):
+        r.decode(None)
+    res["decode_page_placement"] = _equal_rows(r2.out, r1.out)
+    res["decode_table_width"] = _equal_rows(r3.out, r1.out)
+    # decode at n' = n - j against the prefill rows of the last 16 positions (keys past n' exist
+    # in the pages but are causally masked)
+    eq = tot = 0
+    q16 = torch.cat([w1.seqs[b].q(SEED, shape, lens8[b] - 16, lens8[b]) for b in range(8)]).to(DEV)
+    cu = torch.as_tensor(np.arange(0, 8 * 16 + 1, 16, dtype=np.int32), device=DEV)
+    sl = torch.as_tensor(np.array(lens8, np.int32), device=DEV)
+    pre = torch.empty((8 * 16, shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
+    ia.ia_paged_attn_prefill(w1.ctx, q16, cu, sl, w1.k, w1.v, w1.bt, 16, max(lens8), pre)
+    pre = pre.view(8, 16, shape.Hq, shape.d)
+    ws = torch.empty(ia.ia_decode_workspace_bytes(w1.ctx, 8, max(lens8)), dtype=torch.uint8, device=DEV)
+    for j in range(16):
+        nj = [n - 16 + j + 1 for n in lens8]
+        qd = torch.stack([q16[b * 16 + j] for b in range(8)])
+        out = torch.empty((8, shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
+        ia.ia_paged_attn_decode(w1.ctx, qd, w1.k, w1.v, w1.bt, torch.as_tensor(np.array(nj, np.int32), device=DEV),
+                                max(lens8), out, ws)
+        e, t = _equal_rows(out, pre[:, j])
+        eq, tot = eq + e, tot + t
+    res["decode_vs_prefill"] = (eq, tot)
+    del w1, w2, wide, r1, r2, r3
+    torch.cuda.empty_cache()
+    shape = wl.QWEN3_8B
+    n = 4096
+    seqs, layout, ctx, k, v = _prefill_world(shape, [n, n], 11)
+    whole = _prefill_rows(shape, seqs, layout, ctx, k, v, 0, n)
+    for budget in (64, 256, 1024):
+        parts = [_prefill_rows(shape, seqs, layout, ctx, k, v, c0, min(n, c0 + budget)) for c0 in range(0, n, budget)]
+        chunked = torch.cat(parts, dim=1)
+        res[f"prefill_chunks_{budget}"] = _equal_rows(chunked.reshape(-1, shape.Hq, shape.d),
+                                                     whole.reshape(-1, shape.Hq, shape.d))
+    half = _prefill_rows(shape, seqs, layout, ctx, k, v, n // 2, n)
+    res["prefill_cached_prefix_2048"] = _equal_rows(half.reshape(-1, shape.Hq, shape.d),
+                                                     whole[:, n // 2:].reshape(-1, shape.Hq, shape.d))
+    return res
 
 
 def copy_gbs(nbytes=COPY_PROBE_BYTES, reps=10):
@@ -790,10 +878,14 @@ def main():
         probes = [0, 1, 37, 100, 200, args.batch - 1]
         eq, tot = invariance_pairs(world, world.ctx, probes)
         eq_c, tot_c = invariance_pairs(world, bc_ctx, probes)
-        result["invariance_rate"] = round(eq / tot, 6)
-        result["invariance_pairs"] = f"{eq}/{tot}"
+        var = invariance_variations(lens)
+        var["batch_composition"] = (eq, tot)
+        eq_all, tot_all = sum(e for e, _ in var.values()), sum(t for _, t in var.values())
+        result["invariance_rate"] = round(eq_all / tot_all, 6)
+        result["invariance_pairs"] = f"{eq_all}/{tot_all}"
+        result["invariance_by_variation"] = {k: f"{e}/{t}" for k, (e, t) in var.items()}
         result["split_by_count_invariance_rate"] = round(eq_c / tot_c, 6)
-        log(f"invariance: fixed {eq}/{tot}, split-by-count {eq_c}/{tot_c}")
+        log(f"invariance: fixed {eq_all}/{tot_all} {result['invariance_by_variation']}, split-by-count {eq_c}/{tot_c}")
         del world, head
         torch.cuda.empty_cache()
         result["prefill"] = prefill_tflops(max(3, args.steps // 4), 1)
