@@ -448,9 +448,24 @@ class DecodeRunner:
                                 self.ws, self.w.k_scale, self.w.v_scale, stream=stream)
 
 
-def time_steps(runner: DecodeRunner, steps: int, warmup: int, with_append=True):
+FLUSH_BYTES = 512 << 20
+_flush_buf = None
+
+
+def flush_caches(stream):
+    """Writes a 512 MiB buffer: the L2s and the 256 MB MALL then hold none of the workload's data."""
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(stream):
+        _flush_buf.fill_(1.0)
+
+
+def time_steps(runner: DecodeRunner, steps: int, warmup: int, with_append=True, flush=False):
     """Times `steps` steps.  Returns (ms per step over the whole timed region, mean ms of the decode
-    call alone).  All work goes to torch's current stream, which the events are recorded on."""
+    call alone).  All work goes to torch's current stream, which the events are recorded on.
+    flush: a 512 MiB write before each decode call (outside its events; the step time then
+    includes it), so the call reads its K/V from HBM rather than from the caches."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         if with_append:
@@ -463,6 +478,8 @@ def time_steps(runner: DecodeRunner, steps: int, warmup: int, with_append=True):
     for e1, e2 in ev:
         if with_append:
             runner.append(stream)
+        if flush:
+            flush_caches(stream)
         e1.record(stream)
         runner.decode(stream)
         e2.record(stream)
@@ -852,17 +869,27 @@ def main():
         bc_ctx = make_ctx(shape, by_count=True)
         for B in (1, 8, 64, args.batch):
             s_ms, d_ms = time_steps(DecodeRunner(world, range(B)), args.steps, args.warmup)
+            _, dc_ms = time_steps(DecodeRunner(world, range(B)), args.steps, args.warmup, flush=True)
             kb = world.kv_bytes(range(B))
             batches[str(B)] = {"step_ms": round(s_ms, 4), "decode_ms": round(d_ms, 4),
-                               "gbs": round(kb / (s_ms * 1e-3) / 1e9, 1)}
+                               "gbs": round(kb / (s_ms * 1e-3) / 1e9, 1), "decode_ms_cold": round(dc_ms, 4),
+                               "decode_gbs_cold": round(kb / (dc_ms * 1e-3) / 1e9, 1)}
             s2, d2 = time_steps(DecodeRunner(world, range(B), bc_ctx), args.steps, args.warmup)
+            _, d2c = time_steps(DecodeRunner(world, range(B), bc_ctx), args.steps, args.warmup, flush=True)
             by_count[str(B)] = {"step_ms": round(s2, 4), "gbs": round(kb / (s2 * 1e-3) / 1e9, 1),
-                                "fixed_over_by_count_time": round(s_ms / s2, 3)}
+                                "fixed_over_by_count_time": round(s_ms / s2, 3), "decode_ms_cold": round(d2c, 4),
+                                "fixed_over_by_count_time_cold": round(dc_ms / d2c, 3)}
             log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
         result["batches"] = batches
         result["split_by_count"] = by_count
+        # The same decode call with the caches flushed before each call (no K/V, table or TLB state
+        # left from the previous step), beside the steady-state figure above.
+        cold_ms = batches[str(args.batch)]["decode_ms_cold"]
+        result["roofline"]["cache_flushed"] = {"avg_launch_ms": cold_ms,
+                                               "achieved": round(kvb / (cold_ms * 1e-3) / 1e9, 2),
+                                               "frac": round(kvb / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # The bitwise-equivalent decode kernels at small batches: the split kernel alone, the spread
-        # pair alone (the automatic choice runs it up to 512 split units) and the wide kernel.
+        # kernels alone (the automatic choice runs them up to 64 split units) and the wide kernel.
         kern = {}
         for name, kid in (("split", ia.IA_DECODE_SPLIT), ("spread", ia.IA_DECODE_SPREAD), ("wide", ia.IA_DECODE_WIDE)):
             kctx = make_ctx(shape, decode_kernel=kid)
@@ -873,6 +900,9 @@ def main():
                 s_ms, d_ms = time_steps(DecodeRunner(world, range(B), kctx), args.steps, args.warmup)
                 kern[name][str(B)] = {"decode_ms": round(d_ms, 4),
                                       "decode_gbs": round(world.kv_bytes(range(B)) / (d_ms * 1e-3) / 1e9, 1)}
+                if B in (1, 8):
+                    _, dc = time_steps(DecodeRunner(world, range(B), kctx), args.steps, args.warmup, flush=True)
+                    kern[name][str(B)]["decode_ms_cold"] = round(dc, 4)
             log(f"{name} decode kernel: {kern[name]}")
         result["decode_kernels"] = kern
         probes = [0, 1, 37, 100, 200, args.batch - 1]
