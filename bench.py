@@ -450,21 +450,23 @@ class DecodeRunner:
 
 FLUSH_BYTES = 512 << 20
 _flush_buf = None
+_flush_out = None
 
 
 def flush_caches(stream):
-    """Writes a 512 MiB buffer: the L2s and the 256 MB MALL then hold none of the workload's data."""
-    global _flush_buf
+    """Reads a 512 MiB buffer: the L2s and the 256 MB MALL then hold none of the workload's data.
+    (A read, not a write: written lines would be written back to HBM during the timed call.)"""
+    global _flush_buf, _flush_out
     if _flush_buf is None:
-        _flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=DEV)
+        _flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=DEV)
     with torch.cuda.stream(stream):
-        _flush_buf.fill_(1.0)
+        _flush_out = _flush_buf.sum()
 
 
 def time_steps(runner: DecodeRunner, steps: int, warmup: int, with_append=True, flush=False):
     """Times `steps` steps.  Returns (ms per step over the whole timed region, mean ms of the decode
     call alone).  All work goes to torch's current stream, which the events are recorded on.
-    flush: a 512 MiB write before each decode call (outside its events; the step time then
+    flush: a 512 MiB read before each decode call (outside its events; the step time then
     includes it), so the call reads its K/V from HBM rather than from the caches."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -882,8 +884,8 @@ def main():
             log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
         result["batches"] = batches
         result["split_by_count"] = by_count
-        # The same decode call with the caches flushed before each call (no K/V, table or TLB state
-        # left from the previous step), beside the steady-state figure above.
+        # The same decode call with the caches flushed before each call (no K/V or table data left
+        # from the previous step), beside the steady-state figure above.
         cold_ms = batches[str(args.batch)]["decode_ms_cold"]
         result["roofline"]["cache_flushed"] = {"avg_launch_ms": cold_ms,
                                                "achieved": round(kvb / (cold_ms * 1e-3) / 1e9, 2),
