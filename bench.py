@@ -624,6 +624,24 @@ def copy_gbs(nbytes=COPY_PROBE_BYTES, reps=10):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 4), "gbs": round(2 * nbytes / ms / 1e6, 1)}
 
 
+def read_gbs(nbytes=4 * COPY_PROBE_BYTES, reps=10):
+    """A plain device read (torch's sum over 4 GiB of fp32): bytes read / time."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=DEV)
+    for _ in range(2):
+        src.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        src.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1)}
+
+
 def prefill_tflops(steps: int, warmup: int):
     """Whole prefill of 8 prompts x 4096 tokens (Qwen3-8B shape); flops = 4 d Hq sum_rows (p+1)."""
     shape = wl.QWEN3_8B
@@ -866,7 +884,8 @@ def main():
     }
     if not args.decode_only:
         result["copy_reference"] = copy_gbs()
-        log(f"plain copy: {result['copy_reference']}")
+        result["read_reference"] = read_gbs()
+        log(f"plain copy: {result['copy_reference']}, plain read: {result['read_reference']}")
         batches, by_count = {}, {}
         bc_ctx = make_ctx(shape, by_count=True)
         for B in (1, 8, 64, args.batch):
