@@ -20,13 +20,14 @@
 // (global_load_lds, 1 KiB runs of K and V), with a zero fill of the keys past
 // the sequence end only in a tile that has them; e4m3 pages go through
 // registers, where they are zero filled and converted to bf16 (exactly).
-// Both tensors keep the pages' own layout:
+// K keeps the pages' own layout; V is regrouped by key pair:
 //   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B
-//   LDS V: [4 blocks][D dims][2 halves] x 16 B   (8 tokens per half)
-// except that in V the two halves of a dim row trade places when bit 3 of
-// the dim is set, so a wave's 8-byte fragment reads hit 64 distinct banks.
-// A K operand fragment is one 16-byte LDS read; a V fragment is two 8-byte
-// reads (tokens 4g..4g+3 of two page blocks).
+//   LDS V: [2 block pairs][D/16 dim groups][2 blocks][16 dims][2 halves] x 16 B
+// (8 tokens per half), so the two page blocks of a key pair sit 512 bytes
+// apart for each dim, and in V the two halves of a dim row trade places when
+// bit 3 of the dim is set, so a wave's 8-byte fragment reads hit 64 distinct
+// banks.  A K operand fragment is one 16-byte LDS read; a V fragment is two
+// 8-byte reads 512 bytes apart (tokens 4g..4g+3 of the two page blocks).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +59,21 @@ constexpr int tile_lds_bytes() {
 // LDS position of V half `half` of dim `dim` in a page block's copy: halves
 // swap when bit 3 of the dim is set (and the map is its own inverse).
 __device__ __forceinline__ int v_half_pos(int dim, int half) { return half ^ ((dim >> 3) & 1); }
+
+// The page block, dim and half held by 16-byte unit c of a tile's LDS V.
+// The V region is D/8 runs of 1 KiB, run (k, m) = (c / 64) for key pair k
+// (page blocks 2k, 2k+1) and dims 16m..16m+15: its first 512 bytes hold those
+// dims of block 2k, the next 512 the same dims of block 2k+1, each dim as its
+// two 8-token halves (placed by v_half_pos).  A V operand fragment (4 tokens
+// of blocks 2k and 2k+1 for one dim) is then two 8-byte reads 512 bytes apart,
+// which one paired LDS read returns in operand order.
+template <int D>
+__device__ __forceinline__ void v_unit(int c, int& blk, int& dim, int& half) {
+  const int run = c >> 6, l = c & 63;
+  blk = 2 * (run / (D / 16)) + (l >> 5);
+  dim = 16 * (run % (D / 16)) + ((l & 31) >> 1);
+  half = v_half_pos(dim, l & 1);
+}
 
 // Staging registers of one thread for one tile (e4m3 pages).
 //  K: the tile's K is 4 page blocks of D * 16 elements in the pages' own
@@ -108,7 +124,8 @@ __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc,
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int blk = c / (2 * D), dim = (c % (2 * D)) >> 1, half = v_half_pos(dim, c & 1);
+    int blk, dim, half;
+    v_unit<D>(c, blk, dim, half);
     st.vnv[i] = select4(blk, tp.valid) - 8 * half;
     const uint8_t* base = vc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
 #pragma unroll
@@ -174,8 +191,8 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
 // The data moves from the pages to LDS without passing through registers.
 // Each instruction of a wave fills a contiguous 1 KiB LDS run, 16 bytes per
 // lane in lane order.  A page block's K or V (D x 16 values) is contiguous in
-// its page, so a tile is 4 blocks x D/32 such copies per tensor; the lanes of
-// a V copy fetch their 16 bytes from the position v_half_pos maps them to.
+// its page, so a tile's K is 4 blocks x D/32 such copies; a V copy fills one
+// run of the V region, each lane fetching the 16 bytes v_unit assigns it.
 template <int D>
 __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
                                              int kvh, int Hkv, int w, int lane) {
@@ -191,10 +208,10 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
     const int pg = blk == 0 ? tp.page[0] : (blk == 1 ? tp.page[1] : (blk == 2 ? tp.page[2] : tp.page[3]));
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(kc, pg) + part * 1024 + lane * 16),
                                      (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
-    // V: LDS unit u = 64 part + lane of the block = dim u / 2, position u % 2.
-    const int u = part * 64 + lane;
-    const int dim = u >> 1;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, pg) + dim * 32 + v_half_pos(dim, u & 1) * 16),
+    // V: run ch; the lane's unit comes from a block that depends on the lane.
+    int vb, vd, vh;
+    v_unit<D>(ch * 64 + lane, vb, vd, vh);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, select4(vb, tp.page)) + vd * 32 + vh * 16),
                                      (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
   }
 }
@@ -218,8 +235,9 @@ __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp,
 #pragma unroll
   for (int i = 0; i < kVUnits / kPrefillThreads; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const int blk = c / (2 * D), dim = (c % (2 * D)) >> 1;
-    const int nv = select4(blk, tp.valid) - 8 * v_half_pos(dim, c & 1);
+    int blk, dim, half;
+    v_unit<D>(c, blk, dim, half);
+    const int nv = select4(blk, tp.valid) - 8 * half;
     uint4* p = reinterpret_cast<uint4*>(slot + kKBytes + (size_t)c * 16);
     const uint4 v = *p;
     const uint2 lo = v_keep(make_uint2(v.x, v.y), nv), hi = v_keep(make_uint2(v.z, v.w), nv - 4);
@@ -240,16 +258,17 @@ __device__ __forceinline__ void lds_k_block(const uint8_t* lds, int blk, int r, 
         bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + r) * 16));
 }
 // V^T fragment of dim block mb for key half ks2: tokens 4g..4g+3 of page
-// blocks 2 ks2 and 2 ks2 + 1 for dim 16 mb + r (8 bytes from each).
+// blocks 2 ks2 and 2 ks2 + 1 for dim 16 mb + r (8 bytes from each, 512 bytes
+// apart in run (ks2, mb)).
 template <int D>
 __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, int g, bf16x8 (&vf)[2]) {
   constexpr int kKBytes = kTileKeys * D * 2;
   const int dim = 16 * mb + r;
-  const uint8_t* base = lds + kKBytes + dim * 32 + v_half_pos(dim, g >> 1) * 16 + 8 * (g & 1);
+  const uint8_t* base = lds + kKBytes + mb * 1024 + r * 32 + v_half_pos(dim, g >> 1) * 16 + 8 * (g & 1);
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(base + (2 * ks2) * D * 32);
-    const uint2 hi = *reinterpret_cast<const uint2*>(base + (2 * ks2 + 1) * D * 32);
+    const uint2 lo = *reinterpret_cast<const uint2*>(base + ks2 * (D / 16) * 1024);
+    const uint2 hi = *reinterpret_cast<const uint2*>(base + ks2 * (D / 16) * 1024 + 512);
     vf[ks2] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
 }
