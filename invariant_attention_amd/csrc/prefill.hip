@@ -413,19 +413,23 @@ __global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_ke
       f32x4 sc[4];
       bf16x8 kf[2][D / 32];
       lds_k_block<D>(tile, 0, r, g, kf[0]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         if (blk < 3) lds_k_block<D>(tile, blk + 1, r, g, kf[(blk + 1) & 1]);
         sc[blk] = block_scores<D>(kf[blk & 1], q);
       }
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 vf[2][2];
       lds_v_block<D>(tile, 0, r, g, vf[0]);
       const TileStep ts = tile_softmax<MASK>(st.m, st.z, sc, c, t0, lo, limit, g);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < D / 16; ++mb) {
         if (mb + 1 < D / 16) lds_v_block<D>(tile, mb + 1, r, g, vf[(mb + 1) & 1]);
         st.u[mb] = pv_block<MASK>(st.u[mb], vf[mb & 1], ts);
       }
+      __builtin_amdgcn_s_setprio(0);
       commit_scalars<MASK>(st.m, st.z, ts);
     };
     if (needs(t)) {
