@@ -164,6 +164,22 @@ def test_v5_decode_equals_prefill_at_every_position(shape, lens):
         off += n
 
 
+@pytest.mark.parametrize("shape,lens", [(wl.TINY, list(wl.TINY_LENS)), (wl.LLAMA31_70B, [2100, 300])],
+                         ids=["tiny", "llama70b"])
+def test_v5_fp8_decode_equals_prefill(shape, lens):
+    # e4m3 pages: prefill converts them while staging, decode while loading; both must give the
+    # same bits at every position checked
+    w = World(shape, lens, fp8=True, scales=wl.fp8_scales(21, shape.Hkv, False))
+    pre = w.prefill_rows(range(len(lens)), lens)
+    off = 0
+    for b, n in enumerate(lens):
+        positions = sorted(set([0, n - 1, n // 2] + list(range(max(0, n - 40), n, 5))
+                               + [p for p in (63, 64, 127, 128, 2047, 2048) if p < n]))
+        dec = w.decode_rows([b] * len(positions), positions)
+        assert all(_rows_equal(dec, pre[[off + p for p in positions]]))
+        off += n
+
+
 def test_v9_decode_entry_equals_prefill_entry_qlen1():
     w = World(wl.LLAMA3_8B, wl.uniform_lens(15, 12, 512, 8192))
     dec = w.decode_rows()

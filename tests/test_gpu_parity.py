@@ -159,6 +159,18 @@ def test_fp8_prefill_matches_oracle():
     ok, err, ratio = gs.within_tolerance(out, ref)
     assert ok, f"max abs err {err}, worst err/bound {ratio}"
 
+def test_fp8_prefill_head_dim_64_ragged():
+    # e4m3 pages at head_dim 64, grouped 3:1, with tiles that end inside a page block and a
+    # sequence shorter than one tile
+    shape = wl.AttnShape(Hq=6, Hkv=2, d=64, P=16, S=64)
+    lens = [130, 64, 7]
+    scales = wl.fp8_scales(11, shape.Hkv, False)
+    seqs, layout, ctx, pages = _setup(shape, lens, fp8=True, scales=scales)
+    ref, q, cu, *_ = _oracle(shape, seqs, layout, 0, [130, 20, 7], fp8=True, scales=scales)
+    out = gs.prefill(ctx, pages, q, cu, layout, lens)
+    ok, err, ratio = gs.within_tolerance(out, ref)
+    assert ok, f"max abs err {err}, worst err/bound {ratio}"
+
 # ------------------------------------------------- unwritten page slots
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
