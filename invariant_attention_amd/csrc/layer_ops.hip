@@ -89,61 +89,63 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const __bf16* __r
 // --------------------------------------------------------------------- GEMM
 
 constexpr int kComputeUnits = 256;              // MI355X
-constexpr int kBK = 32;                          // K step
+constexpr int kBK = 32;                          // K granularity of every tile (and the big tile's K step)
 constexpr int kStages = 4;                       // LDS ring slots
-constexpr int kChunks = kBK / 8;                 // 16-byte chunks (8 k) per tile row
-constexpr int kRowBytes = kBK * 2;               // 64 B
-constexpr int kRowsPerCopy = 1024 / kRowBytes;   // rows one 1 KiB copy fills: 16
 
-// A workgroup tile of BM x BN outputs over WM x WN waves; each wave owns a
-// (BM / WM) x (BN / WN) block as 32 x 32 MFMA tiles.  Every configuration
-// computes each output with the same MFMA chain over k in ascending order,
-// so the choice of tile never changes a bit.
-template <int BM_, int BN_, int WM_, int WN_>
+// A workgroup tile of BM x BN outputs over WM x WN waves, K steps of BK; each
+// wave owns a (BM / WM) x (BN / WN) block as 32 x 32 MFMA tiles.  Every
+// configuration computes each output with the same MFMA chain over k in
+// ascending 16-wide steps, so neither the tile nor its K step changes a bit.
+template <int BM_, int BN_, int WM_, int WN_, int BK_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kMI = BM / WM / 32, kNI = BN / WN / 32;
+  static constexpr int kChunks = BK / 8;                 // 16-byte chunks (8 k) per tile row
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;  // rows one 1 KiB copy fills
   static constexpr int kATileBytes = BM * kRowBytes;
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
   static constexpr int kALoads = BM / kRowsPerCopy / kWaves;  // 1 KiB copies per wave per stage
   static constexpr int kBLoads = BN / kRowsPerCopy / kWaves;
   static constexpr int kLoadsPerStage = kALoads + kBLoads;
+  static_assert(BK % kBK == 0 && kChunks <= 16, "K step");
   static_assert(kMI >= 1 && kNI >= 1 && kALoads >= 1 && kBLoads >= 1, "tile must divide over the waves");
   static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BN % (kRowsPerCopy * kWaves) == 0, "copies per wave");
+  // A tile row holds its chunks at positions c ^ ((row / (16 / kChunks)) %
+  // kChunks), so the 16 rows a quarter-wave reads for one chunk fall on 16
+  // distinct 16-byte bank groups (256 bytes span the 64 banks).
+  static __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row / (16 / kChunks)) & (kChunks - 1)); }
 };
-using BigTile = Tile<256, 256, 2, 4>;   // 8 waves of 128 x 64
-using SmallTile = Tile<64, 64, 2, 2>;   // 4 waves of 32 x 32, for calls with few big tiles
-
-// A tile row holds its 4 chunks at positions c ^ ((row >> 2) & 3), so the 16
-// rows a quarter-wave reads for one chunk fall on 16 distinct bank groups
-// (rows are 64 B: 4 rows span the 64 banks).
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
+using BigTile = Tile<256, 256, 2, 4, 32>;     // 8 waves of 128 x 64
+using SmallTile = Tile<64, 64, 2, 2, 32>;     // 4 waves of 32 x 32, for calls with few big tiles
+using SmallTileK128 = Tile<64, 64, 2, 2, 128>;  // the same with 4x the work between barriers
 
 // Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
-// Copy i of wave w fills tile rows 16 (i * waves + w) .. +15; lane l writes
-// row + l / 4, position l % 4, from chunk swz(row, l % 4) of that row.  Rows
-// past M read row M - 1 (never stored).
+// Copy i of wave w fills the kRowsPerCopy tile rows from kRowsPerCopy (i *
+// waves + w); lane l writes row + l / kChunks, position l % kChunks, from
+// chunk swz(row, l % kChunks) of that row.  Rows past M read row M - 1 (never
+// stored).
 template <class T>
 __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const __bf16* wt, int M, int K, int m0,
                                            int n0, int kt, int w, int lane) {
-  const int k0 = kt * kBK;
+  const int k0 = kt * T::BK;
 #pragma unroll
   for (int i = 0; i < T::kALoads; ++i) {
-    const int r0 = (i * T::kWaves + w) * kRowsPerCopy;
-    const int row = r0 + lane / kChunks;
+    const int r0 = (i * T::kWaves + w) * T::kRowsPerCopy;
+    const int row = r0 + lane / T::kChunks;
     int m = m0 + row;
     m = m < M ? m : M - 1;
-    const __bf16* src = a + (size_t)m * K + k0 + 8 * swz(row, lane % kChunks);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + r0 * kRowBytes), 16, 0, 0);
+    const __bf16* src = a + (size_t)m * K + k0 + 8 * T::swz(row, lane % T::kChunks);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + r0 * T::kRowBytes), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < T::kBLoads; ++i) {
-    const int r0 = (i * T::kWaves + w) * kRowsPerCopy;
-    const int row = r0 + lane / kChunks;
-    const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * swz(row, lane % kChunks);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + T::kATileBytes + r0 * kRowBytes), 16, 0,
-                                     0);
+    const int r0 = (i * T::kWaves + w) * T::kRowsPerCopy;
+    const int row = r0 + lane / T::kChunks;
+    const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * T::swz(row, lane % T::kChunks);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + T::kATileBytes + r0 * T::kRowBytes), 16,
+                                     0, 0);
   }
 }
 
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
   const int ntn = N / T::BN;
   const int n0 = (blockIdx.x % ntn) * T::BN;
   const int m0 = (blockIdx.x / ntn) * T::BM;
-  const int KT = K / kBK;
+  const int KT = K / T::BK;
   auto slot = [&](int kt) { return lds + (kt % kStages) * T::kStageBytes; };
 
   lf32x16 acc[MI][NI];
@@ -199,12 +201,12 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int row = wm * (32 * MI) + mi * 32 + r32;
-        af[mi] = *reinterpret_cast<const lbf16x8*>(sa + row * kRowBytes + swz(row, ch) * 16);
+        af[mi] = *reinterpret_cast<const lbf16x8*>(sa + row * T::kRowBytes + T::swz(row, ch) * 16);
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int row = wn * (32 * NI) + ni * 32 + r32;
-        bf[ni] = *reinterpret_cast<const lbf16x8*>(sb + row * kRowBytes + swz(row, ch) * 16);
+        bf[ni] = *reinterpret_cast<const lbf16x8*>(sb + row * T::kRowBytes + T::swz(row, ch) * 16);
       }
     };
     lbf16x8 af[2][MI], bf[2][NI];
@@ -213,15 +215,15 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
     // MFMAs takes precedence over the other's fragment reads and copies.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (ks + 1 < kBK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+    for (int ks = 0; ks < T::BK / 16; ++ks) {
+      if (ks + 1 < T::BK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bf[ks & 1][ni], acc[mi][ni], 0, 0, 0);
       if constexpr (MI * NI >= MI + NI) {
-        if (ks + 1 < kBK / 16) {
+        if (ks + 1 < T::BK / 16) {
           // One LDS read after each of the first MFMAs of this step.
 #pragma unroll
           for (int i = 0; i < MI + NI; ++i) {
@@ -281,11 +283,15 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
 }
 
 // The big tile when it gives at least one workgroup per compute unit, else the
-// small one (same bits either way).
+// small one; K steps of 128 when K allows and the small tiles fit one round of
+// the compute units (its 128 KiB ring leaves room for one workgroup per unit),
+// else K steps of 32.  Same bits every way.
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const int64_t big = (int64_t)(N / BigTile::BN) * ((M + BigTile::BM - 1) / BigTile::BM);
   if (big >= kComputeUnits) return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
+  const int64_t small = (int64_t)(N / SmallTile::BN) * ((M + SmallTile::BM - 1) / SmallTile::BM);
+  if (K % SmallTileK128::BK == 0 && small <= kComputeUnits) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
   return launch_gemm_t<SmallTile>(a, wt, c, M, N, K, st);
 }
 

@@ -73,16 +73,18 @@ def test_gemm_matches_oracle(M, N, K):
     assert ok, f"max abs err {err}, worst err/bound {ratio}"
 
 
-@pytest.mark.parametrize("N,K,Ms", [(256, 1024, (300, 1000)), (6144, 4096, (300, 4096))])
+@pytest.mark.parametrize("N,K,Ms", [(256, 1024, (300, 1000)), (6144, 4096, (300, 4096)), (4096, 14336, (4096,)),
+                                    (256, 160, (5, 700))])
 def test_gemm_row_alone_equals_row_in_batch(N, K, Ms):
     # Rows at every position class of a tile (first, last, both halves of a 32-row MFMA block, a
     # ragged last tile), computed alone and inside larger batches.  A lone row runs on the small
-    # 64 x 64 tile; the 4096-row call at N = 6144 runs on the 256 x 256 tile.
+    # 64 x 64 tile (K steps of 128 when K allows, else 32); the 4096-row calls at N = 6144 and
+    # N = 4096 run on the 256 x 256 tile.
     w = li.gemm_weight(4, N, K).to(DEV)
     for M in Ms:
         a = li.activations(4, 0, M, K)
         full = _gemm(a.to(DEV), w)
-        for r in sorted({0, 1, 3, 4, 7, 8, 31, 32, 127, 128, 255, 256, 257, M - 1}):
+        for r in sorted(r for r in {0, 1, 3, 4, 7, 8, 31, 32, 127, 128, 255, 256, 257, M - 1} if r < M):
             one = _gemm(li.activations(4, r, r + 1, K).to(DEV), w)
             assert np.array_equal(_bits(one), _bits(full[r:r + 1])), (M, r)
 
