@@ -21,6 +21,7 @@ reference, and the fp64 CPU oracle timed on a bounded sample of the same workloa
     python bench.py --suite             also the long-context, mixed and shared-prefix workloads
     python bench.py --summarize-profile TRACE_DIR PMC_DIR   write the profile summary under profiles/
     python bench.py --summarize-spread-profile TRACE_DIR    the batch-1 spread-kernel trace summary
+    python bench.py --summarize-layer-profile TRACE_DIR LAYER_JSON   the layer-operator trace summary
 
 The roofline's `traffic` (HBM bytes per launch of the decode split kernel) comes from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters, each scaled by what the same counter reads for a plain 1 GiB
@@ -34,6 +35,7 @@ import csv
 import glob
 import hashlib
 import json
+import re
 import math
 import os
 import subprocess
@@ -268,6 +270,76 @@ def summarize_spread_profile(trace_dir):
 PREFILL_KERNEL = "prefill_kernel<128, false>"
 PREFILL_SQ = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
               "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES"]
+
+
+LAYER_SHAPES = [("qkv_proj", 8192, 6144, 4096), ("down_proj", 8192, 4096, 14336), ("qkv_proj", 256, 6144, 4096),
+                ("down_proj", 256, 4096, 14336)]
+
+
+def summarize_layer_profile(trace_dir, layer_json):
+    """Writes the layer-operator profile summary: per-shape median kernel time from a kernel trace of
+    `bench.py --layer-only`, beside the vendor library's rate from that run's own JSON line."""
+    trace = _csv_rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    with open(layer_json) as f:
+        lo = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])["layer_ops"]
+
+    def wgs(r):
+        return int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+
+    def tile_of(name):
+        m = re.search(r"TileILi(\d+)ELi(\d+)ELi\d+ELi\d+ELi(\d+)E", name) or re.search(
+            r"Tile<(\d+), (\d+), \d+, \d+, (\d+)>", name)
+        return f"{m.group(1)}x{m.group(2)}, K step {m.group(3)}" if m else name
+
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o layer -- "
+           "python3 bench.py --layer-only --steps 10 --warmup 10")
+    lines = [
+        "# gemm_kernel / rmsnorm_kernel -- Llama-3-8B / Qwen3-8B layer shapes (batch-invariant layer operators)",
+        "",
+        "C = A W^T with bf16 A [M][K] and W [N][K], fp32 accumulation, bf16 C; one MFMA chain over k per output. "
+        "The 256 x 256 tile runs when it gives at least one workgroup per compute unit, else the 64 x 64 tile, "
+        "with K steps of 128 when K allows and its tiles fit one round of the compute units (same bits every "
+        "way).  RMSNorm: 8192 rows of 4096.",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace)",
+        "",
+        f"    {cmd}",
+        "",
+        "Median over the dispatches of each shape (warmup included; the median is past the clock ramp).",
+        "",
+        "| kernel | shape | workgroups | dispatches | median ns | TFLOP/s (median) | fraction of 2.5 PFLOP/s |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    vendor = []
+    for name, M, N, K in LAYER_SHAPES:
+        big = (N // 256) * ((M + 255) // 256)
+        ngroups = big if big >= 256 else (N // 64) * ((M + 63) // 64)
+        rows = [r for r in trace if "gemm_kernel" in r["Kernel_Name"] and wgs(r) == ngroups]
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+        med = float(np.median(d))
+        tf = 2.0 * M * N * K / med / 1e3
+        lines.append(f"| gemm_kernel<{tile_of(rows[0]['Kernel_Name'])}> | {name} M={M} (N={N}, K={K}) | {ngroups} | "
+                     f"{len(d)} | {med:.0f} | {tf:.1f} | {tf / BF16_PEAK_TFLOPS:.4f} |")
+        vendor.append(f"{lo['gemm'][f'{name}_M{M}']['torch_tflops'] / 1e3:.2f} PFLOP/s ({name} M={M})")
+    rn = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if "rmsnorm_kernel" in r["Kernel_Name"]]
+    med = float(np.median(rn))
+    gbs = 2 * 8192 * 4096 * 2 / med
+    lines += [
+        "",
+        "| kernel | shape | dispatches | median ns | GB/s (read x + write y) | fraction of 8 TB/s |",
+        "|---|---|---|---|---|---|",
+        f"| rmsnorm_kernel | 8192 x 4096 | {len(rn)} | {med:.0f} | {gbs:.1f} | {gbs / HBM_PEAK_GBS:.4f} |",
+        "",
+        "The vendor library (torch.matmul on hipBLASLt) on the same shapes, timed by `bench.py --layer-only` in "
+        "the same traced run: " + ", ".join(vendor) + f".  Row 0 computed alone equals row 0 inside the "
+        f"8192-row batch: ours {lo['row0_alone_equals_in_batch']['ours']}, the vendor library's "
+        f"{lo['row0_alone_equals_in_batch']['torch']}.",
+        "",
+    ]
+    out = os.path.join(ROOT, "profiles", "gemm_rmsnorm_llama3-8b-layer.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
 
 
 PREFILL_PROFILE_STEPS = 10
@@ -840,6 +912,7 @@ def main():
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-spread-profile", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-layer-profile", nargs=2, metavar=("TRACE_DIR", "LAYER_JSON"))
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile)
@@ -849,6 +922,9 @@ def main():
         return
     if args.summarize_spread_profile:
         summarize_spread_profile(args.summarize_spread_profile)
+        return
+    if args.summarize_layer_profile:
+        summarize_layer_profile(*args.summarize_layer_profile)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; there is no multi-GPU path (run with --gpus 1)",
