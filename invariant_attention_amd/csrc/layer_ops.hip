@@ -90,15 +90,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const __bf16* __r
 
 constexpr int kComputeUnits = 256;              // MI355X
 constexpr int kBK = 32;                          // K granularity of every tile (and the big tile's K step)
-constexpr int kStages = 4;                       // LDS ring slots
 
 // A workgroup tile of BM x BN outputs over WM x WN waves, K steps of BK; each
 // wave owns a (BM / WM) x (BN / WN) block as 32 x 32 MFMA tiles.  Every
 // configuration computes each output with the same MFMA chain over k in
 // ascending 16-wide steps, so neither the tile nor its K step changes a bit.
-template <int BM_, int BN_, int WM_, int WN_, int BK_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_ = 4>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int kStages = STAGES_;  // LDS ring slots: 4, or 2
   static constexpr int kWaves = WM * WN;
   static constexpr int kMI = BM / WM / 32, kNI = BN / WN / 32;
   static constexpr int kChunks = BK / 8;                 // 16-byte chunks (8 k) per tile row
@@ -110,6 +110,7 @@ struct Tile {
   static constexpr int kBLoads = BN / kRowsPerCopy / kWaves;
   static constexpr int kLoadsPerStage = kALoads + kBLoads;
   static_assert(BK % kBK == 0 && kChunks <= 16, "K step");
+  static_assert(kStages == 4 || kStages == 2, "ring slots");
   static_assert(kMI >= 1 && kNI >= 1 && kALoads >= 1 && kBLoads >= 1, "tile must divide over the waves");
   static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BN % (kRowsPerCopy * kWaves) == 0, "copies per wave");
   // A tile row holds its chunks at positions c ^ ((row / (16 / kChunks)) %
@@ -118,6 +119,7 @@ struct Tile {
   static __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row / (16 / kChunks)) & (kChunks - 1)); }
 };
 using BigTile = Tile<256, 256, 2, 4, 32>;     // 8 waves of 128 x 64
+using BigTileK64 = Tile<256, 256, 2, 4, 64, 2>;  // the same, K steps of 64 in a 2-slot ring (K % 64 == 0)
 using SmallTile = Tile<64, 64, 2, 2, 32>;     // 4 waves of 32 x 32, for calls with few big tiles
 using SmallTileK128 = Tile<64, 64, 2, 2, 128>;  // the same with 4x the work between barriers
 
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
   const int n0 = (blockIdx.x % ntn) * T::BN;
   const int m0 = (blockIdx.x / ntn) * T::BM;
   const int KT = K / T::BK;
-  auto slot = [&](int kt) { return lds + (kt % kStages) * T::kStageBytes; };
+  auto slot = [&](int kt) { return lds + (kt % T::kStages) * T::kStageBytes; };
 
   lf32x16 acc[MI][NI];
 #pragma unroll
@@ -180,18 +182,24 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = lf32x16{};
 
-  for (int s = 0; s < kStages - 1; ++s)
+  for (int s = 0; s < T::kStages - 1; ++s)
     if (s < KT) gemm_issue<T>(slot(s), a, wt, M, K, m0, n0, s, w, lane);
   const int r32 = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    // Copies in flight after this step's: those of steps kt+1 and kt+2.
-    if (kt + 2 < KT)
-      stage_barrier<2 * L>();
-    else if (kt + 1 < KT)
-      stage_barrier<L>();
-    else
+    // Copies in flight after this step's: those of steps kt+1 and kt+2 (4
+    // slots), or none (2 slots).
+    if constexpr (T::kStages == 4) {
+      if (kt + 2 < KT)
+        stage_barrier<2 * L>();
+      else if (kt + 1 < KT)
+        stage_barrier<L>();
+      else
+        stage_barrier<0>();
+    } else {
       stage_barrier<0>();
-    if (kt + 3 < KT) gemm_issue<T>(slot(kt + 3), a, wt, M, K, m0, n0, kt + 3, w, lane);
+    }
+    if (kt + T::kStages - 1 < KT)
+      gemm_issue<T>(slot(kt + T::kStages - 1), a, wt, M, K, m0, n0, kt + T::kStages - 1, w, lane);
     const uint8_t* sa = slot(kt);
     const uint8_t* sb = sa + T::kATileBytes;
     // Operand fragments of the lane's 8 k of each 16-k step; the reads of
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
 
 template <class T>
 hipError_t launch_gemm_t(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
-  const int lds = kStages * T::kStageBytes;
+  const int lds = T::kStages * T::kStageBytes;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<T>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
@@ -282,14 +290,19 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
   return hipGetLastError();
 }
 
-// The big tile when it gives at least one workgroup per compute unit, else the
-// small one; K steps of 128 when K allows and the small tiles fit one round of
-// the compute units (its 128 KiB ring leaves room for one workgroup per unit),
-// else K steps of 32.  Same bits every way.
+// The big tile when it gives at least one workgroup per compute unit (K steps
+// of 64 in two slots when K allows: half the barriers of 32-wide steps in four
+// slots, in the same 128 KiB), else the small one; K steps of 128 when K
+// allows and the small tiles fit one round of the compute units (its 128 KiB
+// ring leaves room for one workgroup per unit), else K steps of 32.  Same bits
+// every way.
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const int64_t big = (int64_t)(N / BigTile::BN) * ((M + BigTile::BM - 1) / BigTile::BM);
-  if (big >= kComputeUnits) return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
+  if (big >= kComputeUnits) {
+    if (K % BigTileK64::BK == 0) return launch_gemm_t<BigTileK64>(a, wt, c, M, N, K, st);
+    return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
+  }
   const int64_t small = (int64_t)(N / SmallTile::BN) * ((M + SmallTile::BM - 1) / SmallTile::BM);
   if (K % SmallTileK128::BK == 0 && small <= kComputeUnits) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
   return launch_gemm_t<SmallTile>(a, wt, c, M, N, K, st);

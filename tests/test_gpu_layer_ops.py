@@ -62,7 +62,7 @@ def test_rmsnorm_row_alone_equals_row_in_batch():
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 32), (3, 256, 64), (7, 256, 128), (300, 512, 4096),
                                    (257, 1024, 1024), (256, 256, 14336), (513, 6144, 4096),
-                                   (3000, 6144, 256)])
+                                   (3000, 6144, 256), (4096, 4096, 1056)])
 def test_gemm_matches_oracle(M, N, K):
     a = li.activations(3, 0, M, K)
     w = li.gemm_weight(3, N, K)
@@ -74,12 +74,12 @@ def test_gemm_matches_oracle(M, N, K):
 
 
 @pytest.mark.parametrize("N,K,Ms", [(256, 1024, (300, 1000)), (6144, 4096, (300, 4096)), (4096, 14336, (4096,)),
-                                    (256, 160, (5, 700))])
+                                    (256, 160, (5, 700)), (4096, 1056, (4096,))])
 def test_gemm_row_alone_equals_row_in_batch(N, K, Ms):
     # Rows at every position class of a tile (first, last, both halves of a 32-row MFMA block, a
     # ragged last tile), computed alone and inside larger batches.  A lone row runs on the small
     # 64 x 64 tile (K steps of 128 when K allows, else 32); the 4096-row calls at N = 6144 and
-    # N = 4096 run on the 256 x 256 tile.
+    # N = 4096 run on the 256 x 256 tile (K steps of 64, or 32 at K = 1056).
     w = li.gemm_weight(4, N, K).to(DEV)
     for M in Ms:
         a = li.activations(4, 0, M, K)
