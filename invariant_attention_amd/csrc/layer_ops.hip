@@ -122,6 +122,7 @@ using BigTile = Tile<256, 256, 2, 4, 32>;     // 8 waves of 128 x 64
 using BigTileK64 = Tile<256, 256, 2, 4, 64, 2>;  // the same, K steps of 64 in a 2-slot ring (K % 64 == 0)
 using SmallTile = Tile<64, 64, 2, 2, 32>;     // 4 waves of 32 x 32, for calls with few big tiles
 using SmallTileK128 = Tile<64, 64, 2, 2, 128>;  // the same with 4x the work between barriers
+using SmallTileK128x2 = Tile<64, 64, 2, 2, 128, 2>;  // and in a 2-slot ring: 2 workgroups per compute unit
 
 // Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
 // Copy i of wave w fills the kRowsPerCopy tile rows from kRowsPerCopy (i *
@@ -292,10 +293,10 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
 
 // The big tile when it gives at least one workgroup per compute unit (K steps
 // of 64 in two slots when K allows: half the barriers of 32-wide steps in four
-// slots, in the same 128 KiB), else the small one; K steps of 128 when K
-// allows and the small tiles fit one round of the compute units (its 128 KiB
-// ring leaves room for one workgroup per unit), else K steps of 32.  Same bits
-// every way.
+// slots, in the same 128 KiB), else the small one with K steps of 128 when K
+// allows (else 32): in 4 slots (128 KiB, one workgroup per compute unit) when
+// its tiles fit one round of the compute units, else in 2 slots (64 KiB, two
+// workgroups per unit).  Same bits every way.
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const int64_t big = (int64_t)(N / BigTile::BN) * ((M + BigTile::BM - 1) / BigTile::BM);
@@ -304,7 +305,10 @@ hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int 
     return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
   }
   const int64_t small = (int64_t)(N / SmallTile::BN) * ((M + SmallTile::BM - 1) / SmallTile::BM);
-  if (K % SmallTileK128::BK == 0 && small <= kComputeUnits) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
+  if (K % SmallTileK128::BK == 0) {
+    if (small <= kComputeUnits) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
+    return launch_gemm_t<SmallTileK128x2>(a, wt, c, M, N, K, st);
+  }
   return launch_gemm_t<SmallTile>(a, wt, c, M, N, K, st);
 }
 
