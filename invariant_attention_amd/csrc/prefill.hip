@@ -413,6 +413,9 @@ __global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_ke
       f32x4 sc[4];
       bf16x8 kf[2][D / 32];
       lds_k_block<D>(tile, 0, r, g, kf[0]);
+      // A wave issuing its score or value MFMAs takes precedence over the
+      // other wave of its SIMD (another workgroup's), whose softmax then
+      // fills the issue slots between the MFMAs.
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
