@@ -287,9 +287,9 @@ def summarize_layer_profile(trace_dir, layer_json):
         return int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
 
     def tile_of(name):
-        m = re.search(r"TileILi(\d+)ELi(\d+)ELi\d+ELi\d+ELi(\d+)E(?:Li(\d+)E)?", name) or re.search(
-            r"Tile<(\d+), (\d+), \d+, \d+, (\d+)(?:, (\d+))?>", name)
-        return f"{m.group(1)}x{m.group(2)}, K step {m.group(3)}, {m.group(4) or 4} slots" if m else name
+        m = re.search(r"TileILi(\d+)ELi(\d+)ELi\d+ELi\d+ELi(\d+)E", name) or re.search(
+            r"Tile<(\d+), (\d+), \d+, \d+, (\d+)>", name)
+        return f"{m.group(1)}x{m.group(2)}, K step {m.group(3)}, 2 slots" if m else name
 
     cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o layer -- "
            "python3 bench.py --layer-only --steps 10 --warmup 10")

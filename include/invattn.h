@@ -156,8 +156,9 @@ const char* ia_version(void);
  * the score slots runs the split kernel (the same bits). */
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
-/* Device workspace for ia_paged_attn_prefill (0: prefill folds its split
- * partials in registers). */
+/* Device workspace for ia_paged_attn_prefill.  Returns 0: prefill folds each
+ * row's split partials in registers and needs no workspace, so its
+ * workspace / ws_bytes arguments are accepted and ignored (NULL / 0 is fine). */
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len);
 
 /*
@@ -184,9 +185,15 @@ ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, 
  * (its own K/V already appended).  Keys are cut into splits at absolute
  * multiples of split_tokens; each split is walked in 64-key tiles in
  * ascending order with the online-softmax update of Vosti App. A.2 (fp32
- * state m, z, U; weights rounded to bf16 before the PV product, z summing the
- * unrounded weights); the split states are then folded in ascending split
- * order and the row is finalised as O = bf16(U * select(z > 0, 1/z, 0)).
+ * state m, z, U; z sums the fp32 weights).  One deliberate departure from
+ * App. A.2, which casts the weights once to the cache type before the PV
+ * product: each fp32 weight w enters the PV product as two bf16 numbers,
+ * hi = bf16(w) and lo = bf16(w - hi), in two MFMAs (hi first), so a weight
+ * carries about 16 significant bits instead of 8 (a single cast misses the
+ * 2e-3 + 1e-2 |ref| tolerance on rows over a few keys whose values cancel).
+ * Every kernel does the same, so invariance is unaffected.  The split states
+ * are then folded in ascending split order and the row is finalised as
+ * O = bf16(U * select(z > 0, 1/z, 0)).
  *   q            dev [B][Hq][d] bf16
  *   block_table  dev [B][bt_stride] int32
  *   seq_lens     dev [B] int32, n_b >= 1 keys including the current token
@@ -216,6 +223,7 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
  *   max_q_len    host upper bound of q lengths (grid only)
  *   max_seq_len  host upper bound of seq_lens (grid only)
  *   out          dev [total_q][Hq][d] bf16
+ *   workspace    ignored (ia_prefill_workspace_bytes returns 0)
  */
 ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
                                 const int32_t* seq_lens, const void* k_cache, const void* v_cache,
@@ -246,10 +254,17 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
 ia_status ia_rmsnorm(const void* x, const void* weight, int32_t M, int32_t H, float eps, void* out, void* stream);
 
 /*
- * C = A W^T: c[m][n] = bf16(sum_k a[m][k] w[n][k]), fp32 accumulation.  One
- * tile shape for every call (256 x 256 outputs, 32-wide K steps) and no
- * split-K: each output is one accumulation over k in ascending order, so a
- * row of C depends on its row of A and on W only, never on M.
+ * C = A W^T: c[m][n] = bf16(sum_k a[m][k] w[n][k]), fp32 accumulation, no
+ * split-K.  Every output is one MFMA accumulator chain over k in ascending
+ * 16-wide steps (v_mfma_f32_32x32x16_bf16), whatever tile computes it, so a
+ * row of C depends on its row of A and on W only, never on M.  Two tiles
+ * (chosen from M, N and K only to fill the chip; the same bits either way):
+ *  - 256 x 256 outputs, 8 waves, when it gives at least one workgroup per
+ *    compute unit: K steps of 64 in a 2-slot LDS ring when K % 64 == 0, else
+ *    32 in a 4-slot ring;
+ *  - 64 x 64 outputs, 4 waves, otherwise: K steps of 128 when K % 128 == 0
+ *    (4 slots when its tiles fit one round of the compute units, else 2),
+ *    else 32 in 4 slots.
  *   a  dev [M][K] bf16 (row-major activations, one row per token)
  *   w  dev [N][K] bf16 (a linear layer's weight, one row per output feature)
  *   c  dev [M][N] bf16
@@ -318,6 +333,36 @@ ia_status ia_pool_evict(ia_pool* pool, int32_t want, int32_t* evicted);
 int32_t ia_pool_page_refs(const ia_pool* pool, int32_t page);
 int32_t ia_pool_page_published(const ia_pool* pool, int32_t page);
 int32_t ia_pool_num_free(const ia_pool* pool);
+
+/* ------------------------------------------------------------------------
+ * Opt-in host validators of the device-resident preconditions that the
+ * launches leave unchecked (Vosti §4.3 "Sharing and write isolation": new
+ * K/V go only to private, pairwise disjoint slots and shared pages are never
+ * written; App. A.1: every key of a row is read through its block-table
+ * entry).  The caller copies the arrays to host memory first; nothing here
+ * touches the GPU, so a deployment runs them when it wants the guarantee,
+ * off the hot path.  The first violation found is reported through
+ * ia_last_error().
+ * ------------------------------------------------------------------------ */
+
+/* kv_append slots (host [T] int64; negative entries are padding and skipped).
+ * Taken in slot order, the first slot at or past num_pages * page_size gives
+ * IA_ERR_INVALID_ARG, and, with a pool (may be NULL), the first slot on a
+ * published page gives IA_ERR_PAGE_REFERENCED (published pages are shared
+ * and immutable); failing both, a slot listed twice gives IA_ERR_INVALID_ARG.
+ * The pool must have num_pages pages of page_size tokens. */
+ia_status ia_validate_slots(const ia_pool* pool, const int64_t* slot_mapping, int32_t T, int32_t num_pages,
+                            int32_t page_size);
+
+/* Attention launch arguments (all host arrays): cu_q_lens [B+1] with
+ * cu_q_lens[0] = 0 and cu_q_lens[B] = total_q (NULL for decode, where each
+ * q_len is 1); for every sequence 1 <= q_len <= seq_lens[b] <= max_seq_len,
+ * its ceil(seq_len / page_size) pages fit a block-table row of bt_stride
+ * entries, and each of those entries names a page in [0, num_pages).
+ * IA_OK, or IA_ERR_INVALID_ARG with the first violation. */
+ia_status ia_validate_attention_args(const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t B, int32_t total_q,
+                                     const int32_t* block_table, int32_t bt_stride, int32_t num_pages,
+                                     int32_t page_size, int32_t max_seq_len);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,8 @@ EXPORTS = [
     "ia_prefill_workspace_bytes", "ia_kv_append", "ia_paged_attn_decode", "ia_paged_attn_prefill",
     "ia_pool_create", "ia_pool_destroy", "ia_seq_begin", "ia_seq_append_tokens", "ia_seq_reserve",
     "ia_seq_commit", "ia_seq_block_table", "ia_seq_len", "ia_seq_end", "ia_pool_evict", "ia_pool_page_refs",
-    "ia_pool_page_published", "ia_pool_num_free", "ia_rmsnorm", "ia_gemm_bf16",
+    "ia_pool_page_published", "ia_pool_num_free", "ia_rmsnorm", "ia_gemm_bf16", "ia_validate_slots",
+    "ia_validate_attention_args",
 ]
 
 
@@ -94,6 +95,8 @@ def load() -> ctypes.CDLL:
         "ia_pool_num_free": ([vp], i32),
         "ia_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp, vp], ctypes.c_int),
         "ia_gemm_bf16": ([vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
+        "ia_validate_slots": ([vp, vp, i32, i32, i32], ctypes.c_int),
+        "ia_validate_attention_args": ([vp, vp, i32, i32, vp, i32, i32, i32, i32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -290,3 +293,33 @@ def ia_pool_page_published(pool: Pool, page: int) -> int:
 
 def ia_pool_num_free(pool: Pool) -> int:
     return int(load().ia_pool_num_free(pool.handle))
+
+
+# ------------------------------------------------------------ host validators
+
+def _host_array(x, dtype):
+    import numpy as np
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=dtype))
+
+
+def ia_validate_slots(pool, slot_mapping, num_pages: int, page_size: int) -> None:
+    """Host check of a kv_append slot mapping (raises IAError with the first violation)."""
+    import numpy as np
+    sl = _host_array(slot_mapping, np.int64)
+    _check(load().ia_validate_slots(pool.handle if pool is not None else None, _p(sl), int(sl.shape[0]),
+                                    int(num_pages), int(page_size)))
+
+
+def ia_validate_attention_args(cu_q_lens, seq_lens, block_table, num_pages: int, page_size: int,
+                               max_seq_len: int, total_q: int | None = None) -> None:
+    """Host check of an attention call's lengths and block table; cu_q_lens None for decode."""
+    import numpy as np
+    sl = _host_array(seq_lens, np.int32)
+    bt = _host_array(block_table, np.int32)
+    cu = None if cu_q_lens is None else _host_array(cu_q_lens, np.int32)
+    B = int(sl.shape[0])
+    tq = (int(cu[-1]) if cu is not None else B) if total_q is None else int(total_q)
+    _check(load().ia_validate_attention_args(_p(cu), _p(sl), B, tq, _p(bt), int(bt.shape[1]) if bt.ndim == 2 else 0,
+                                             int(num_pages), int(page_size), int(max_seq_len)))

@@ -3,9 +3,9 @@
 // Every value-relevant operation of a query row lives here, so decode, prefill
 // and the split merge apply the same operations in the same order (Vosti:
 // Specifying, Implementing, and Verifying Deterministic LLM Inference, App. A.2:
-// "operations retain fixed floating-point types, parameters, and value-relevant
-// order").  The library is compiled with -ffp-contract=off: no product is fused
-// into an add unless written as such here.
+// each operation keeps its floating-point type, its operands and its place in
+// the order of evaluation).  The library is compiled with -ffp-contract=off: no
+// product is fused into an add unless written as such here.
 //
 // Wave geometry (gfx950, wave64).  A wave owns one block of 16 query rows and
 // walks 64-key tiles.  Both contractions run on v_mfma_f32_16x16x32_bf16 with

@@ -11,13 +11,21 @@
 // r = 1 / sqrt(mean + eps) and y = bf16((x * r) * w).  A row's operations
 // depend on nothing but the row.
 //
-// GEMM.  C[M][N] = A[M][K] W[N][K]^T, bf16 in, fp32 accumulation, bf16 out.
-// One tile shape for every call: 256 x 256 outputs per workgroup, 32-wide
-// K steps, 8 waves of 128 x 64 (two per SIMD), v_mfma_f32_32x32x16_bf16.  Every output element is one MFMA accumulator chain
-// over k = 0, 16, 32, ... in order, so its bits depend on its row of A and
-// its row of W only -- not on M, on the row's place in a tile, or on the
-// other rows.  A/W tiles go from memory straight into a 4-slot LDS ring
-// (global_load_lds), three K steps ahead.
+// GEMM.  C[M][N] = A[M][K] W[N][K]^T, bf16 in, fp32 accumulation, bf16 out,
+// on v_mfma_f32_32x32x16_bf16.  Every output element is one MFMA accumulator
+// chain over k = 0, 16, 32, ... in order, so its bits depend on its row of A
+// and its row of W only -- not on M, on the tile that computes it, on the
+// row's place in that tile, or on the other rows.  Two tiles, chosen from M,
+// N and K only to fill the chip (the same bits either way):
+//  - 256 x 256 outputs, 8 waves of 128 x 64 (two per SIMD), when it gives at
+//    least one workgroup per compute unit; K steps of 64 in a 2-slot LDS ring
+//    when K % 64 == 0, else 32 in a 4-slot ring;
+//  - 64 x 64 outputs, 4 waves of 32 x 32, otherwise; K steps of 128 when
+//    K % 128 == 0 (a 4-slot ring when its tiles fit one round of the compute
+//    units, else 2 slots), else 32 in 4 slots.
+// A/W tiles go from memory straight into the LDS ring (global_load_lds),
+// slots - 1 K steps ahead; each stage is waited for with vmcnt(0) before the
+// barrier that publishes it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,10 +103,10 @@ constexpr int kBK = 32;                          // K granularity of every tile 
 // wave owns a (BM / WM) x (BN / WN) block as 32 x 32 MFMA tiles.  Every
 // configuration computes each output with the same MFMA chain over k in
 // ascending 16-wide steps, so neither the tile nor its K step changes a bit.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_ = 4>
+template <int BM_, int BN_, int WM_, int WN_, int BK_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
-  static constexpr int kStages = STAGES_;  // LDS ring slots: 4, or 2
+  static constexpr int kStages = 2;  // LDS ring slots
   static constexpr int kWaves = WM * WN;
   static constexpr int kMI = BM / WM / 32, kNI = BN / WN / 32;
   static constexpr int kChunks = BK / 8;                 // 16-byte chunks (8 k) per tile row
@@ -110,7 +118,6 @@ struct Tile {
   static constexpr int kBLoads = BN / kRowsPerCopy / kWaves;
   static constexpr int kLoadsPerStage = kALoads + kBLoads;
   static_assert(BK % kBK == 0 && kChunks <= 16, "K step");
-  static_assert(kStages == 4 || kStages == 2, "ring slots");
   static_assert(kMI >= 1 && kNI >= 1 && kALoads >= 1 && kBLoads >= 1, "tile must divide over the waves");
   static_assert(BM % (kRowsPerCopy * kWaves) == 0 && BN % (kRowsPerCopy * kWaves) == 0, "copies per wave");
   // A tile row holds its chunks at positions c ^ ((row / (16 / kChunks)) %
@@ -118,11 +125,10 @@ struct Tile {
   // distinct 16-byte bank groups (256 bytes span the 64 banks).
   static __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row / (16 / kChunks)) & (kChunks - 1)); }
 };
-using BigTile = Tile<256, 256, 2, 4, 32>;     // 8 waves of 128 x 64
-using BigTileK64 = Tile<256, 256, 2, 4, 64, 2>;  // the same, K steps of 64 in a 2-slot ring (K % 64 == 0)
-using SmallTile = Tile<64, 64, 2, 2, 32>;     // 4 waves of 32 x 32, for calls with few big tiles
+using BigTile = Tile<256, 256, 2, 4, 32>;       // 8 waves of 128 x 64
+using BigTileK64 = Tile<256, 256, 2, 4, 64>;    // the same, K steps of 64 (K % 64 == 0)
+using SmallTile = Tile<64, 64, 2, 2, 32>;       // 4 waves of 32 x 32, for calls with few big tiles
 using SmallTileK128 = Tile<64, 64, 2, 2, 128>;  // the same with 4x the work between barriers
-using SmallTileK128x2 = Tile<64, 64, 2, 2, 128, 2>;  // and in a 2-slot ring: 2 workgroups per compute unit
 
 // Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
 // Copy i of wave w fills the kRowsPerCopy tile rows from kRowsPerCopy (i *
@@ -152,20 +158,20 @@ __device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const
   }
 }
 
-// Waits until this wave's copies of the step to be consumed have landed (N
-// copies of later steps may stay in flight), then meets the other waves.  The
-// copies write LDS behind the compiler's back, so the wait is explicit.
-template <int N>
+// Waits until every copy this wave has issued has landed in LDS, then meets
+// the other waves: after it, the slot about to be read is complete.  The wait
+// is explicit (the copies write LDS behind the compiler's back) and counts
+// down to zero: waiting for only the older copies would assume that the
+// copies land in the order they were issued.
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <class T>
 __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __restrict__ a,
                                                                const __bf16* __restrict__ wt,
                                                                __bf16* __restrict__ c, int M, int N, int K) {
-  constexpr int MI = T::kMI, NI = T::kNI, L = T::kLoadsPerStage;
+  constexpr int MI = T::kMI, NI = T::kNI;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,18 +193,9 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
     if (s < KT) gemm_issue<T>(slot(s), a, wt, M, K, m0, n0, s, w, lane);
   const int r32 = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    // Copies in flight after this step's: those of steps kt+1 and kt+2 (4
-    // slots), or none (2 slots).
-    if constexpr (T::kStages == 4) {
-      if (kt + 2 < KT)
-        stage_barrier<2 * L>();
-      else if (kt + 1 < KT)
-        stage_barrier<L>();
-      else
-        stage_barrier<0>();
-    } else {
-      stage_barrier<0>();
-    }
+    // Step kt's copies have landed; those of step kt + 1 are issued next,
+    // into the slot every wave has finished reading.
+    stage_barrier();
     if (kt + T::kStages - 1 < KT)
       gemm_issue<T>(slot(kt + T::kStages - 1), a, wt, M, K, m0, n0, kt + T::kStages - 1, w, lane);
     const uint8_t* sa = slot(kt);
@@ -292,11 +289,8 @@ hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, in
 }
 
 // The big tile when it gives at least one workgroup per compute unit (K steps
-// of 64 in two slots when K allows: half the barriers of 32-wide steps in four
-// slots, in the same 128 KiB), else the small one with K steps of 128 when K
-// allows (else 32): in 4 slots (128 KiB, one workgroup per compute unit) when
-// its tiles fit one round of the compute units, else in 2 slots (64 KiB, two
-// workgroups per unit).  Same bits every way.
+// of 64 when K allows: half the barriers of 32-wide steps), else the small one
+// with K steps of 128 when K allows (else 32).  Same bits every way.
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const int64_t big = (int64_t)(N / BigTile::BN) * ((M + BigTile::BM - 1) / BigTile::BM);
@@ -304,11 +298,7 @@ hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int 
     if (K % BigTileK64::BK == 0) return launch_gemm_t<BigTileK64>(a, wt, c, M, N, K, st);
     return launch_gemm_t<BigTile>(a, wt, c, M, N, K, st);
   }
-  const int64_t small = (int64_t)(N / SmallTile::BN) * ((M + SmallTile::BM - 1) / SmallTile::BM);
-  if (K % SmallTileK128::BK == 0) {
-    if (small <= kComputeUnits) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
-    return launch_gemm_t<SmallTileK128x2>(a, wt, c, M, N, K, st);
-  }
+  if (K % SmallTileK128::BK == 0) return launch_gemm_t<SmallTileK128>(a, wt, c, M, N, K, st);
   return launch_gemm_t<SmallTile>(a, wt, c, M, N, K, st);
 }
 

@@ -322,4 +322,67 @@ int32_t ia_pool_page_published(const ia_pool* pool, int32_t page) {
 
 int32_t ia_pool_num_free(const ia_pool* pool) { return pool ? (int32_t)pool->free_pages.size() : -1; }
 
+// ---------------------------------------------------------------------------
+// Opt-in host checks of the preconditions the launches leave unchecked (Vosti
+// §4.3 "Sharing and write isolation": new K/V go only to private, disjoint
+// slots; shared pages are never written).
+
+ia_status ia_validate_slots(const ia_pool* pool, const int64_t* slot_mapping, int32_t T, int32_t num_pages,
+                            int32_t page_size) {
+  if (T < 0 || num_pages <= 0 || page_size <= 0 || (T > 0 && !slot_mapping))
+    return fail(IA_ERR_INVALID_ARG, "bad argument");
+  if (pool && (pool->num_pages != num_pages || pool->P != page_size))
+    return fail(IA_ERR_INVALID_ARG, "pool has %d pages of %d tokens, the call names %d of %d", pool->num_pages,
+                pool->P, num_pages, page_size);
+  const int64_t limit = (int64_t)num_pages * page_size;
+  std::vector<int64_t> seen;
+  try {
+    seen.reserve((size_t)T);
+  } catch (...) {
+    return fail(IA_ERR_INTERNAL, "out of host memory");
+  }
+  for (int32_t i = 0; i < T; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;  // a padding row writes nothing
+    if (s >= limit) return fail(IA_ERR_INVALID_ARG, "slot_mapping[%d] = %lld is past the pool", i, (long long)s);
+    if (pool && pool->published[(size_t)(s / page_size)])
+      return fail(IA_ERR_PAGE_REFERENCED, "slot_mapping[%d] = %lld lands on published page %lld", i, (long long)s,
+                  (long long)(s / page_size));
+    seen.push_back(s);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t i = 1; i < seen.size(); ++i)
+    if (seen[i] == seen[i - 1]) return fail(IA_ERR_INVALID_ARG, "slot %lld is written twice", (long long)seen[i]);
+  return ok();
+}
+
+ia_status ia_validate_attention_args(const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t B, int32_t total_q,
+                                     const int32_t* block_table, int32_t bt_stride, int32_t num_pages,
+                                     int32_t page_size, int32_t max_seq_len) {
+  if (B < 0 || (B > 0 && (!seq_lens || !block_table)) || num_pages <= 0 || page_size <= 0 || bt_stride < 0)
+    return fail(IA_ERR_INVALID_ARG, "bad argument");
+  if (cu_q_lens) {
+    if (cu_q_lens[0] != 0) return fail(IA_ERR_INVALID_ARG, "cu_q_lens[0] = %d, not 0", cu_q_lens[0]);
+    if (cu_q_lens[B] != total_q)
+      return fail(IA_ERR_INVALID_ARG, "cu_q_lens[%d] = %d, not total_q = %d", B, cu_q_lens[B], total_q);
+  }
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t q_len = cu_q_lens ? (int64_t)cu_q_lens[b + 1] - cu_q_lens[b] : 1;
+    const int64_t n = seq_lens[b];
+    if (q_len < 1 || q_len > n || n > max_seq_len)
+      return fail(IA_ERR_INVALID_ARG, "sequence %d: need 1 <= q_len (%lld) <= seq_len (%lld) <= max_seq_len (%d)", b,
+                  (long long)q_len, (long long)n, max_seq_len);
+    const int64_t pages = (n + page_size - 1) / page_size;
+    if (pages > bt_stride)
+      return fail(IA_ERR_INVALID_ARG, "sequence %d: %lld pages do not fit a block-table row of %d", b,
+                  (long long)pages, bt_stride);
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t e = block_table[(size_t)b * bt_stride + j];
+      if (e < 0 || e >= num_pages)
+        return fail(IA_ERR_INVALID_ARG, "sequence %d: block_table entry %lld = %d is not a page", b, (long long)j, e);
+    }
+  }
+  return ok();
+}
+
 }  // extern "C"
