@@ -210,6 +210,31 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
                                void* stream);
 
 /*
+ * Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory or be handed a workspace: code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc.  Same arguments (minus
+ * the workspace), same kernels and the same output bits as
+ * ia_paged_attn_decode; the workspace is a fixed device array inside the
+ * library, one per GPU, of ia_decode_noalloc_scratch_bytes() bytes (32 MiB:
+ * enough for 256 sequences of up to 8192 keys at 32 query heads and head_dim
+ * 128), held from the library's load until the process ends.  A launch whose
+ * workspace would exceed it is rejected with IA_ERR_WORKSPACE_TOO_SMALL
+ * before anything is enqueued (under IA_DECODE_AUTO a launch that fits only
+ * without the spread kernels' slots runs the split kernel, the same bits).
+ * Nothing in the array needs to start at zero: every call writes what it
+ * later reads.  Calls on one GPU share its array, so calls that may overlap
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.
+ */
+ia_status ia_paged_attn_decode_noalloc(const ia_ctx* ctx, const void* q, const void* k_cache, const void* v_cache,
+                                       int32_t num_pages, const float* k_scale, const float* v_scale,
+                                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                       int32_t B, int32_t max_seq_len, void* out, void* stream);
+
+/* Bytes of the fixed workspace ia_paged_attn_decode_noalloc uses. */
+size_t ia_decode_noalloc_scratch_bytes(void);
+
+/*
  * Chunked / whole prefill (and mixed batches): packed ragged query rows,
  * causal, grouped-query.  Sequence b owns rows cu_q_lens[b] ..
  * cu_q_lens[b+1]-1; row i of it is position p = seq_lens[b] - q_len_b + i and

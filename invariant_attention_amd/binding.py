@@ -38,7 +38,7 @@ EXPORTS = [
     "ia_pool_create", "ia_pool_destroy", "ia_seq_begin", "ia_seq_append_tokens", "ia_seq_reserve",
     "ia_seq_commit", "ia_seq_block_table", "ia_seq_len", "ia_seq_end", "ia_pool_evict", "ia_pool_page_refs",
     "ia_pool_page_published", "ia_pool_num_free", "ia_rmsnorm", "ia_gemm_bf16", "ia_validate_slots",
-    "ia_validate_attention_args",
+    "ia_validate_attention_args", "ia_paged_attn_decode_noalloc", "ia_decode_noalloc_scratch_bytes",
 ]
 
 
@@ -97,6 +97,9 @@ def load() -> ctypes.CDLL:
         "ia_gemm_bf16": ([vp, vp, i32, i32, i32, vp, vp], ctypes.c_int),
         "ia_validate_slots": ([vp, vp, i32, i32, i32], ctypes.c_int),
         "ia_validate_attention_args": ([vp, vp, i32, i32, vp, i32, i32, i32, i32], ctypes.c_int),
+        "ia_paged_attn_decode_noalloc": ([vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, vp, vp],
+                                         ctypes.c_int),
+        "ia_decode_noalloc_scratch_bytes": ([], sz),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -188,6 +191,18 @@ def ia_paged_attn_decode(ctx: Context, q, k_cache, v_cache, block_table, seq_len
                                        _p(k_scale), _p(v_scale), _p(block_table), int(block_table.shape[1]),
                                        _p(seq_lens), B, int(max_seq_len), _p(out), _p(workspace), ws_bytes,
                                        _stream(stream)))
+
+
+def ia_paged_attn_decode_noalloc(ctx: Context, q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
+                                 out, k_scale=None, v_scale=None, stream=None) -> None:
+    B = int(seq_lens.shape[0])
+    _check(load().ia_paged_attn_decode_noalloc(ctx.handle, _p(q), _p(k_cache), _p(v_cache), int(k_cache.shape[0]),
+                                               _p(k_scale), _p(v_scale), _p(block_table), int(block_table.shape[1]),
+                                               _p(seq_lens), B, int(max_seq_len), _p(out), _stream(stream)))
+
+
+def ia_decode_noalloc_scratch_bytes() -> int:
+    return int(load().ia_decode_noalloc_scratch_bytes())
 
 
 def ia_paged_attn_prefill(ctx: Context, q, cu_q_lens, seq_lens, k_cache, v_cache, block_table, max_q_len: int,
@@ -323,3 +338,4 @@ def ia_validate_attention_args(cu_q_lens, seq_lens, block_table, num_pages: int,
     tq = (int(cu[-1]) if cu is not None else B) if total_q is None else int(total_q)
     _check(load().ia_validate_attention_args(_p(cu), _p(sl), B, tq, _p(bt), int(bt.shape[1]) if bt.ndim == 2 else 0,
                                              int(num_pages), int(page_size), int(max_seq_len)))
+

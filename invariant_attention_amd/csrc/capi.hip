@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/invattn.h"
@@ -132,6 +133,40 @@ ia_status check_pages(const void* k_cache, const void* v_cache, int32_t num_page
   if (num_pages <= 0) return fail(IA_ERR_INVALID_ARG, "num_pages must be positive (got %d)", num_pages);
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(IA_ERR_INVALID_ARG, "page pools must be 16-byte aligned");
+  return IA_OK;
+}
+
+// Workspace of ia_paged_attn_decode_noalloc: one fixed array per GPU, held
+// from the library's load until the process ends.  Host code never uses the
+// array's name as an address (on the host it only names the symbol); each
+// device's own address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address reaches kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on its first use).
+ia_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(IA_ERR_HIP, "hipGetDevice: HIP error %d (%s)", (int)e, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(IA_ERR_INTERNAL, "device %d is past the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(IA_ERR_HIP, "hipGetSymbolAddress(scratch): HIP error %d (%s)", (int)e, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
   return IA_OK;
 }
 
@@ -292,6 +327,26 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
                                       static_cast<hipStream_t>(stream)),
                     "decode launch");
 }
+
+ia_status ia_paged_attn_decode_noalloc(const ia_ctx* ctx, const void* q, const void* k_cache, const void* v_cache,
+                                       int32_t num_pages, const float* k_scale, const float* v_scale,
+                                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                       int32_t B, int32_t max_seq_len, void* out, void* stream) {
+  if (!ctx) return fail(IA_ERR_INVALID_ARG, "ctx is NULL");
+  void* ws = nullptr;
+  ia_status st = scratch_address(&ws);
+  if (st != IA_OK) return st;
+  st = ia_paged_attn_decode(ctx, q, k_cache, v_cache, num_pages, k_scale, v_scale, block_table, bt_stride, seq_lens,
+                            B, max_seq_len, out, ws, kScratchBytes, stream);
+  if (st == IA_ERR_WORKSPACE_TOO_SMALL)
+    return fail(IA_ERR_WORKSPACE_TOO_SMALL,
+                "ia_paged_attn_decode_noalloc: batch %d at max_seq_len %d needs %zu bytes of workspace, more than "
+                "the library's %zu-byte scratch; use ia_paged_attn_decode with a caller workspace",
+                B, max_seq_len, ia_decode_workspace_bytes(ctx, B, max_seq_len), kScratchBytes);
+  return st;
+}
+
+size_t ia_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
                                 const int32_t* seq_lens, const void* k_cache, const void* v_cache,
