@@ -9,16 +9,27 @@ merge).  The timed region starts with every input resident in HBM.
 
 `value` is decode KV-read throughput: the algorithmic KV bytes of a step (sum_b n_b * Hkv * d *
 2 tensors * 2 bytes -- each sequence's K and V read once per KV head) divided by the step time
-(K steps timed between two device synchronisations).  The JSON line also carries the roofline of
-the decode call (its own duration from HIP events on the launch stream), batch sizes 1/8/64,
-the split-by-count comparison variant (the cost of invariance), a bitwise invariance rate
-measured in the same run, whole-prefill TFLOP/s, a plain device copy as the achievable-bandwidth
-reference, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+(K steps timed between two device synchronisations).  The JSON line also carries:
+  - roofline: the decode call's own duration from HIP events on the launch stream, with the HBM
+    traffic of the split kernel from the committed rocprofv3 counters;
+  - references: a plain streaming-read kernel (the achievable-HBM reference), torch's device copy
+    and sum, and kv_append at prefill size (32768 rows);
+  - batch sizes 1/8/64/256 (steady state and caches flushed), the split-by-count variant under the
+    automatic kernel choice and with the split kernel pinned for both policies (the cost of
+    invariance on one kernel), the bitwise-equivalent decode kernels at small batches;
+  - a bitwise invariance rate over execution variations measured in the same run;
+  - Qwen3-8B prefill: whole, in chunks of 64/256/1024, and over a cached 2048-token prefix;
+  - Qwen3-235B-shaped decode at 32768 context, batch 1/16/64, and the mixed decode + prefill batch;
+  - Llama-3.1-70B-shaped decode on a 16384-token shared prefix (bf16 and fp8), and one 131072-key
+    sequence;
+  - the batch-invariant layer operators against the vendor library;
+  - the fp64 CPU oracle on the whole headline workload (all host threads) and single-thread
+    figures for the tiny decode and for 8 sequences;
+  - a manifest (git commit, source hash, gfx architecture, config hash).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
     python bench.py --decode-only ...   headline decode only (for profilers)
     python bench.py --copy-probe        a plain copy of known size (counter calibration)
-    python bench.py --suite             also the long-context, mixed and shared-prefix workloads
     python bench.py --summarize-profile TRACE_DIR PMC_DIR   write the profile summary under profiles/
     python bench.py --summarize-spread-profile TRACE_DIR    the batch-1 spread-kernel trace summary
     python bench.py --summarize-layer-profile TRACE_DIR LAYER_JSON   the layer-operator trace summary
@@ -454,7 +465,10 @@ class DecodeWorld:
     """A decode workload resident on the GPU: pages, tables, queries, new-token rows, slots."""
 
     def __init__(self, shape: wl.AttnShape, lens, fp8=False, shared_prefix=0, width=None, scales=None,
-                 layout_seed=3):
+                 layout_seed=3, gpu_values=False, keep_host=False):
+        """gpu_values: K/V/Q drawn on the GPU from a seeded torch generator (N(0,1) rounded to bf16), for
+        the large timing-only worlds; otherwise from synth.workloads on the host (the tests' values).
+        keep_host: keep the host rows (bf16) so the oracle can scatter the same values."""
         self.shape = shape
         self.lens = [int(n) for n in lens]
         self.B = len(self.lens)
@@ -474,17 +488,30 @@ class DecodeWorld:
             self.k_scale = self.v_scale = None
         t0 = time.time()
         qs, knew, vnew, slots = [], [], [], []
+        self.host_rows = [] if keep_host else None
         n_shared = shared_prefix // shape.P
+        gen = None
+        if gpu_values:
+            gen = torch.Generator(device=DEV)
+            gen.manual_seed(SEED * 1000003 + layout_seed)
         for b, s in enumerate(self.seqs):
             # Shared prefix pages are written once (by the first sequence), as a prefix cache would.
             p0 = 0 if b == 0 else min(s.n, n_shared * shape.P)
-            kr = s.k(SEED, shape, p0, s.n)
-            vr = s.v(SEED, shape, p0, s.n)
+            if gen is not None:
+                kr = torch.randn((s.n - p0, shape.Hkv, shape.d), generator=gen, device=DEV).to(torch.bfloat16)
+                vr = torch.randn((s.n - p0, shape.Hkv, shape.d), generator=gen, device=DEV).to(torch.bfloat16)
+                qr = torch.randn((1, shape.Hq, shape.d), generator=gen, device=DEV).to(torch.bfloat16)
+            else:
+                kr = s.k(SEED, shape, p0, s.n)
+                vr = s.v(SEED, shape, p0, s.n)
+                qr = s.q(SEED, shape, s.n - 1, s.n)
+            if keep_host:
+                self.host_rows.append((p0, kr.cpu(), vr.cpu()))
             sl = torch.as_tensor(self.layout.slots(b, p0, s.n, shape.P), device=DEV)
             ia.ia_kv_append(self.ctx, kr.to(DEV), vr.to(DEV), sl, self.k, self.v, self.k_scale, self.v_scale)
-            qs.append(s.q(SEED, shape, s.n - 1, s.n))
-            knew.append(kr[-1:])
-            vnew.append(vr[-1:])
+            qs.append(qr.to(DEV))
+            knew.append(kr[-1:].to(DEV))
+            vnew.append(vr[-1:].to(DEV))
             slots.append(self.layout.slots(b, s.n - 1, s.n, shape.P))
         torch.cuda.synchronize()
         log(f"  filled {self.B} sequences ({sum(self.lens)} tokens) in {time.time() - t0:.1f}s")
@@ -824,24 +851,24 @@ def layer_ops(steps: int, warmup: int):
     return out
 
 
-def cpu_baseline(lens, shape, target_s=10.0, sample=32):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline workload: the first
-    `sample` sequences' decode rows (all query heads), on all host threads, repeated until about
-    target_s seconds of CPU time.  Its inputs come from the oracle's own page scatter."""
+def _oracle_decode_rate(shape, lens, rows_of, threads, layout_seed=9, repeat_to_s=0.0):
+    """Times the fp64 oracle on the decode rows of sequences with the given lengths: host pools laid
+    out by the oracle's own scatter of the rows rows_of(b) -> (K bf16, V bf16, Q bf16 of the last
+    position).  Returns (seconds per pass, passes, KV bytes per pass, fp64 flops per pass)."""
     from oracle import oracle
     oracle.build(force=False)
-    lens = [int(n) for n in lens[:sample]]
-    seqs = wl.make_sequences(lens)
-    layout = wl.layout_pages(9, lens, shape.P)
+    lens = [int(n) for n in lens]
+    layout = wl.layout_pages(layout_seed, lens, shape.P)
     kshape, vshape = oracle.kv_cache_shapes(layout.num_pages, shape.Hkv, shape.d, shape.P)
     kc, vc = np.zeros(kshape, np.uint16), np.zeros(vshape, np.uint16)
-    for b, s in enumerate(seqs):
-        oracle.kv_append(s.k(SEED, shape).view(torch.int16).numpy().view(np.uint16),
-                         s.v(SEED, shape).view(torch.int16).numpy().view(np.uint16),
-                         layout.slots(b, 0, s.n, shape.P), kc, vc, Hkv=shape.Hkv, d=shape.d, P=shape.P)
-    q = torch.cat([s.q(SEED, shape, s.n - 1, s.n) for s in seqs]).view(torch.int16).numpy().view(np.uint16)
-    cu = np.arange(sample + 1, dtype=np.int32)
-    threads = oracle.max_threads()
+    qs = []
+    for b in range(len(lens)):
+        k, v, q = rows_of(b)
+        oracle.kv_append(k.view(torch.int16).numpy().view(np.uint16), v.view(torch.int16).numpy().view(np.uint16),
+                         layout.slots(b, 0, lens[b], shape.P), kc, vc, Hkv=shape.Hkv, d=shape.d, P=shape.P)
+        qs.append(q)
+    q = torch.cat(qs).view(torch.int16).numpy().view(np.uint16)
+    cu = np.arange(len(lens) + 1, dtype=np.int32)
 
     def once():
         oracle.paged_attention(q, cu, np.array(lens, np.int32), kc, vc, layout.block_table, Hq=shape.Hq,
@@ -849,52 +876,289 @@ def cpu_baseline(lens, shape, target_s=10.0, sample=32):
 
     t0 = time.perf_counter()
     once()
-    t1 = time.perf_counter() - t0
-    reps = max(1, min(200, int(math.ceil(target_s / max(t1, 1e-3)))) - 1)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        once()
-    dt = time.perf_counter() - t0 if reps else t1
-    reps = max(reps, 1)
+    dt = time.perf_counter() - t0
+    passes = 1
+    if repeat_to_s > dt:
+        reps = min(200, int(math.ceil(repeat_to_s / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            once()
+        dt = (time.perf_counter() - t0) / reps
+        passes = reps + 1
     kvb = int(sum(lens)) * shape.Hkv * shape.d * 2 * 2
-    return {"value": round(kvb * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample} of the batch-256 sequences ({sum(lens)} tokens), their decode rows over "
-                      f"all 32 query heads in fp64, {reps} passes in {dt:.1f} s",
-            "cpu": cpu_model()}
+    flops = 4.0 * shape.d * shape.Hq * sum(lens)  # q.k and p.v per key and query head
+    return dt, passes, kvb, flops
 
 
-def suite(args):
-    """Long-context (Qwen3-235B shape), mixed-batch and shared-prefix (Llama-3.1-70B shape, bf16 and
-    fp8) decode points, each timed alone."""
-    out = {}
-    # 16 decode rows at 32768 context + batch 1 vs 64.
-    shape = wl.QWEN3_235B
-    w = DecodeWorld(shape, [32768] * 64)
-    split_ctx = make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT)
-    for B in (1, 16, 64):
-        s_ms, d_ms = time_steps(DecodeRunner(w, range(B)), args.steps, args.warmup, with_append=False)
-        s2, d2 = time_steps(DecodeRunner(w, range(B), split_ctx), args.steps, args.warmup, with_append=False)
-        out[f"qwen3-235b-32k-B{B}"] = {"decode_ms": round(d_ms, 4),
-                                       "gbs": round(w.kv_bytes(range(B)) / d_ms / 1e6, 1),
-                                       "split_kernel_decode_ms": round(d2, 4)}
-        log(f"qwen3-235b 32k B={B}: {out[f'qwen3-235b-32k-B{B}']}")
-    del w
+def cpu_baseline(world: DecodeWorld):
+    """The fp64 oracle, as it stands, timed on the host cores on the headline workload itself: the
+    whole batch-256 decode (every sequence's decode row, all query heads) once on all host threads,
+    plus single-thread figures for the tiny decode and for the first 8 sequences.  Its inputs are
+    the same bf16 values the GPU saw, laid out by the oracle's own scatter."""
+    from oracle import oracle
+    threads = oracle.max_threads()
+    shape = world.shape
+
+    def rows_of(b):
+        p0, k, v = world.host_rows[b]
+        assert p0 == 0
+        return k, v, world.q[b:b + 1].cpu()
+
+    dt, passes, kvb, fl = _oracle_decode_rate(shape, world.lens, rows_of, threads)
+    out = {"value": round(kvb / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole batch-256 headline workload ({sum(world.lens)} tokens): every sequence's decode "
+                     f"row over all {shape.Hq} query heads in fp64, one pass",
+           "wall_s": round(dt, 3), "gflops_fp64": round(fl / dt / 1e9, 2), "cpu": cpu_model()}
+    # Single thread: the first 8 sequences of the same workload, and the tiny decode (4 sequences,
+    # 8 query / 2 kv heads, head_dim 64, contexts 17 / 100 / 211 / 300).
+    dt8, p8, kv8, fl8 = _oracle_decode_rate(shape, world.lens[:8], rows_of, 1, repeat_to_s=3.0)
+    tiny = wl.TINY
+    tseqs = wl.make_sequences(list(wl.TINY_LENS))
+    dtt, pt, kvt, flt = _oracle_decode_rate(
+        tiny, list(wl.TINY_LENS), lambda b: (tseqs[b].k(SEED, tiny), tseqs[b].v(SEED, tiny),
+                                             tseqs[b].q(SEED, tiny, tseqs[b].n - 1, tseqs[b].n)), 1,
+        repeat_to_s=1.0)
+    out["single_thread"] = {
+        "llama3-8b-decode-B8": {"wall_s": round(dt8, 4), "passes": p8, "gbs": round(kv8 / dt8 / 1e9, 3),
+                                "gflops_fp64": round(fl8 / dt8 / 1e9, 3)},
+        "tiny-decode-B4": {"wall_s": round(dtt, 6), "passes": pt, "gbs": round(kvt / dtt / 1e9, 3),
+                           "gflops_fp64": round(flt / dtt / 1e9, 3)}}
+    return out
+
+
+def stream_read_reference(nbytes=4 * COPY_PROBE_BYTES, reps=20):
+    """The library's plain streaming-read kernel over nbytes: the achievable-HBM reference."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=DEV)
+    sink = torch.empty(ia.ia_stream_read_sink_bytes() // 4, dtype=torch.int32, device=DEV)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        ia.ia_stream_read(src, sink, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ia.ia_stream_read(src, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src
     torch.cuda.empty_cache()
-    # 128 sequences sharing a 16384-token prefix + private suffixes of 256-4096.
+    return {"kernel": "stream_read_kernel (16-byte loads, 8 in flight per thread)", "bytes_read": nbytes,
+            "ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1), "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
+def kv_append_prefill_size(steps=20, warmup=5):
+    """kv_append of a whole 8 x 4096-token prefill (Qwen3-8B shape: 32768 rows of 8 KV heads x 128,
+    bf16 K and V) into a shuffled page pool: bytes read + written per second."""
+    shape = wl.QWEN3_8B
+    lens = [4096] * 8
+    layout = wl.layout_pages(5, lens, shape.P)
+    ctx = make_ctx(shape)
+    k = torch.zeros((layout.num_pages, shape.Hkv, shape.d // 8, shape.P, 8), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros((layout.num_pages, shape.Hkv, shape.d, shape.P), dtype=torch.bfloat16, device=DEV)
+    T = sum(lens)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(SEED + 17)
+    kn = torch.randn((T, shape.Hkv, shape.d), generator=g, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((T, shape.Hkv, shape.d), generator=g, device=DEV).to(torch.bfloat16)
+    slots = torch.as_tensor(np.concatenate([layout.slots(b, 0, n, shape.P) for b, n in enumerate(lens)]), device=DEV)
+    stream = torch.cuda.current_stream()
+    run = lambda: ia.ia_kv_append(ctx, kn, vn, slots, k, v, stream=stream)  # noqa: E731
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 2 * (2 * T * shape.Hkv * shape.d * 2) + T * 8  # K and V read and written, plus the slots
+    return {"rows": T, "ms": round(ms, 4), "gbs_read_plus_written": round(nbytes / ms / 1e6, 1),
+            "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
+def qwen235_points(steps, warmup):
+    """Qwen3-235B-A22B attention shape (64 query / 4 KV heads, head_dim 128, bf16): decode at 32768
+    context for batch 1 / 16 / 64 -- the automatic kernel choice, and the cost of invariance with the
+    split kernel pinned (fixed 2048-token splits against the split-by-count variant, same kernel) --
+    and the mixed batch: 16 decode rows at 32768 context co-batched with 4 fresh 512-token prefill
+    chunks in one prefill call."""
+    shape = wl.QWEN3_235B
+    w = DecodeWorld(shape, [32768] * 64, gpu_values=True)
+    ctxs = {"auto": w.ctx, "split_fixed": make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT),
+            "split_by_count": make_ctx(shape, by_count=True, decode_kernel=ia.IA_DECODE_SPLIT)}
+    out = {}
+    for B in (1, 16, 64):
+        kb = w.kv_bytes(range(B))
+        row = {}
+        for name, ctx in ctxs.items():
+            _, d_ms = time_steps(DecodeRunner(w, range(B), ctx), steps, warmup, with_append=False)
+            _, dc_ms = time_steps(DecodeRunner(w, range(B), ctx), max(5, steps // 5), 3, with_append=False, flush=True)
+            row[name] = {"decode_ms": round(d_ms, 4), "gbs": round(kb / d_ms / 1e6, 1),
+                         "hbm_frac": round(kb / d_ms / 1e6 / HBM_PEAK_GBS, 4), "decode_ms_cold": round(dc_ms, 4),
+                         "gbs_cold": round(kb / dc_ms / 1e6, 1)}
+        row["fixed_over_by_count_time_same_kernel"] = round(row["split_fixed"]["decode_ms"] /
+                                                            row["split_by_count"]["decode_ms"], 3)
+        out[f"B{B}"] = row
+        log(f"qwen3-235b 32k B={B}: {row}")
+    # Mixed batch: one prefill call of 16 one-row decode queries (n = 32768) + 4 fresh 512-token prompts.
+    nq = 512
+    lens_p = [nq] * 4
+    layout_p = wl.layout_pages(21, lens_p, shape.P)
+    kp = torch.zeros((layout_p.num_pages, shape.Hkv, shape.d // 8, shape.P, 8), dtype=torch.bfloat16, device=DEV)
+    vp = torch.zeros((layout_p.num_pages, shape.Hkv, shape.d, shape.P), dtype=torch.bfloat16, device=DEV)
+    # One pool holds both: the prompts' pages are placed after the decode world's pages.
+    base = w.layout.num_pages
+    kk = torch.cat([w.k, kp])
+    vv = torch.cat([w.v, vp])
+    g = torch.Generator(device=DEV)
+    g.manual_seed(SEED + 23)
+    for b in range(4):
+        sl = torch.as_tensor(layout_p.slots(b, 0, nq, shape.P) + base * shape.P, device=DEV)
+        ia.ia_kv_append(w.ctx, torch.randn((nq, shape.Hkv, shape.d), generator=g, device=DEV).to(torch.bfloat16),
+                        torch.randn((nq, shape.Hkv, shape.d), generator=g, device=DEV).to(torch.bfloat16), sl, kk, vv)
+    width = max(w.layout.block_table.shape[1], layout_p.block_table.shape[1])
+    bt = np.full((20, width), -1, np.int32)
+    bt[:16, :w.layout.block_table.shape[1]] = w.layout.block_table[:16]
+    btp = layout_p.block_table.copy()
+    btp[btp >= 0] += base
+    bt[16:, :btp.shape[1]] = btp
+    q = torch.cat([w.q[:16], torch.randn((4 * nq, shape.Hq, shape.d), generator=g, device=DEV).to(torch.bfloat16)])
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum([1] * 16 + [nq] * 4)]).astype(np.int32), device=DEV)
+    sl = torch.as_tensor(np.array([32768] * 16 + [nq] * 4, np.int32), device=DEV)
+    btd = torch.as_tensor(bt, device=DEV)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def mixed():
+        ia.ia_paged_attn_prefill(w.ctx, q, cu, sl, kk, vv, btd, nq, 32768, o, stream=stream)
+
+    ms = _timed(mixed, steps, warmup)
+    flops = 4.0 * shape.d * shape.Hq * (16 * 32768 + 4 * nq * (nq + 1) / 2)
+    out["mixed_16x32k_decode_4x512_prefill"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                                                 "decode_kv_gbs": round(w.kv_bytes(range(16)) / ms / 1e6, 1)}
+    log(f"qwen3-235b mixed: {out['mixed_16x32k_decode_4x512_prefill']}")
+    del w, kk, vv, kp, vp
+    torch.cuda.empty_cache()
+    return out
+
+
+def llama70_points(steps, warmup):
+    """Llama-3.1-70B-shaped attention (64 query / 8 KV heads, head_dim 128): 128 sequences on a shared
+    16384-token prefix (1024 refcounted pages) plus private suffixes of 256-4096 tokens, block tables
+    of 8192 entries (131072 keys), bf16 pages and fp8 e4m3 pages with static per-head scales; and one
+    sequence at 131072 keys.  Logical KV bytes (what every sequence reads) against the distinct pages'
+    bytes; DRAM bytes of the same launch come from the profile's FETCH_SIZE counters."""
     shape = wl.LLAMA31_70B
     rng = np.random.default_rng([SEED, 5])
     lens = [16384 + int(x) for x in rng.integers(256, 4097, 128)]
+    out = {}
     for fp8 in (False, True):
-        w = DecodeWorld(shape, lens, fp8=fp8, shared_prefix=16384, width=8192)
-        s_ms, d_ms = time_steps(DecodeRunner(w, range(128)), args.steps, args.warmup, with_append=False)
+        w = DecodeWorld(shape, lens, fp8=fp8, shared_prefix=16384, width=8192, gpu_values=True)
+        _, d_ms = time_steps(DecodeRunner(w, range(128)), steps, warmup, with_append=False)
+        _, dc_ms = time_steps(DecodeRunner(w, range(128)), max(5, steps // 5), 3, with_append=False, flush=True)
         bpt = shape.Hkv * shape.d * 2 * (1 if fp8 else 2)
-        key = f"llama70b-shared-prefix-{'fp8' if fp8 else 'bf16'}"
+        key = "fp8" if fp8 else "bf16"
         out[key] = {"decode_ms": round(d_ms, 4), "logical_gbs": round(w.kv_bytes() / d_ms / 1e6, 1),
-                    "distinct_page_gbs": round(w.distinct_pages * shape.P * bpt / d_ms / 1e6, 1)}
-        log(f"{key}: {out[key]}")
+                    "distinct_page_gbs": round(w.distinct_pages * shape.P * bpt / d_ms / 1e6, 1),
+                    "decode_ms_cold": round(dc_ms, 4), "logical_gbs_cold": round(w.kv_bytes() / dc_ms / 1e6, 1),
+                    "logical_bytes": w.kv_bytes(), "distinct_page_bytes": w.distinct_pages * shape.P * bpt}
+        log(f"llama70b shared prefix {key}: {out[key]}")
         del w
         torch.cuda.empty_cache()
+    w = DecodeWorld(shape, [131072], width=8192, gpu_values=True)
+    _, d_ms = time_steps(DecodeRunner(w, range(1)), steps, warmup, with_append=False)
+    out["B1_131072"] = {"decode_ms": round(d_ms, 4), "gbs": round(w.kv_bytes() / d_ms / 1e6, 1)}
+    log(f"llama70b B=1 at 131072: {out['B1_131072']}")
+    del w
+    torch.cuda.empty_cache()
     return out
+
+
+def _timed(fn, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def prefill_chunked(steps, warmup):
+    """Qwen3-8B-shaped prefill of 8 prompts x 4096 tokens in chunks of 64 / 256 / 1024 tokens (chunk k of
+    every prompt in one call, key length = the chunk's end), and its second half alone over a cached
+    2048-token prefix; TFLOP/s over all the calls of a pass (4 d Hq sum over rows of p + 1)."""
+    shape = wl.QWEN3_8B
+    n, B = 4096, 8
+    seqs, layout, ctx, k, v = _prefill_world(shape, [n] * B, 5)
+    q = torch.cat([s.q(SEED, shape, 0, n) for s in seqs]).to(DEV).view(B, n, shape.Hq, shape.d)
+    bt = torch.as_tensor(layout.block_table, device=DEV)
+    stream = torch.cuda.current_stream()
+
+    def calls(p_pairs):
+        prepared = []
+        for p0, p1 in p_pairs:
+            qc = q[:, p0:p1].reshape(-1, shape.Hq, shape.d).contiguous()
+            cu = torch.as_tensor(np.arange(0, B * (p1 - p0) + 1, p1 - p0, dtype=np.int32), device=DEV)
+            sl = torch.as_tensor(np.full(B, p1, np.int32), device=DEV)
+            prepared.append((qc, cu, sl, torch.empty_like(qc), p1 - p0, p1))
+        return prepared
+
+    def run(prepared):
+        for qc, cu, sl, o, ql, kl in prepared:
+            ia.ia_paged_attn_prefill(ctx, qc, cu, sl, k, v, bt, ql, kl, o, stream=stream)
+
+    def flops(p0, p1):
+        return 4.0 * shape.d * shape.Hq * B * sum(p + 1 for p in range(p0, p1))
+
+    out = {}
+    for budget in (64, 256, 1024, n):
+        pairs = [(c0, min(n, c0 + budget)) for c0 in range(0, n, budget)]
+        prep = calls(pairs)
+        ms = _timed(lambda: run(prep), max(3, steps // 10), 2)
+        fl = sum(flops(a, b) for a, b in pairs)
+        key = "whole" if budget == n else f"chunks_{budget}"
+        out[key] = {"calls_per_pass": len(pairs), "ms_per_pass": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                    "frac_of_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        log(f"prefill {key}: {out[key]}")
+    prep = calls([(n // 2, n)])
+    ms = _timed(lambda: run(prep), max(5, steps // 5), 3)
+    fl = flops(n // 2, n)
+    out["cached_prefix_2048_suffix_2048"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                                             "frac_of_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    log(f"prefill cached prefix: {out['cached_prefix_2048_suffix_2048']}")
+    del k, v, q
+    torch.cuda.empty_cache()
+    return out
+
+
+def manifest(config: dict):
+    """Where the numbers came from: git commit (or the one recorded at build time when the tree has no
+    .git), a hash of the library's sources as they ran, the GPU's architecture, and a config hash."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "invariant_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    build_sha = None
+    try:
+        with open(os.path.join(ROOT, "invariant_attention_amd", "build_info.json")) as f:
+            build_sha = json.load(f).get("git")
+    except (OSError, ValueError):
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"git": git_sha() or build_sha, "git_at_build": build_sha, "sources_sha256": h.hexdigest()[:16],
+            "config_sha256": hashlib.sha256(json.dumps(config, sort_keys=True).encode()).hexdigest()[:16],
+            "torch": torch.__version__, "hip": torch.version.hip, "device": torch.cuda.get_device_name(0),
+            "gfx_arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "seed": SEED, "host_threads": os.cpu_count(), "cpu": cpu_model()}
 
 
 def main():
@@ -905,7 +1169,6 @@ def main():
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--decode-only", action="store_true", help="time the headline batch only (for profilers)")
     ap.add_argument("--copy-probe", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--suite", action="store_true", help="also time the long-context and shared-prefix points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time the prefill workload only (for profilers)")
     ap.add_argument("--layer-only", action="store_true", help="time the layer operators only (for profilers)")
@@ -944,7 +1207,7 @@ def main():
     shape = wl.LLAMA3_8B
     lens = wl.uniform_lens(SEED, args.batch, 512, 8192)
     log(f"decode workload: llama3-8b shape, B={args.batch}, {sum(lens)} tokens")
-    world = DecodeWorld(shape, lens)
+    world = DecodeWorld(shape, lens, keep_host=not (args.no_cpu_baseline or args.decode_only))
     head = DecodeRunner(world, range(args.batch))
     torch.cuda.synchronize()
     step_ms, dec_ms = time_steps(head, args.steps, args.warmup)
@@ -972,10 +1235,16 @@ def main():
     }
     if not args.decode_only:
         result["copy_reference"] = copy_gbs()
+        result["stream_read_reference"] = stream_read_reference()
         result["read_reference"] = read_gbs()
-        log(f"plain copy: {result['copy_reference']}, plain read: {result['read_reference']}")
-        batches, by_count = {}, {}
+        log(f"plain copy: {result['copy_reference']}, stream read: {result['stream_read_reference']}, "
+            f"torch sum: {result['read_reference']}")
+        result["kv_append_prefill_size"] = kv_append_prefill_size()
+        log(f"kv_append at prefill size: {result['kv_append_prefill_size']}")
+        batches, by_count, same_kernel = {}, {}, {}
         bc_ctx = make_ctx(shape, by_count=True)
+        split_fixed = make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT)
+        split_bc = make_ctx(shape, by_count=True, decode_kernel=ia.IA_DECODE_SPLIT)
         for B in (1, 8, 64, args.batch):
             s_ms, d_ms = time_steps(DecodeRunner(world, range(B)), args.steps, args.warmup)
             _, dc_ms = time_steps(DecodeRunner(world, range(B)), args.steps, args.warmup, flush=True)
@@ -988,9 +1257,18 @@ def main():
             by_count[str(B)] = {"step_ms": round(s2, 4), "gbs": round(kb / (s2 * 1e-3) / 1e9, 1),
                                 "fixed_over_by_count_time": round(s_ms / s2, 3), "decode_ms_cold": round(d2c, 4),
                                 "fixed_over_by_count_time_cold": round(dc_ms / d2c, 3)}
-            log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s")
+            # The cost of invariance on one kernel: both split policies on the split kernel.
+            _, f_ms = time_steps(DecodeRunner(world, range(B), split_fixed), args.steps, args.warmup)
+            _, c_ms = time_steps(DecodeRunner(world, range(B), split_bc), args.steps, args.warmup)
+            same_kernel[str(B)] = {"fixed_decode_ms": round(f_ms, 4), "by_count_decode_ms": round(c_ms, 4),
+                                   "fixed_gbs": round(kb / (f_ms * 1e-3) / 1e9, 1),
+                                   "by_count_gbs": round(kb / (c_ms * 1e-3) / 1e9, 1),
+                                   "fixed_over_by_count_time": round(f_ms / c_ms, 3)}
+            log(f"B={B}: fixed {batches[str(B)]['gbs']} GB/s, split-by-count {by_count[str(B)]['gbs']} GB/s; "
+                f"split kernel for both: {same_kernel[str(B)]}")
         result["batches"] = batches
         result["split_by_count"] = by_count
+        result["cost_of_invariance_split_kernel"] = same_kernel
         # The same decode call with the caches flushed before each call (no K/V or table data left
         # from the previous step), beside the steady-state figure above.
         cold_ms = batches[str(args.batch)]["decode_ms_cold"]
@@ -1025,19 +1303,19 @@ def main():
         result["invariance_by_variation"] = {k: f"{e}/{t}" for k, (e, t) in var.items()}
         result["split_by_count_invariance_rate"] = round(eq_c / tot_c, 6)
         log(f"invariance: fixed {eq_all}/{tot_all} {result['invariance_by_variation']}, split-by-count {eq_c}/{tot_c}")
-        del world, head
-        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and not args.decode_only:
+        result["cpu_baseline"] = cpu_baseline(world)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    del world, head
+    torch.cuda.empty_cache()
+    if not args.decode_only:
         result["prefill"] = prefill_tflops(max(10, args.steps // 4), 10)
         log(f"prefill: {result['prefill']}")
+        result["prefill_chunked"] = prefill_chunked(args.steps, args.warmup)
+        result["qwen3_235b"] = qwen235_points(args.steps, args.warmup)
+        result["llama31_70b_shared_prefix"] = llama70_points(args.steps, args.warmup)
         result["layer_ops"] = layer_ops(max(3, args.steps // 4), 2)
-        if args.suite:
-            result["suite"] = suite(args)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(lens, shape)
-        log(f"cpu baseline: {result['cpu_baseline']}")
-    result["manifest"] = {"git": git_sha(), "torch": torch.__version__, "hip": torch.version.hip,
-                          "device": torch.cuda.get_device_name(0), "seed": SEED,
-                          "host_threads": os.cpu_count(), "cpu": cpu_model()}
+    result["manifest"] = manifest(result["config"])
     print(json.dumps(result), flush=True)
 
 

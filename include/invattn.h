@@ -389,6 +389,19 @@ ia_status ia_validate_attention_args(const int32_t* cu_q_lens, const int32_t* se
                                      const int32_t* block_table, int32_t bt_stride, int32_t num_pages,
                                      int32_t page_size, int32_t max_seq_len);
 
+/* ------------------------------------------------------------------------
+ * Measurement reference (not part of the attention path): a kernel that does
+ * nothing but stream `bytes` of device memory from buf (16-byte loads, 8 in
+ * flight per thread, 8 workgroups of 256 threads per compute unit) and xor
+ * them into one word per workgroup in sink, so that the decode kernel's
+ * KV-read rate can be set beside what a plain read reaches on the same GPU.
+ *   buf   dev, 16-byte aligned, bytes a multiple of 16
+ *   sink  dev, >= ia_stream_read_sink_bytes() bytes (its contents are
+ *         meaningless)
+ */
+size_t ia_stream_read_sink_bytes(void);
+ia_status ia_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

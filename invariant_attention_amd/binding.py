@@ -39,6 +39,7 @@ EXPORTS = [
     "ia_seq_commit", "ia_seq_block_table", "ia_seq_len", "ia_seq_end", "ia_pool_evict", "ia_pool_page_refs",
     "ia_pool_page_published", "ia_pool_num_free", "ia_rmsnorm", "ia_gemm_bf16", "ia_validate_slots",
     "ia_validate_attention_args", "ia_paged_attn_decode_noalloc", "ia_decode_noalloc_scratch_bytes",
+    "ia_stream_read", "ia_stream_read_sink_bytes",
 ]
 
 
@@ -100,6 +101,8 @@ def load() -> ctypes.CDLL:
         "ia_paged_attn_decode_noalloc": ([vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, vp, vp],
                                          ctypes.c_int),
         "ia_decode_noalloc_scratch_bytes": ([], sz),
+        "ia_stream_read": ([vp, sz, vp, sz, vp], ctypes.c_int),
+        "ia_stream_read_sink_bytes": ([], sz),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -339,3 +342,14 @@ def ia_validate_attention_args(cu_q_lens, seq_lens, block_table, num_pages: int,
     _check(load().ia_validate_attention_args(_p(cu), _p(sl), B, tq, _p(bt), int(bt.shape[1]) if bt.ndim == 2 else 0,
                                              int(num_pages), int(page_size), int(max_seq_len)))
 
+
+# --------------------------------------------------------- measurement helper
+
+def ia_stream_read_sink_bytes() -> int:
+    return int(load().ia_stream_read_sink_bytes())
+
+
+def ia_stream_read(buf, sink, stream=None) -> None:
+    """Streams every byte of the device tensor buf (the achievable-HBM reference kernel)."""
+    _check(load().ia_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                 sink.numel() * sink.element_size(), _stream(stream)))

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libinvattn.so")
-SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "layer_ops.hip", "capi.hip", "pool.cpp"]
+SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "layer_ops.hip", "probe.hip", "capi.hip", "pool.cpp"]
 HEADERS = ["arith.hpp", "pages.hpp", "launch.hpp", "errors.hpp"]
 
 # -ffp-contract=off: no implicit FMA contraction -- the arithmetic order is the one
@@ -45,7 +45,21 @@ def build(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+def _write_build_info() -> None:
+    """Records the git commit the library was built from (build_info.json, beside the library), for
+    runs on a copy of the tree that has no .git."""
+    import json
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=os.path.dirname(HERE), capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        sha = None
+    with open(os.path.join(HERE, "build_info.json"), "w") as f:
+        json.dump({"git": sha}, f)
 
 
 if __name__ == "__main__":

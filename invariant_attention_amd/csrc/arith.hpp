@@ -14,14 +14,23 @@
 //   scores   D[key][row] = sum_d K[key][d] * Q[row][d]     A = K tile, B = Q^T
 //   values   D[dim][row] = sum_key V^T[dim][key] * P^T[key][row]
 //                                                          A = V^T,    B = P^T
+// Keys.  A 64-key tile is four 16-key pages; keys 32*h .. 32*h + 31 (pages
+// 2h and 2h + 1) form the pair h.  The value product takes the pair h as its
+// k-step ks2 = h, and MFMA k-slot j (0..7) of lane group g is key
+// 32*h + 8*g + j there: 8 consecutive tokens of one page (page 2h + g/2,
+// tokens 8*(g%2) .. 8*(g%2) + 7), so a lane's V^T operand is one 16-byte
+// run of the page layout.  The score product computes the same pair as two
+// score blocks sb = 2h (half 0) and 2h + 1 (half 1): MFMA row m of score block
+// sb is key 32*h + 8*(m/4) + 4*(sb%2) + m%4 (score_row_key), so the block's
+// output leaves in lane group g the keys 32*h + 8*g + 4*(sb%2) + j, j = 0..3
+// (tile_key) -- exactly the k-slots 4*(sb%2) + j of the value product.  The
+// weights a lane produces are thus the B operand it feeds into the value
+// product, with no cross-lane shuffle.
 // Lane l (group g = l / 16) holds, for its row l % 16:
-//   scores of keys 16*blk + 4*g + j          (blk = 0..3, j = 0..3)
-//   accumulators of dims 16*mb + 4*g + j     (mb = 0..d/16-1, j = 0..3)
-// MFMA k-slot j (0..7) of lane group g is, in k-step ks of the score product,
-// dim 32*ks + 8*g + j; in k-step ks2 of the value product it is key
-// 32*ks2 + 4*g + j for j < 4 and key 32*ks2 + 16 + 4*g + (j - 4) for j >= 4.
-// So the weights a lane produces are exactly the B operand it feeds into the
-// value product, with no cross-lane shuffle.
+//   scores of keys tile_key(sb, g, j)          (sb = 0..3, j = 0..3)
+//   accumulators of dims 16*mb + 4*g + j       (mb = 0..d/16-1, j = 0..3)
+// MFMA k-slot j of lane group g in k-step ks of the score product is dim
+// 32*ks + 8*g + j.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +49,13 @@ constexpr int kBlockKeys = 16;  // keys per MFMA block (one page)
 constexpr int kRows = 16;       // query rows per wave
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Key (offset in its tile) of element j (0..3) that lane group g holds in
+// score block sb, and key of MFMA row m of score block sb (the K operand row).
+__device__ __forceinline__ int tile_key(int sb, int g, int j) { return 32 * (sb >> 1) + 8 * g + 4 * (sb & 1) + j; }
+__device__ __forceinline__ int score_row_key(int sb, int m) {
+  return 32 * (sb >> 1) + 8 * (m >> 2) + 4 * (sb & 1) + (m & 3);
+}
 
 // The single exp2 of the library (v_exp_f32).  exp2(0) = 1 and
 // exp2(-inf) = 0 exactly.
@@ -103,8 +119,8 @@ struct QFrag {
   bf16x8 f[D / 32];
 };
 
-// Scores of one key block (16 keys) for the wave's rows: s[j] = <q_row,
-// k_{16 blk + 4 g + j}> as one MFMA chain over the D/32 k-steps of the head
+// Scores of one score block (16 keys) for the wave's rows: s[j] = <q_row,
+// k_{tile_key(sb, g, j)}> as one MFMA chain over the D/32 k-steps of the head
 // dim, in ascending order.  Which wave computes a block does not change its
 // bits: a column of the product depends only on its own operands.
 template <int D>
@@ -169,7 +185,7 @@ __device__ __forceinline__ TileMax tile_max(const f32x4 (&s)[4], float c, int ti
   for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
+      const int key = tile_key0 + tile_key(blk, lane_group, j);
       const float g = s[blk][j] * c;
       tm.x[blk][j] = (!MASK || key_visible(key, lo, limit)) ? g : neg_inf();
       mx = fmaxf(mx, tm.x[blk][j]);
@@ -208,7 +224,7 @@ __device__ __forceinline__ TileStep tile_weights(float m, const TileMax& tm, int
   for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = tile_key0 + 16 * blk + 4 * lane_group + j;
+      const int key = tile_key0 + tile_key(blk, lane_group, j);
       a[blk][j] = (!MASK || key_visible(key, lo, limit)) ? ia_exp2(tm.x[blk][j] - ts.m_new) : 0.f;
       sum = sum + a[blk][j];
     }

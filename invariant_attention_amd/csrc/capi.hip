@@ -348,6 +348,18 @@ ia_status ia_paged_attn_decode_noalloc(const ia_ctx* ctx, const void* q, const v
 
 size_t ia_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+size_t ia_stream_read_sink_bytes(void) { return (size_t)ia::stream_read_blocks() * sizeof(uint32_t); }
+
+ia_status ia_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(IA_ERR_INVALID_ARG, "buf/sink is NULL");
+  if (!aligned(buf, 16) || bytes % 16 != 0) return fail(IA_ERR_INVALID_ARG, "buf and bytes must be 16-byte aligned");
+  if (sink_bytes < ia_stream_read_sink_bytes())
+    return fail(IA_ERR_WORKSPACE_TOO_SMALL, "sink needs %zu bytes (got %zu)", ia_stream_read_sink_bytes(), sink_bytes);
+  return hip_status(ia::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)),
+                    "stream read launch");
+}
+
 ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
                                 const int32_t* seq_lens, const void* k_cache, const void* v_cache,
                                 int32_t num_pages, const float* k_scale, const float* v_scale,

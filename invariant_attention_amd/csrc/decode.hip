@@ -3,7 +3,7 @@
 //
 // One workgroup of 4 waves per (sequence b, kv head, split s).  The g query
 // heads of the group are the rows (padded to 16).  Per 64-key tile, wave w
-// computes the scores of key block w (its own 16 keys, all head dims),
+// computes the scores of score block w (its own 16 keys, all head dims),
 // the 4 waves exchange scores through LDS, every wave runs the same softmax
 // step on the whole tile, and wave w applies it to dim blocks
 // [w * D/64, (w + 1) * D/64) of the value accumulators.  A row's operations
@@ -36,14 +36,14 @@ __device__ __forceinline__ int split_len(int policy, int S, int n, int B) {
   return len < 64 ? 64 : len;
 }
 
-// Raw fragments one wave needs for one tile: K block w (all k-steps) and the
-// V^T fragments of its D/64 dim blocks (4 key quads each), plus the key
-// count of every block for the zero fill of V.
+// Raw fragments one wave needs for one tile: score block w's K (all k-steps)
+// and the V^T runs of its D/64 dim blocks (one per k-step), plus the key
+// count of every page block for the zero fill of V.
 template <int D, bool FP8>
 struct DecodeFrags {
   static constexpr int MB = D / 64;
   typename Raw<FP8>::K k[D / 32];
-  typename Raw<FP8>::V v[MB][2][2];
+  typename Raw<FP8>::V8 v[MB][2];
   int valid[4];
 };
 
@@ -58,24 +58,22 @@ __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const 
   constexpr int EB = Raw<FP8>::kElemBytes;
   constexpr size_t kHeadBytes = (size_t)D * 16 * EB;  // one (page, kv head) block
   const TilePages tp = tile_pages_of(e, t0, n, num_pages);
-  const int kpg = w == 0 ? tp.page[0] : (w == 1 ? tp.page[1] : (w == 2 ? tp.page[2] : tp.page[3]));
-  const uint8_t* kp = kc + ((size_t)kpg * Hkv + kvh) * kHeadBytes;
+  // Score block w: the lane's key lies in page block 2 (w / 2) + r / 8.
+  const int kpa = (w >> 1) == 0 ? tp.page[0] : tp.page[2];
+  const int kpb = (w >> 1) == 0 ? tp.page[1] : tp.page[3];
+  const uint8_t* kp = kc + ((size_t)((r >> 3) ? kpb : kpa) * Hkv + kvh) * kHeadBytes;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const uint32_t off = (uint32_t)(((4 * ks + g) * 16 + r) * 8 * EB);
-    f.k[ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(kp + off);
+  for (int ks = 0; ks < D / 32; ++ks)
+    f.k[ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(kp + k_frag_off<D, FP8>(w, ks, r, g));
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    // The lane's V run lies in page block 2 ks2 + g / 2.
+    const int pg = (g >> 1) ? tp.page[2 * ks2 + 1] : tp.page[2 * ks2];
+    const uint8_t* vp = vc + ((size_t)pg * Hkv + kvh) * kHeadBytes;
+#pragma unroll
+    for (int mbi = 0; mbi < MB; ++mbi)
+      f.v[mbi][ks2] = *reinterpret_cast<const typename Raw<FP8>::V8*>(vp + v_frag_off<D, FP8>(w * MB + mbi, r, g));
   }
-#pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const uint8_t* vp = vc + ((size_t)tp.page[2 * ks2 + hb] * Hkv + kvh) * kHeadBytes;
-#pragma unroll
-      for (int mbi = 0; mbi < MB; ++mbi) {
-        const uint32_t off = (uint32_t)(((16 * (w * MB + mbi) + r) * 16 + 4 * g) * EB);
-        f.v[mbi][ks2][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(vp + off);
-      }
-    }
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) f.valid[blk] = tp.valid[blk];
 }
@@ -105,14 +103,8 @@ __device__ __forceinline__ void decode_tile(const DecodeFrags<D, FP8>& f, const 
   for (int mbi = 0; mbi < MB; ++mbi) {
     bf16x8 vf[2];
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const bf16x4 v4 = v_to_bf16(f.v[mbi][ks2][hb], FULL ? 4 : f.valid[2 * ks2 + hb] - 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
-      }
-    }
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+      vf[ks2] = v8_to_bf16(f.v[mbi][ks2], FULL ? 8 : ((g >> 1) ? f.valid[2 * ks2 + 1] : f.valid[2 * ks2]) - 8 * (g & 1));
     u[mbi] = pv_block(u[mbi], vf, ts);
   }
   commit_scalars(m, z, ts);
@@ -267,12 +259,12 @@ constexpr int kWideChunk = kWideWaves;  // tiles per chunk: one per wave in A an
 constexpr int kWideMaxTiles = 256;      // longest split the wide kernel takes: 16384 keys
 
 template <int D, bool FP8>
-struct WideK {  // K of one tile: 4 key blocks x D/32 k-steps
+struct WideK {  // K of one tile: 4 score blocks x D/32 k-steps
   typename Raw<FP8>::K k[4][D / 32];
 };
 template <int D, bool FP8>
-struct WideV {  // V^T of one dim block of one tile: [ks2][hb] key quads
-  typename Raw<FP8>::V v[2][2];
+struct WideV {  // V^T of one dim block of one tile: one run per k-step
+  typename Raw<FP8>::V8 v[2];
 };
 
 template <int D, bool FP8>
@@ -352,21 +344,22 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
       const TilePages tp = pages(c0 + i);
       vv[i] = tp.valid[0] | (tp.valid[1] << 5) | (tp.valid[2] << 10) | (tp.valid[3] << 15);
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const uint8_t* base = vc + ((size_t)tp.page[2 * ks2 + hb] * a.Hkv + kvh) * kHeadBytes;
-          vr[i].v[ks2][hb] = load_v_raw<FP8>(base, (size_t)(16 * wd + r) * 16 + 4 * g);
-        }
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const int pg = (g >> 1) ? tp.page[2 * ks2 + 1] : tp.page[2 * ks2];
+        const uint8_t* base = vc + ((size_t)pg * a.Hkv + kvh) * kHeadBytes;
+        vr[i].v[ks2] = *reinterpret_cast<const typename Raw<FP8>::V8*>(base + v_frag_off<D, FP8>(wd, r, g));
+      }
     }
   };
   auto load_k = [&](WideK<D, FP8>& kr, int c0) {
     const TilePages kp = pages(c0 + w);
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const uint8_t* base = kc + ((size_t)kp.page[blk] * a.Hkv + kvh) * kHeadBytes;
+    for (int sb = 0; sb < 4; ++sb) {
+      const int pg = (r >> 3) ? kp.page[2 * (sb >> 1) + 1] : kp.page[2 * (sb >> 1)];
+      const uint8_t* base = kc + ((size_t)pg * a.Hkv + kvh) * kHeadBytes;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) kr.k[blk][ks] = load_k_raw<FP8>(base, (size_t)((4 * ks + g) * 16 + r) * 8);
+      for (int ks = 0; ks < D / 32; ++ks)
+        kr.k[sb][ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(base + k_frag_off<D, FP8>(sb, ks, r, g));
     }
   };
 
@@ -427,9 +420,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
       if (!full(k_begin + kTileKeys * (c0 + i))) {
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            vr[i].v[ks2][hb] = v_keep(vr[i].v[ks2][hb], ((vvalid[i] >> (5 * (2 * ks2 + hb))) & 31) - 4 * g);
+          vr[i].v[ks2] = v8_keep(vr[i].v[ks2], ((vvalid[i] >> (5 * v_block(ks2, g))) & 31) - 8 * (g & 1));
       }
     }
     __syncthreads();
@@ -466,13 +457,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
         ts.plo[1] = __builtin_bit_cast(bf16x8, pw[i][3][lane]);
         bf16x8 vf[2];
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const bf16x4 v4 = v_to_bf16(vr[i].v[ks2][hb], 4);  // already zero filled
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
-          }
+        for (int ks2 = 0; ks2 < 2; ++ks2) vf[ks2] = v8_to_bf16(vr[i].v[ks2], 8);  // already zero filled
         // The masked form's final select is the identity where every key is
         // visible, so one form serves full and masked tiles.
         u = pv_block<true>(u, vf, ts);
@@ -592,14 +577,17 @@ __global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
   const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
                            __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
   const TilePages tp = tile_pages_of(e, t0, sp.n, a.num_pages);
-  // The K of all 4 key blocks, then their scores (the split kernel's k-slot
-  // mapping: lane (r, g) holds chunk 4 ks + g of token r).
+  // The K of all 4 score blocks, then their scores (the split kernel's
+  // key-to-slot mapping: lane (r, g) holds chunk 4 ks + g of the key of MFMA
+  // row r).
   typename Raw<FP8>::K kr[4][D / 32];
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    const uint8_t* base = a.k_cache + ((size_t)tp.page[blk] * a.Hkv + un.kvh) * kHeadBytes;
+  for (int sb = 0; sb < 4; ++sb) {
+    const int pg = (r >> 3) ? tp.page[2 * (sb >> 1) + 1] : tp.page[2 * (sb >> 1)];
+    const uint8_t* base = a.k_cache + ((size_t)pg * a.Hkv + un.kvh) * kHeadBytes;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) kr[blk][ks] = load_k_raw<FP8>(base, (size_t)((4 * ks + g) * 16 + r) * 8);
+    for (int ks = 0; ks < D / 32; ++ks)
+      kr[sb][ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(base + k_frag_off<D, FP8>(sb, ks, r, g));
   }
   f32x4 sc[4];
 #pragma unroll
@@ -689,7 +677,7 @@ template <bool FP8>
 struct SpreadFrag {  // one tile's operands for one wave of decode_value_kernel
   uint4 w[4];                    // phi[0], plo[0], phi[1], plo[1]
   f32x4 asm4;                    // alpha, row sum, row maximum, 0
-  typename Raw<FP8>::V v[2][2];  // V^T quads of the wave's dim block
+  typename Raw<FP8>::V8 v[2];    // V^T runs of the wave's dim block
 };
 
 // The chain half of the split kernel's tile step, for one dim block: the z
@@ -709,14 +697,10 @@ __device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, int valid
   ts.z_new = z_update(z, f.asm4[0], f.asm4[1]);
   bf16x8 vf[2];
 #pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int nv = FULL ? 4 : ((valid >> (5 * (2 * ks2 + hb))) & 31) - 4 * g;
-      const bf16x4 v4 = v_to_bf16(f.v[ks2][hb], nv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vf[ks2][4 * hb + j] = v4[j];
-    }
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    const int nv = FULL ? 8 : ((valid >> (5 * v_block(ks2, g))) & 31) - 8 * (g & 1);
+    vf[ks2] = v8_to_bf16(f.v[ks2], nv);
+  }
   u = pv_block(u, vf, ts);
   commit_scalars(m, z, ts);
 }
@@ -839,10 +823,8 @@ __global__ __launch_bounds__(256) void decode_value_kernel(DecodeArgs a) {
       const uint8_t* src = ring + j * kSlotBytes;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          f.v[ks2][hb] = *reinterpret_cast<const typename Raw<FP8>::V*>(src + (2 * ks2 + hb) * (kVBytes / 4) +
-                                                                         (r * 16 + 4 * g) * EB);
+        f.v[ks2] = *reinterpret_cast<const typename Raw<FP8>::V8*>(src + v_block(ks2, g) * (kVBytes / 4) +
+                                                                    (r * 16 + 8 * (g & 1)) * EB);
 #pragma unroll
       for (int part = 0; part < 4; ++part)
         f.w[part] = *reinterpret_cast<const uint4*>(src + kVBytes + ((4 * part + g) * a.group + rr) * 16);

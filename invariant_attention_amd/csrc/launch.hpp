@@ -74,6 +74,9 @@ int prefill_positions_per_block(int group);
 // Layer operators (layer_ops.hip).
 hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, int H, float eps, hipStream_t st);
 hipError_t launch_gemm(const __bf16* a, const __bf16* wt, __bf16* c, int M, int N, int K, hipStream_t st);
+// Measurement reference (probe.hip): a plain streaming read of `bytes`.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+int stream_read_blocks();
 int gemm_tile_m();
 int gemm_tile_n();
 int gemm_tile_k();

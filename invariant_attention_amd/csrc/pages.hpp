@@ -23,20 +23,23 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 // ---------------------------------------------------------------- raw types
 
-// Raw page words of one K chunk (8 dims of one token) and of one V quad
-// (4 tokens of one dim): bf16 bits, or e4m3 codes.
+// Raw page words of one K chunk (8 dims of one token), of one V quad (4
+// tokens of one dim) and of one V run (8 tokens of one dim: a lane's V^T
+// operand of the value product): bf16 bits, or e4m3 codes.
 template <bool FP8>
 struct Raw;
 template <>
 struct Raw<false> {
   using K = uint4;
   using V = uint2;
+  using V8 = uint4;
   static constexpr int kElemBytes = 2;
 };
 template <>
 struct Raw<true> {
   using K = uint2;
   using V = uint32_t;
+  using V8 = uint2;
   static constexpr int kElemBytes = 1;
 };
 
@@ -88,6 +91,48 @@ __device__ __forceinline__ bf16x4 v_to_bf16(uint32_t w, int nv) {
   bf16x4 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   return r;
+}
+
+// V run with only the first nv of its 8 tokens kept (nv may be <= 0 or
+// >= 8); the others become zero bits.
+__device__ __forceinline__ uint4 v8_keep(uint4 w, int nv) {
+  const uint2 lo = v_keep(make_uint2(w.x, w.y), nv), hi = v_keep(make_uint2(w.z, w.w), nv - 4);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+__device__ __forceinline__ uint2 v8_keep(uint2 w, int nv) {
+  return make_uint2(v_keep((uint32_t)w.x, nv), v_keep((uint32_t)w.y, nv - 4));
+}
+
+// V run -> bf16x8 (a V^T operand); only the first nv of the 8 tokens are
+// keys, the rest become +0.
+__device__ __forceinline__ bf16x8 v8_to_bf16(uint4 w, int nv) { return __builtin_bit_cast(bf16x8, v8_keep(w, nv)); }
+__device__ __forceinline__ bf16x8 v8_to_bf16(uint2 w, int nv) {
+  w = v8_keep(w, nv);
+  const bf16x2 a = fp8x2_to_bf16(w.x, false), b = fp8x2_to_bf16(w.x, true);
+  const bf16x2 c = fp8x2_to_bf16(w.y, false), d = fp8x2_to_bf16(w.y, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Operand addressing in the page layout for the key-to-slot mapping of
+// arith.hpp.  K operand of score block sb, k-step ks, lane (r, g): page block
+// 2*(sb/2) + r/8 of the tile, token k_token(sb, r), chunk 4*ks + g.  V^T
+// operand of dim block mb, k-step ks2, lane (r, g): page block 2*ks2 + g/2,
+// dim 16*mb + r, tokens 8*(g%2) .. 8*(g%2) + 7.
+__device__ __forceinline__ int k_block(int sb, int r) { return 2 * (sb >> 1) + (r >> 3); }
+__device__ __forceinline__ int k_token(int sb, int r) { return 8 * ((r >> 2) & 1) + 4 * (sb & 1) + (r & 3); }
+__device__ __forceinline__ int v_block(int ks2, int g) { return 2 * ks2 + (g >> 1); }
+// Byte offset, inside one (page, kv head) block, of a lane's K chunk and of
+// its V run.
+template <int D, bool FP8>
+__device__ __forceinline__ uint32_t k_frag_off(int sb, int ks, int r, int g) {
+  return (uint32_t)((((4 * ks + g) * 16 + k_token(sb, r)) * 8) * Raw<FP8>::kElemBytes);
+}
+template <int D, bool FP8>
+__device__ __forceinline__ uint32_t v_frag_off(int mb, int r, int g) {
+  return (uint32_t)((((16 * mb + r) * 16) + 8 * (g & 1)) * Raw<FP8>::kElemBytes);
 }
 
 // Element offsets inside a page pool.

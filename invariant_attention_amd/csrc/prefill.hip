@@ -20,14 +20,16 @@
 // (global_load_lds, 1 KiB runs of K and V), with a zero fill of the keys past
 // the sequence end only in a tile that has them; e4m3 pages go through
 // registers, where they are zero filled and converted to bf16 (exactly).
-// K keeps the pages' own layout; V is regrouped by key pair:
-//   LDS K: [4 blocks][D/8 chunks][16 tokens] x 16 B
-//   LDS V: [2 block pairs][D/16 dim groups][2 blocks][16 dims][2 halves] x 16 B
-// (8 tokens per half), so the two page blocks of a key pair sit 512 bytes
-// apart for each dim, and in V the two halves of a dim row trade places when
-// bit 3 of the dim is set, so a wave's 8-byte fragment reads hit 64 distinct
-// banks.  A K operand fragment is one 16-byte LDS read; a V fragment is two
-// 8-byte reads 512 bytes apart (tokens 4g..4g+3 of the two page blocks).
+// K keeps the pages' own layout; V is staged in operand order:
+//   LDS K: [4 blocks][D/8 chunks][16 positions] x 16 B, token t of an odd
+//          page block at position t ^ 4
+//   LDS V: [2 k-steps][D/16 dim blocks][64 lanes] x 16 B, lane 16 g + r
+//          holding dim 16 mb + r, tokens 8 (g % 2) .. + 7 of page block
+//          2 ks2 + g / 2 (its V^T operand of the value product)
+// Every operand fragment is one 16-byte LDS read per lane.  A K read takes
+// keys of two page blocks (arith.hpp's key-to-slot mapping); the swap of
+// 64-byte quarters in odd page blocks puts them on disjoint banks.  A V read
+// is 1 KiB in lane order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,23 +58,21 @@ constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
 
-// LDS position of V half `half` of dim `dim` in a page block's copy: halves
-// swap when bit 3 of the dim is set (and the map is its own inverse).
-__device__ __forceinline__ int v_half_pos(int dim, int half) { return half ^ ((dim >> 3) & 1); }
+// LDS position of token t in a page block's K chunk row: quarters swap in
+// odd blocks (the map is its own inverse).
+__device__ __forceinline__ int k_pos(int blk, int t) { return t ^ ((blk & 1) << 2); }
 
-// The page block, dim and half held by 16-byte unit c of a tile's LDS V.
-// The V region is D/8 runs of 1 KiB, run (k, m) = (c / 64) for key pair k
-// (page blocks 2k, 2k+1) and dims 16m..16m+15: its first 512 bytes hold those
-// dims of block 2k, the next 512 the same dims of block 2k+1, each dim as its
-// two 8-token halves (placed by v_half_pos).  A V operand fragment (4 tokens
-// of blocks 2k and 2k+1 for one dim) is then two 8-byte reads 512 bytes apart,
-// which one paired LDS read returns in operand order.
-template <int D>
-__device__ __forceinline__ void v_unit(int c, int& blk, int& dim, int& half) {
+// The page block, and the byte offset of the V run inside its (page, kv head)
+// block, held by 16-byte unit c of a tile's LDS V (unit c = run c / 64 =
+// (ks2, mb), lane c % 64 of that run's operand).
+template <int D, bool FP8>
+__device__ __forceinline__ void v_unit(int c, int& blk, uint32_t& off, int& first_tok) {
   const int run = c >> 6, l = c & 63;
-  blk = 2 * (run / (D / 16)) + (l >> 5);
-  dim = 16 * (run % (D / 16)) + ((l & 31) >> 1);
-  half = v_half_pos(dim, l & 1);
+  const int ks2 = run / (D / 16), mb = run % (D / 16);
+  const int r = l & 15, g = l >> 4;
+  blk = v_block(ks2, g);
+  off = v_frag_off<D, FP8>(mb, r, g);
+  first_tok = 8 * (g & 1);
 }
 
 // Staging registers of one thread for one tile (e4m3 pages).
@@ -89,7 +89,7 @@ struct Stage {
   static_assert(kKUnits % 64 == 0 && kVUnits % kPrefillThreads == 0, "tile must divide over the waves");
   uint4 k[kKPer];
   int knv[kKPer];                  // keys in the unit's page block
-  typename Raw<FP8>::V v[kVPer][2];
+  typename Raw<FP8>::V8 v[kVPer];
   int vnv[kVPer];                  // keys among the unit's 8 tokens
 };
 
@@ -124,14 +124,12 @@ __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc,
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    int blk, dim, half;
-    v_unit<D>(c, blk, dim, half);
-    st.vnv[i] = select4(blk, tp.valid) - 8 * half;
+    int blk, first;
+    uint32_t off;
+    v_unit<D, FP8>(c, blk, off, first);
+    st.vnv[i] = select4(blk, tp.valid) - first;
     const uint8_t* base = vc + ((size_t)select4(blk, tp.page) * Hkv + kvh) * kHeadBytes;
-#pragma unroll
-    for (int q4 = 0; q4 < 2; ++q4)
-      st.v[i][q4] =
-          *reinterpret_cast<const typename Raw<FP8>::V*>(base + (uint32_t)((dim * 16 + 8 * half + 4 * q4) * EB));
+    st.v[i] = *reinterpret_cast<const typename Raw<FP8>::V8*>(base + off);
   }
 }
 
@@ -159,20 +157,22 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
     uint4 w = st.k[i];
     if constexpr (!FP8) {
       // unit u = chunk u / 16, token u % 16: 8 dims of one token
-      const bool keep = (u & 15) < st.knv[i];
+      const int tok = u & 15;
+      const bool keep = tok < st.knv[i];
       w.x = keep ? w.x : 0u;
       w.y = keep ? w.y : 0u;
       w.z = keep ? w.z : 0u;
       w.w = keep ? w.w : 0u;
-      *reinterpret_cast<uint4*>(lds + (size_t)c * 16) = w;
+      *reinterpret_cast<uint4*>(lds + ((size_t)(blk * (D / 8) + (u >> 4)) * 16 + k_pos(blk, tok)) * 16) = w;
     } else {
-      // unit u = chunk u / 8, tokens 2 (u % 8) and +1: 8 codes each
+      // unit u = chunk u / 8, tokens 2 (u % 8) and +1: 8 codes each (their
+      // positions stay adjacent under k_pos)
       const int chunk = u >> 3, tok = 2 * (u & 7);
       const bool k0 = tok < st.knv[i], k1 = tok + 1 < st.knv[i];
       uint2 a1, b1;
       const uint2 a0 = fp8x8_to_bf16(k0 ? w.x : 0u, k0 ? w.y : 0u, &a1);
       const uint2 b0 = fp8x8_to_bf16(k1 ? w.z : 0u, k1 ? w.w : 0u, &b1);
-      uint8_t* dst = lds + ((size_t)(blk * (D / 8) + chunk) * 16 + tok) * 16;
+      uint8_t* dst = lds + ((size_t)(blk * (D / 8) + chunk) * 16 + k_pos(blk, tok)) * 16;
       *reinterpret_cast<uint4*>(dst) = make_uint4(a0.x, a0.y, a1.x, a1.y);
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(b0.x, b0.y, b1.x, b1.y);
     }
@@ -180,19 +180,18 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
 #pragma unroll
   for (int i = 0; i < S::kVPer; ++i) {
     const int c = tid + kPrefillThreads * i;
-    const bf16x4 lo = v_to_bf16(st.v[i][0], st.vnv[i]);
-    const bf16x4 hi = v_to_bf16(st.v[i][1], st.vnv[i] - 4);
-    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
-    *reinterpret_cast<uint4*>(lds + kKBytes + (size_t)c * 16) = make_uint4(l.x, l.y, h.x, h.y);
+    *reinterpret_cast<bf16x8*>(lds + kKBytes + (size_t)c * 16) = v8_to_bf16(st.v[i], st.vnv[i]);
   }
 }
 
 // ---- bf16 tiles: direct global -> LDS loads (global_load_lds) --------------
 // The data moves from the pages to LDS without passing through registers.
 // Each instruction of a wave fills a contiguous 1 KiB LDS run, 16 bytes per
-// lane in lane order.  A page block's K or V (D x 16 values) is contiguous in
-// its page, so a tile's K is 4 blocks x D/32 such copies; a V copy fills one
-// run of the V region, each lane fetching the 16 bytes v_unit assigns it.
+// lane in lane order, each lane from an address of its own.  A page block's
+// K (D x 16 values) is contiguous in its page, so a tile's K is 4 blocks x
+// D/32 copies of 4 chunk rows (the lanes of an odd block fetch their row's
+// tokens in k_pos order); a V copy fills one operand run of the V region,
+// each lane fetching the 16 bytes v_unit assigns it.
 template <int D>
 __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
                                              int kvh, int Hkv, int w, int lane) {
@@ -201,47 +200,40 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
   constexpr int kKBytes = kTileKeys * D * 2;
   static_assert(kChunks % kPrefillWaves == 0, "chunks must divide over waves");
   auto head = [&](const uint8_t* pool, int pg) { return pool + ((size_t)pg * Hkv + kvh) * kHeadBytes; };
+  const int kl = (lane & ~15) | k_pos(1, lane & 15);  // the source position of an odd block's lane
 #pragma unroll
   for (int i = 0; i < kChunks / kPrefillWaves; ++i) {
     const int ch = i * kPrefillWaves + w;  // wave-uniform
     const int blk = ch / (kChunks / 4), part = ch % (kChunks / 4);
     const int pg = blk == 0 ? tp.page[0] : (blk == 1 ? tp.page[1] : (blk == 2 ? tp.page[2] : tp.page[3]));
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(kc, pg) + part * 1024 + lane * 16),
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(kc, pg) + part * 1024 + ((blk & 1) ? kl : lane) * 16),
                                      (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
-    // V: run ch; the lane's unit comes from a block that depends on the lane.
-    int vb, vd, vh;
-    v_unit<D>(ch * 64 + lane, vb, vd, vh);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, select4(vb, tp.page)) + vd * 32 + vh * 16),
+    // V: run ch; the lane's run lies in page block 2 ks2 + (lane / 32).
+    int vb, first;
+    uint32_t off;
+    v_unit<D, false>(ch * 64 + lane, vb, off, first);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, select4(vb, tp.page)) + off),
                                      (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
   }
 }
 
-// Zero fills the K and V of tokens past each block's key count in a landed
-// tile (only tiles that reach past the sequence end, or hold an invalid page),
-// as the register path does.
+// Zero fills the V of tokens past each block's key count in a landed tile
+// (only tiles that reach past the sequence end, or hold an invalid page).
+// Their K needs no fill: a key's score column depends only on its own K row,
+// and a masked score is replaced by the mask, never used.
 template <int D>
 __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp, int tid) {
   constexpr int kKBytes = kTileKeys * D * 2;
-  constexpr int kKUnits = kKBytes / 16;
   constexpr int kVUnits = 4 * D * 2;
-  static_assert(kKUnits % kPrefillThreads == 0, "K units must divide over the threads");
-#pragma unroll
-  for (int i = 0; i < kKUnits / kPrefillThreads; ++i) {
-    const int c = tid + kPrefillThreads * i;
-    // unit c = block c / (units per block), chunk, token c % 16
-    if ((c & 15) >= select4(c / (kKUnits / 4), tp.valid))
-      *reinterpret_cast<uint4*>(slot + (size_t)c * 16) = make_uint4(0u, 0u, 0u, 0u);
-  }
+  static_assert(kVUnits % kPrefillThreads == 0, "V units must divide over the threads");
 #pragma unroll
   for (int i = 0; i < kVUnits / kPrefillThreads; ++i) {
     const int c = tid + kPrefillThreads * i;
-    int blk, dim, half;
-    v_unit<D>(c, blk, dim, half);
-    const int nv = select4(blk, tp.valid) - 8 * half;
+    int blk, first;
+    uint32_t off;
+    v_unit<D, false>(c, blk, off, first);
     uint4* p = reinterpret_cast<uint4*>(slot + kKBytes + (size_t)c * 16);
-    const uint4 v = *p;
-    const uint2 lo = v_keep(make_uint2(v.x, v.y), nv), hi = v_keep(make_uint2(v.z, v.w), nv - 4);
-    *p = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    *p = v8_keep(*p, select4(blk, tp.valid) - first);
   }
 }
 
@@ -249,28 +241,25 @@ __device__ __forceinline__ bool tile_partial(const TilePages& tp) {
   return (tp.valid[0] & tp.valid[1] & tp.valid[2] & tp.valid[3]) != 16;
 }
 
-// Operand fragments of one tile from LDS.
+// Operand fragments of one tile from LDS: the K of score block sb (the key
+// of MFMA row r lies in page block k_block(sb, r)), and the V^T runs of dim
+// block mb (lane order).
 template <int D>
-__device__ __forceinline__ void lds_k_block(const uint8_t* lds, int blk, int r, int g, bf16x8 (&kf)[D / 32]) {
+__device__ __forceinline__ void lds_k_block(const uint8_t* lds, int sb, int r, int g, bf16x8 (&kf)[D / 32]) {
+  const int blk = k_block(sb, r);
+  const int pos = k_pos(blk, k_token(sb, r));
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     kf[ks] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + r) * 16));
+        bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + pos) * 16));
 }
-// V^T fragment of dim block mb for key half ks2: tokens 4g..4g+3 of page
-// blocks 2 ks2 and 2 ks2 + 1 for dim 16 mb + r (8 bytes from each, 512 bytes
-// apart in run (ks2, mb)).
 template <int D>
 __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, int g, bf16x8 (&vf)[2]) {
   constexpr int kKBytes = kTileKeys * D * 2;
-  const int dim = 16 * mb + r;
-  const uint8_t* base = lds + kKBytes + mb * 1024 + r * 32 + v_half_pos(dim, g >> 1) * 16 + 8 * (g & 1);
 #pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(base + ks2 * (D / 16) * 1024);
-    const uint2 hi = *reinterpret_cast<const uint2*>(base + ks2 * (D / 16) * 1024 + 512);
-    vf[ks2] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-  }
+  for (int ks2 = 0; ks2 < 2; ++ks2)
+    vf[ks2] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + (ks2 * (D / 16) + mb) * 1024 + (16 * g + r) * 16));
 }
 
 // Scores of one tile for the wave's rows, from the LDS copy of its K.
