@@ -107,6 +107,21 @@ typedef enum { IA_SPLIT_FIXED = 0, IA_SPLIT_BY_COUNT = 1 } ia_split_policy;
  *     otherwise (measured: outside that range SPLIT is faster). */
 typedef enum { IA_DECODE_AUTO = 0, IA_DECODE_SPLIT = 1, IA_DECODE_WIDE = 2, IA_DECODE_SPREAD = 3 } ia_decode_kernel;
 
+/* Cache policy of the decode split kernel's K/V page loads.  It changes only
+ * where bytes are cached, never a value or an order, so it is free to differ
+ * between calls.
+ *   IA_KV_HINT_STREAM loads every page nontemporally: each byte of a call is
+ *     read once, and streaming loads keep the caches from holding it (a plain
+ *     streaming read of HBM reaches ~7.0 TB/s this way against ~6.3 TB/s).
+ *   IA_KV_HINT_CACHED uses ordinary loads: for batches whose sequences share
+ *     pages (a common prefix), where the cached copy of a shared page serves
+ *     every sequence that reads it (measured: 128 sequences on a 16384-token
+ *     prefix decode at 12.1 TB/s of logical KV bytes cached, 6.8 streamed).
+ *   IA_KV_HINT_AUTO streams launches of at least 512 split units (measured
+ *     faster there on private pages) and caches smaller ones, whose working
+ *     set the caches can hold across calls. */
+typedef enum { IA_KV_HINT_AUTO = 0, IA_KV_HINT_STREAM = 1, IA_KV_HINT_CACHED = 2 } ia_kv_cache_hint;
+
 typedef struct {
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads, Hq / Hkv <= 16 */
   int32_t num_kv_heads;  /* Hkv */
@@ -125,6 +140,8 @@ typedef struct {
                              so decode = prefill and batch invariance hold as for
                              full attention. */
   int32_t decode_kernel;  /* ia_decode_kernel (0 = AUTO) */
+  int32_t kv_cache_hint;  /* ia_kv_cache_hint (0 = AUTO): how the decode split
+                             kernel's page loads use the caches; never a value */
 } ia_config;
 
 typedef struct ia_ctx ia_ctx;
@@ -391,8 +408,9 @@ ia_status ia_validate_attention_args(const int32_t* cu_q_lens, const int32_t* se
 
 /* ------------------------------------------------------------------------
  * Measurement reference (not part of the attention path): a kernel that does
- * nothing but stream `bytes` of device memory from buf (16-byte loads, 8 in
- * flight per thread, 8 workgroups of 256 threads per compute unit) and xor
+ * nothing but stream `bytes` of device memory from buf (16-byte nontemporal
+ * loads, 8 in flight per thread, one contiguous share per workgroup, 16
+ * workgroups of 256 threads per compute unit) and xor
  * them into one word per workgroup in sink, so that the decode kernel's
  * KV-read rate can be set beside what a plain read reaches on the same GPU.
  *   buf   dev, 16-byte aligned, bytes a multiple of 16

@@ -30,6 +30,9 @@ IA_DECODE_AUTO = 0
 IA_DECODE_SPLIT = 1
 IA_DECODE_WIDE = 2
 IA_DECODE_SPREAD = 3
+IA_KV_HINT_AUTO = 0
+IA_KV_HINT_STREAM = 1
+IA_KV_HINT_CACHED = 2
 IA_POOL_CONSTANT_HASH = 1
 
 EXPORTS = [
@@ -54,7 +57,7 @@ class ia_config(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("split_policy", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
-        ("decode_kernel", ctypes.c_int32),
+        ("decode_kernel", ctypes.c_int32), ("kv_cache_hint", ctypes.c_int32),
     ]
 
 
@@ -157,10 +160,11 @@ def ia_create(cfg: ia_config) -> ctypes.c_void_p:
 
 def make_config(Hq: int, Hkv: int, d: int, *, page_size: int = 16, split_tokens: int = 2048,
                 kv_dtype: int = IA_KV_BF16, split_policy: int = IA_SPLIT_FIXED, sm_scale: float | None = None,
-                sliding_window: int = 0, decode_kernel: int = IA_DECODE_AUTO) -> ia_config:
+                sliding_window: int = 0, decode_kernel: int = IA_DECODE_AUTO,
+                kv_cache_hint: int = IA_KV_HINT_AUTO) -> ia_config:
     scale = float(1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
     return ia_config(Hq, Hkv, d, page_size, split_tokens, kv_dtype, split_policy, scale, sliding_window,
-                     decode_kernel)
+                     decode_kernel, kv_cache_hint)
 
 
 def ia_last_error() -> str:

@@ -66,6 +66,10 @@ int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len)
 // speed only.  Its score buffer holds one slot per (unit, tile).
 constexpr int64_t kSpreadMaxUnits = 64;        // IA_DECODE_AUTO: at most this many split units
 constexpr int64_t kSpreadMaxSlots = 1 << 15;   // slots: <= 128 MiB of scores at 16 rows
+// IA_KV_HINT_AUTO: nontemporal page loads for launches of at least this many
+// split units (measured faster from about 700 units up on private pages, and
+// slower at 340 and below).
+constexpr int64_t kStreamMinUnits = 512;
 
 // Tiles of the longest split a launch can have: the fixed split, or the
 // split-by-count length for the longest sequence.
@@ -204,6 +208,9 @@ ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
   if (c.decode_kernel != IA_DECODE_AUTO && c.decode_kernel != IA_DECODE_SPLIT && c.decode_kernel != IA_DECODE_WIDE &&
       c.decode_kernel != IA_DECODE_SPREAD)
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown decode_kernel %d", c.decode_kernel);
+  if (c.kv_cache_hint != IA_KV_HINT_AUTO && c.kv_cache_hint != IA_KV_HINT_STREAM &&
+      c.kv_cache_hint != IA_KV_HINT_CACHED)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown kv_cache_hint %d", c.kv_cache_hint);
   ia_ctx* ctx = new (std::nothrow) ia_ctx;
   if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
   ctx->cfg = c;
@@ -323,6 +330,11 @@ ia_status ia_paged_attn_decode(const ia_ctx* ctx, const void* q, const void* k_c
   a.window = ctx->cfg.sliding_window;
   a.kernel = kernel;
   a.tps = (int)decode_split_tiles(ctx, B, max_seq_len);
+  {
+    const int64_t units = (int64_t)B * ctx->cfg.num_kv_heads * ms;
+    const int hint = ctx->cfg.kv_cache_hint;
+    a.nt = hint == IA_KV_HINT_STREAM || (hint == IA_KV_HINT_AUTO && units >= kStreamMinUnits);
+  }
   return hip_status(ia::launch_decode(ctx->cfg.head_dim, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, a,
                                       static_cast<hipStream_t>(stream)),
                     "decode launch");

@@ -11,7 +11,8 @@
 // prefill's at the same position; splitting the blocks over waves only
 // changes where each operation runs.  Each wave loads exactly the operand
 // fragments it consumes, straight from the pages into registers, one tile
-// ahead of the compute.
+// ahead of the compute; nontemporal loads when the host asks for them (each
+// byte is read once per call; see ia_config.kv_cache_hint).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,10 +48,11 @@ struct DecodeFrags {
   int valid[4];
 };
 
-// Loads the fragments of the tile at t0 given its 4 block-table entries.
-// Addresses are a wave-uniform page base plus a 32-bit per-lane offset that
-// is the same for every tile.
-template <int D, bool FP8>
+// Loads the fragments of the tile at t0 given its 4 block-table entries
+// (nontemporal loads when NT).  Addresses are a page base chosen per lane
+// among two pages plus a 32-bit per-lane offset that is the same for every
+// tile.
+template <int D, bool FP8, bool NT>
 __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const uint8_t* kc, const uint8_t* vc,
                                                   const int4& e, int t0, int n, int num_pages, int kvh, int Hkv,
                                                   int w, int r, int g) {
@@ -63,16 +65,14 @@ __device__ __forceinline__ void load_decode_frags(DecodeFrags<D, FP8>& f, const 
   const int kpb = (w >> 1) == 0 ? tp.page[1] : tp.page[3];
   const uint8_t* kp = kc + ((size_t)((r >> 3) ? kpb : kpa) * Hkv + kvh) * kHeadBytes;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    f.k[ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(kp + k_frag_off<D, FP8>(w, ks, r, g));
+  for (int ks = 0; ks < D / 32; ++ks) load_page<NT>(kp + k_frag_off<D, FP8>(w, ks, r, g), f.k[ks]);
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
     // The lane's V run lies in page block 2 ks2 + g / 2.
     const int pg = (g >> 1) ? tp.page[2 * ks2 + 1] : tp.page[2 * ks2];
     const uint8_t* vp = vc + ((size_t)pg * Hkv + kvh) * kHeadBytes;
 #pragma unroll
-    for (int mbi = 0; mbi < MB; ++mbi)
-      f.v[mbi][ks2] = *reinterpret_cast<const typename Raw<FP8>::V8*>(vp + v_frag_off<D, FP8>(w * MB + mbi, r, g));
+    for (int mbi = 0; mbi < MB; ++mbi) load_page<NT>(vp + v_frag_off<D, FP8>(w * MB + mbi, r, g), f.v[mbi][ks2]);
   }
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) f.valid[blk] = tp.valid[blk];
@@ -127,7 +127,7 @@ __device__ __forceinline__ int first_key(int p, int window) {
   return p - window + 1 > 0 ? p - window + 1 : 0;
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
   constexpr int MB = D / 64;
   __shared__ f32x4 xs[2][4][64];  // score exchange, double buffered by tile parity
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
       const int4 e = *reinterpret_cast<const int4*>(&bt_lds[4 * lt]);
       const int4 eu = make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
                                 __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
-      load_decode_frags<D, FP8>(f, kc, vc, eu, k_begin + kTileKeys * (w0 + lt), n, np, kvh, a.Hkv, w, r, g);
+      load_decode_frags<D, FP8, NT>(f, kc, vc, eu, k_begin + kTileKeys * (w0 + lt), n, np, kvh, a.Hkv, w, r, g);
     };
     load(fa, 0);
     for (int lt = 0; lt < wn; lt += 2) {
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         const int pg = (g >> 1) ? tp.page[2 * ks2 + 1] : tp.page[2 * ks2];
         const uint8_t* base = vc + ((size_t)pg * a.Hkv + kvh) * kHeadBytes;
-        vr[i].v[ks2] = *reinterpret_cast<const typename Raw<FP8>::V8*>(base + v_frag_off<D, FP8>(wd, r, g));
+        load_page<false>(base + v_frag_off<D, FP8>(wd, r, g), vr[i].v[ks2]);
       }
     }
   };
@@ -358,8 +358,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
       const int pg = (r >> 3) ? kp.page[2 * (sb >> 1) + 1] : kp.page[2 * (sb >> 1)];
       const uint8_t* base = kc + ((size_t)pg * a.Hkv + kvh) * kHeadBytes;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        kr.k[sb][ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(base + k_frag_off<D, FP8>(sb, ks, r, g));
+      for (int ks = 0; ks < D / 32; ++ks) load_page<false>(base + k_frag_off<D, FP8>(sb, ks, r, g), kr.k[sb][ks]);
     }
   };
 
@@ -586,8 +585,7 @@ __global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
     const int pg = (r >> 3) ? tp.page[2 * (sb >> 1) + 1] : tp.page[2 * (sb >> 1)];
     const uint8_t* base = a.k_cache + ((size_t)pg * a.Hkv + un.kvh) * kHeadBytes;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      kr[sb][ks] = *reinterpret_cast<const typename Raw<FP8>::K*>(base + k_frag_off<D, FP8>(sb, ks, r, g));
+    for (int ks = 0; ks < D / 32; ++ks) load_page<false>(base + k_frag_off<D, FP8>(sb, ks, r, g), kr[sb][ks]);
   }
   f32x4 sc[4];
 #pragma unroll
@@ -1003,7 +1001,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     } else {
       sa.order = nullptr;
     }
-    hipLaunchKernelGGL((decode_split_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, sa);
+    if (a.nt)
+      hipLaunchKernelGGL((decode_split_kernel<D, FP8, true>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, sa);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<D, FP8, false>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st,
+                         sa);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -43,6 +43,7 @@ struct DecodeArgs {
   int kernel;                  // 0: decode_split_kernel, 1: decode_wide_kernel, 2: the spread kernels
                                // (score, weight, value); all give the same bits
   int tps;                     // spread: tile slots per split (the longest split of the launch, in tiles)
+  int nt;                      // split kernel: nontemporal page loads (caching only, never values)
 };
 
 struct PrefillArgs {

@@ -52,6 +52,30 @@ __device__ __forceinline__ typename Raw<FP8>::V load_v_raw(const uint8_t* base, 
   return *reinterpret_cast<const typename Raw<FP8>::V*>(base + elem * Raw<FP8>::kElemBytes);
 }
 
+// Loads of page data that a kernel reads exactly once (the decode kernels
+// stream each split's K and V): nontemporal, so the caches treat them as
+// streaming data.  The hint changes where the bytes are cached, never their
+// values.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load_stream(const uint8_t* p, uint4& out) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  out = make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void load_stream(const uint8_t* p, uint2& out) {
+  const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  out = make_uint2(v.x, v.y);
+}
+
+// A page load: nontemporal when NT, else an ordinary (cached) load.
+template <bool NT, class T>
+__device__ __forceinline__ void load_page(const uint8_t* p, T& out) {
+  if constexpr (NT)
+    load_stream(p, out);
+  else
+    out = *reinterpret_cast<const T*>(p);
+}
+
 // K chunk -> bf16x8; `keep` false gives +0 (a token that is not a key).
 __device__ __forceinline__ bf16x8 k_to_bf16(uint4 w, bool keep) {
   w.x = keep ? w.x : 0u;

@@ -21,12 +21,13 @@ def within_tolerance(gpu: torch.Tensor, ref: np.ndarray):
 
 
 def make_ctx(shape: wl.AttnShape, fp8=False, by_count=False, split_tokens=None, window=0,
-             decode_kernel=ia.IA_DECODE_AUTO):
+             decode_kernel=ia.IA_DECODE_AUTO, kv_cache_hint=ia.IA_KV_HINT_AUTO):
     cfg = ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P,
                          split_tokens=shape.S if split_tokens is None else split_tokens,
                          kv_dtype=ia.IA_KV_FP8_E4M3 if fp8 else ia.IA_KV_BF16,
                          split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
-                         sm_scale=shape.scale, sliding_window=window, decode_kernel=decode_kernel)
+                         sm_scale=shape.scale, sliding_window=window, decode_kernel=decode_kernel,
+                         kv_cache_hint=kv_cache_hint)
     return ia.Context(cfg)
 
 

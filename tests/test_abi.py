@@ -48,6 +48,7 @@ def test_version_and_clean_error_state():
     (dict(Hq=32, Hkv=8, d=128, sm_scale=-1.0), "sm_scale"),
     (dict(Hq=32, Hkv=8, d=128, sliding_window=-1), "sliding_window"),
     (dict(Hq=32, Hkv=8, d=128, decode_kernel=4), "decode_kernel"),
+    (dict(Hq=32, Hkv=8, d=128, kv_cache_hint=3), "kv_cache_hint"),
 ])
 def test_unsupported_configs_are_rejected(kw, msg):
     Hq, Hkv, d = kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d")

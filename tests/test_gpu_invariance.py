@@ -256,3 +256,22 @@ def test_batches_above_the_order_limit_keep_their_bits():
     assert _eq(w.decode_rows(idx), full[idx])
     for b in (0, 549, 1099):
         assert _eq(w.decode_rows([b]), full[[b]]), f"row {b}"
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_cache_hint_changes_no_bit(fp8):
+    """ia_config.kv_cache_hint picks nontemporal or cached page loads: the same bits either way, on
+    a launch the automatic rule streams (>= 512 split units) and on a small one."""
+    shape = wl.LLAMA3_8B
+    lens = wl.uniform_lens(41, 80, 512, 8192)  # 80 x 8 kv heads x up to 4 splits
+    scales = wl.fp8_scales(2, shape.Hkv, power_of_two=False) if fp8 else None
+    w = World(shape, lens, fp8=fp8, scales=scales)
+    outs = {}
+    for name, hint in (("auto", ia.IA_KV_HINT_AUTO), ("stream", ia.IA_KV_HINT_STREAM),
+                       ("cached", ia.IA_KV_HINT_CACHED)):
+        w.ctx = gs.make_ctx(shape, fp8=fp8, kv_cache_hint=hint)
+        outs[name] = (w.decode_rows(), w.decode_rows([0, 5]))
+    for name in ("stream", "cached"):
+        assert _eq(outs[name][0], outs["auto"][0]), name
+        assert _eq(outs[name][1], outs["auto"][1]), name
+    assert _eq(outs["auto"][1], outs["auto"][0][[0, 5]])
