@@ -37,44 +37,96 @@ __device__ __forceinline__ uint8_t quant_e4m3(float x) {
   return (uint8_t)(sign | (uint32_t)((e + 7) << 3) | q);
 }
 
+// One workgroup per (group of 16 consecutive input rows, kv head); thread
+// (r, c) holds row r's 8-dim chunk c of K and of V.  When the group's 16
+// slots are one whole page in order (slot[t0 + i] = 16 pg + i -- the usual
+// case when a prompt's rows are appended), the group is transposed through
+// LDS and written as whole runs: K as 16-byte units in token order inside
+// each chunk row, V as 8-token runs of each dim row.  Otherwise every row is
+// written to its own slot.  Either way each stored value is the row's value
+// (bf16) or its code (e4m3) at its slot.
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void kv_append_kernel(const __bf16* __restrict__ k_new,
-                                                        const __bf16* __restrict__ v_new,
-                                                        const int64_t* __restrict__ slots, int T, uint8_t* kc,
-                                                        uint8_t* vc, int num_pages, int Hkv,
-                                                        const float* __restrict__ k_scale,
-                                                        const float* __restrict__ v_scale) {
+__device__ __forceinline__ void store_k_unit(uint8_t* kc, size_t head, int c, int tok, uint4 w, float ks) {
   constexpr int kChunks = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)T * Hkv * kChunks;
-  if (idx >= total) return;
-  const int c = (int)(idx % kChunks);
-  const int h = (int)((idx / kChunks) % Hkv);
-  const int t = (int)(idx / kChunks / Hkv);
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= (int64_t)num_pages * 16) return;
-  const int64_t pg = slot >> 4;
-  const int tok = (int)(slot & 15);
-  const size_t src = ((size_t)t * Hkv + h) * D + 8 * c;
-  const uint4 kw = *reinterpret_cast<const uint4*>(k_new + src);
-  const uint4 vw = *reinterpret_cast<const uint4*>(v_new + src);
-  const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kw);
-  const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vw);
-  const size_t head = (size_t)pg * Hkv + h;
-  const size_t ke = ((head * kChunks + c) * 16 + tok) * 8;
-  const size_t ve = (head * D + 8 * c) * 16 + tok;
+  const size_t ke = ((head * kChunks + c) * 16 + tok) * 8;  // element index
   if constexpr (FP8) {
-    const float ks = k_scale[h], vs = v_scale[h];
+    const bf16x8 x = __builtin_bit_cast(bf16x8, w);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= (uint32_t)quant_e4m3<D, FP8>((float)kv8[j] / ks) << (8 * j);
+    for (int j = 0; j < 4; ++j) lo |= (uint32_t)quant_e4m3<D, FP8>((float)x[j] / ks) << (8 * j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= (uint32_t)quant_e4m3<D, FP8>((float)kv8[4 + j] / ks) << (8 * j);
+    for (int j = 0; j < 4; ++j) hi |= (uint32_t)quant_e4m3<D, FP8>((float)x[4 + j] / ks) << (8 * j);
     *reinterpret_cast<uint2*>(kc + ke) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<uint4*>(kc + ke * 2) = w;
+  }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(16 * (D / 8)) void kv_append_kernel(const __bf16* __restrict__ k_new,
+                                                                 const __bf16* __restrict__ v_new,
+                                                                 const int64_t* __restrict__ slots, int T,
+                                                                 uint8_t* kc, uint8_t* vc, int num_pages, int Hkv,
+                                                                 const float* __restrict__ k_scale,
+                                                                 const float* __restrict__ v_scale) {
+  constexpr int kChunks = D / 8;
+  __shared__ uint4 kl[16 * kChunks];  // [row][chunk]
+  __shared__ uint4 vl[16 * kChunks];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % Hkv;
+  const int t0 = (blockIdx.x / Hkv) * 16;
+  const int r = tid / kChunks, c = tid % kChunks;
+  const int t = t0 + r;
+  const int64_t limit = (int64_t)num_pages * 16;
+  int64_t slot = -1;
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+  if (t < T) {
+    slot = slots[t];
+    const size_t src = ((size_t)t * Hkv + h) * D + 8 * c;
+    kw = *reinterpret_cast<const uint4*>(k_new + src);
+    vw = *reinterpret_cast<const uint4*>(v_new + src);
+  }
+  const float ks = FP8 ? k_scale[h] : 1.f, vs = FP8 ? v_scale[h] : 1.f;
+  const int64_t s0 = t0 < T ? slots[t0] : -1;
+  const bool whole = t < T && s0 >= 0 && (s0 & 15) == 0 && s0 + 15 < limit && slot == s0 + r;
+  if (__syncthreads_and(whole)) {
+    kl[tid] = kw;
+    vl[tid] = vw;
+    __syncthreads();
+    const size_t head = (size_t)(s0 >> 4) * Hkv + h;
+    // K: thread (c', tok) = (tid / 16, tid % 16) writes unit [tok][c'].
+    const int cw = tid >> 4, tok = tid & 15;
+    store_k_unit<D, FP8>(kc, head, cw, tok, kl[tok * kChunks + cw], ks);
+    // V: thread (dim, half) = (tid / 2, tid % 2) writes tokens 8 half .. + 7 of its dim row.
+    const int dim = tid >> 1, half = tid & 1;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(vl);
+    const size_t ve = (head * D + dim) * 16 + 8 * half;  // element index
+    if constexpr (FP8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lo |= (uint32_t)quant_e4m3<D, FP8>((float)vb[(8 * half + j) * D + dim] / vs) << (8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hi |= (uint32_t)quant_e4m3<D, FP8>((float)vb[(8 * half + 4 + j) * D + dim] / vs) << (8 * j);
+      *reinterpret_cast<uint2*>(vc + ve) = make_uint2(lo, hi);
+    } else {
+      bf16x8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = vb[(8 * half + j) * D + dim];
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(vc) + ve) = x;
+    }
+    return;
+  }
+  if (slot < 0 || slot >= limit) return;  // padding row, or no row
+  const size_t head = (size_t)(slot >> 4) * Hkv + h;
+  const int tok = (int)(slot & 15);
+  store_k_unit<D, FP8>(kc, head, c, tok, kw, ks);
+  const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vw);
+  const size_t ve = (head * D + 8 * c) * 16 + tok;
+  if constexpr (FP8) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) vc[ve + 16 * j] = quant_e4m3<D, FP8>((float)vv8[j] / vs);
   } else {
-    *reinterpret_cast<uint4*>(kc + ke * 2) = kw;
     __bf16* vb = reinterpret_cast<__bf16*>(vc);
 #pragma unroll
     for (int j = 0; j < 8; ++j) vb[ve + 16 * j] = vv8[j];
@@ -83,11 +135,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const __bf16* __restrict
 
 template <int D, bool FP8>
 static hipError_t launch_append_t(const AppendArgs& a, hipStream_t st) {
-  const int64_t total = (int64_t)a.T * a.Hkv * (D / 8);
-  if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL((kv_append_kernel<D, FP8>), dim3((unsigned)blocks), dim3(256), 0, st, a.k_new, a.v_new,
-                     a.slots, a.T, a.k_cache, a.v_cache, a.num_pages, a.Hkv, a.k_scale, a.v_scale);
+  if (a.T == 0) return hipSuccess;
+  const int64_t groups = ((int64_t)a.T + 15) / 16;
+  hipLaunchKernelGGL((kv_append_kernel<D, FP8>), dim3((unsigned)(groups * a.Hkv)), dim3(16 * (D / 8)), 0, st,
+                     a.k_new, a.v_new, a.slots, a.T, a.k_cache, a.v_cache, a.num_pages, a.Hkv, a.k_scale,
+                     a.v_scale);
   return hipGetLastError();
 }
 

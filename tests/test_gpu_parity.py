@@ -62,6 +62,43 @@ def test_kv_append_pages_bit_exact(shape, fp8):
     assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
 
 
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("shape", [wl.TINY, wl.LLAMA3_8B], ids=["tiny", "llama8b"])
+def test_kv_append_whole_page_groups_bit_exact(shape, fp8):
+    """Groups of 16 rows that fill one page in order take the transposed path; a run that starts
+    mid-page, a group with a padding row, a group whose slots skip a token and a ragged tail take
+    the per-row path.  Every page byte must equal the oracle's scatter."""
+    rng = np.random.default_rng(2)
+    num_pages = 64
+    P = shape.P
+    pages = rng.permutation(num_pages)
+    runs = [np.arange(pages[i] * P, pages[i] * P + P) for i in range(6)]          # whole pages in order
+    runs.append(np.arange(pages[6] * P + 3, pages[6] * P + P))                      # starts mid-page
+    grp = np.arange(pages[7] * P, pages[7] * P + P).copy()
+    grp[5] = -1                                                                     # a padding row
+    runs.append(grp)
+    skip = np.arange(pages[8] * P, pages[8] * P + P).copy()
+    skip[9] = pages[9] * P                                                          # one token elsewhere
+    runs.append(skip)
+    runs.append(np.arange(pages[10] * P, pages[10] * P + 16))                       # another whole page
+    runs.append(np.arange(pages[11] * P, pages[11] * P + 7))                        # ragged tail
+    slots = np.concatenate(runs).astype(np.int64)
+    T = len(slots)
+    k = wl.to_bf16(rng.standard_normal((T, shape.Hkv, shape.d)) * 3)
+    v = wl.to_bf16(rng.standard_normal((T, shape.Hkv, shape.d)) * 3)
+    scales = wl.fp8_scales(2, shape.Hkv, power_of_two=False) if fp8 else (None, None)
+    ctx = gs.make_ctx(shape, fp8=fp8)
+    dev = gs.DevicePages(shape, num_pages, fp8, *scales)
+    dev.append(ctx, k, v, slots)
+    torch.cuda.synchronize()
+    kc, vc = osd.host_pools(shape, num_pages, fp8)
+    oracle.kv_append(osd.bits16(k), osd.bits16(v), slots, kc, vc, Hkv=shape.Hkv, d=shape.d, P=shape.P,
+                     kv_fp8=fp8, k_scale=scales[0], v_scale=scales[1])
+    gk, gv = dev.host_bits()
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+
+
 # ------------------------------------------------------------------- decode
 
 DECODE_CASES = [
