@@ -137,54 +137,40 @@ def _pmc_mean(pmc_dir, kind, counter, kernel):
     return (float(np.mean(vals)) if vals else float("nan")), len(vals)
 
 
-def summarize_profile(trace_dir, pmc_dir):
-    """Writes the decode profile summary (rocprofv3 kernel-trace stats + calibrated FETCH/WRITE)."""
+SPLIT_KERNEL = "decode_split_kernel<128, false"  # bf16 pages, either load policy
+SHARED_PREFIX_PROFILE_MD = os.path.join(ROOT, "profiles", "decode_split_kernel_llama70b_shared_prefix.md")
+
+
+def _decode_profile_lines(trace_dir, pmc_dir, kind, alg, title, workload, bench_args, pmc_steps):
+    """Kernel-trace stats and calibrated FETCH/WRITE bytes of the decode split kernel for one workload.
+    Returns (markdown lines, HBM bytes read per launch, written per launch, mean ns per launch)."""
     stats = _csv_rows(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
-    split = [r for r in stats if "decode_split_kernel<128, false>" in r["Name"]]
+    split = [r for r in stats if SPLIT_KERNEL in r["Name"]]
     merge = [r for r in stats if "decode_merge_kernel<128, false>" in r["Name"]]
     order = [r for r in stats if "decode_order_kernel" in r["Name"]]
     avg_ns = float(split[0]["AverageNs"])
-
-    def pmc_mean(kind, counter, kernel):
-        return _pmc_mean(pmc_dir, kind, counter, kernel)
-
-    fetch_kib, nf = pmc_mean("decode", "FETCH_SIZE", "decode_split_kernel<128, false>")
-    write_kib, nw = pmc_mean("decode", "WRITE_SIZE", "decode_split_kernel<128, false>")
-    copy_fetch, _ = pmc_mean("copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
-    copy_write, _ = pmc_mean("copy", "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    fetch_kib, nf = _pmc_mean(pmc_dir, kind, "FETCH_SIZE", SPLIT_KERNEL)
+    write_kib, nw = _pmc_mean(pmc_dir, kind, "WRITE_SIZE", SPLIT_KERNEL)
+    copy_fetch, _ = _pmc_mean(pmc_dir, "copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    copy_write, _ = _pmc_mean(pmc_dir, "copy", "WRITE_SIZE", "__amd_rocclr_copyBuffer")
     f_scale = COPY_PROBE_BYTES / (copy_fetch * 1024)
     w_scale = COPY_PROBE_BYTES / (copy_write * 1024)
     fetch_b = fetch_kib * 1024 * f_scale
     write_b = write_kib * 1024 * w_scale
-    lens = wl.uniform_lens(SEED, 256, 512, 8192)
-    alg = int(sum(lens)) * 8 * 128 * 2 * 2
-    tr = int(round(fetch_b + write_b))
-    cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o decode -- "
-                 "python3 bench.py --decode-only --steps 10 --warmup 3 --no-cpu-baseline")
+    cmd_trace = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o {kind} -- "
+                 f"python3 bench.py {bench_args} --steps 10 --warmup 3 --no-cpu-baseline")
     cmd_pmc = ("rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- "
-               "python3 bench.py --decode-only --steps 3 --warmup 1 --no-cpu-baseline")
+               f"python3 bench.py {bench_args} --steps {pmc_steps} --warmup 1 --no-cpu-baseline")
     cmd_copy = "rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- python3 bench.py --copy-probe --steps 3"
-    lines = [
-        "# decode_split_kernel<128, bf16> -- Llama-3-8B-shaped decode, batch 256, contexts U[512, 8192]",
-        "",
-        "32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits, "
-        f"{int(sum(lens))} context tokens; algorithmic KV bytes per launch {alg} "
-        "(sum_b n_b x 8 heads x 128 dims x 2 tensors x 2 bytes).",
-        "",
-        "## Kernel trace (rocprofv3 --kernel-trace --stats)",
-        "",
-        f"    {cmd_trace}",
-        "",
-        "| kernel | calls | average ns | min ns | max ns |",
-        "|---|---|---|---|---|",
-    ]
+    lines = [f"# {title}", "", workload, "", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             f"    {cmd_trace}", "", "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in order + split + merge:
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
     lines += [
         "",
-        f"Achieved from the trace: {alg / avg_ns:.1f} GB/s = {alg / avg_ns / HBM_PEAK_GBS:.4f} of the 8 TB/s HBM peak "
-        "(split kernel alone; the dispatch-order kernel before it and the split merge after it add a few us "
-        "each per call).",
+        f"Achieved from the trace: {alg / avg_ns:.1f} GB/s of algorithmic KV bytes = "
+        f"{alg / avg_ns / HBM_PEAK_GBS:.4f} of the 8 TB/s HBM peak (split kernel alone; the dispatch-order "
+        "kernel before it and the split merge after it add a few us each per call).",
         "",
         "## HBM traffic (rocprofv3 --pmc, one counter per run)",
         "",
@@ -203,11 +189,13 @@ def summarize_profile(trace_dir, pmc_dir):
         f"| write scale | {w_scale:.4f} |",
         f"| HBM bytes read per launch | {fetch_b:.4e} |",
         f"| HBM bytes written per launch | {write_b:.4e} |",
-        f"| traffic / algorithmic bytes | {tr / alg:.4f} |",
+        f"| traffic / algorithmic bytes | {(fetch_b + write_b) / alg:.4f} |",
+        f"| DRAM-side rate (HBM bytes read / kernel time) | {fetch_b / avg_ns:.1f} GB/s = "
+        f"{fetch_b / avg_ns / HBM_PEAK_GBS:.4f} of peak |",
         "",
     ]
-    hit, nh = pmc_mean("decode", "TCC_HIT_sum", "decode_split_kernel<128, false>")
-    miss, _ = pmc_mean("decode", "TCC_MISS_sum", "decode_split_kernel<128, false>")
+    hit, nh = _pmc_mean(pmc_dir, kind, "TCC_HIT_sum", SPLIT_KERNEL)
+    miss, _ = _pmc_mean(pmc_dir, kind, "TCC_MISS_sum", SPLIT_KERNEL)
     if nh:
         lines += [
             "## L2 (rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum, one run)",
@@ -220,11 +208,27 @@ def summarize_profile(trace_dir, pmc_dir):
             f"| TCC_MISS_sum per dispatch | {miss:.4e} |",
             f"| L2 hit rate | {hit / (hit + miss):.4f} |",
             "",
-            "The K/V stream is read once and a wave's 16-byte lane loads coalesce into whole lines, so "
-            "nearly every L2 request misses; the few hits are block-table, query and split-partial reads.",
-            "",
         ]
+    return lines, fetch_b, write_b, avg_ns
+
+
+def summarize_profile(trace_dir, pmc_dir):
+    """Writes the headline decode profile summary (rocprofv3 kernel-trace stats + calibrated FETCH/WRITE)
+    and the traffic record the bench's roofline reads."""
+    lens = wl.uniform_lens(SEED, 256, 512, 8192)
+    alg = int(sum(lens)) * 8 * 128 * 2 * 2
+    lines, fetch_b, write_b, _ = _decode_profile_lines(
+        trace_dir, pmc_dir, "decode", alg,
+        "decode_split_kernel<128, bf16> -- Llama-3-8B-shaped decode, batch 256, contexts U[512, 8192]",
+        "32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits, "
+        f"{int(sum(lens))} context tokens; algorithmic KV bytes per launch {alg} "
+        "(sum_b n_b x 8 heads x 128 dims x 2 tensors x 2 bytes).  The launch has ~5.3k split units, so the "
+        "automatic cache hint streams its K/V loads (nontemporal).",
+        "--decode-only", 3)
+    tr = int(round(fetch_b + write_b))
     lines += [
+        "The K/V stream is read once; the few L2 hits are block-table, query and split-partial reads.",
+        "",
         f"traffic_record: source_sha={kernel_source_hash()} bytes_per_launch={tr} read={int(fetch_b)} "
         f"write={int(write_b)} algorithmic={alg}",
         "",
@@ -233,6 +237,55 @@ def summarize_profile(trace_dir, pmc_dir):
     with open(PROFILE_MD, "w") as f:
         f.write("\n".join(lines))
     print(PROFILE_MD)
+
+
+def _shared_prefix_lens():
+    rng = np.random.default_rng([SEED, 5])
+    return [16384 + int(x) for x in rng.integers(256, 4097, 128)]
+
+
+def summarize_shared_prefix_profile(trace_dir, pmc_dir):
+    """Writes the Llama-3.1-70B shared-prefix decode profile: logical KV bytes against the DRAM bytes
+    that FETCH_SIZE counts for the same launch."""
+    shape = wl.LLAMA31_70B
+    lens = _shared_prefix_lens()
+    alg = int(sum(lens)) * shape.Hkv * shape.d * 2 * 2
+    layout = wl.layout_pages(3, lens, shape.P, shared_prefix=16384, width=8192)
+    distinct = len(set(np.concatenate(layout.pages).tolist())) * shape.P * shape.Hkv * shape.d * 2 * 2
+    lines, fetch_b, write_b, avg_ns = _decode_profile_lines(
+        trace_dir, pmc_dir, "shared", alg,
+        "decode_split_kernel<128, bf16> -- Llama-3.1-70B-shaped decode, 128 sequences on a shared "
+        "16384-token prefix",
+        "64 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits; 128 sequences = "
+        "one 16384-token prefix held once in 1024 refcounted pages + private suffixes of 256-4096 tokens; "
+        f"block tables 8192 wide (131072 keys); IA_KV_HINT_CACHED.  Logical KV bytes per launch {alg} (what the "
+        f"128 sequences read); bytes of the distinct pages {distinct}.",
+        "--shared-prefix-only", 3)
+    lines += [
+        "## Logical against DRAM bytes",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| logical KV bytes per launch | {alg:.4e} |",
+        f"| distinct-page bytes | {distinct:.4e} |",
+        f"| bytes the L2s fetch from the fabric per launch (FETCH_SIZE, calibrated) | {fetch_b:.4e} |",
+        f"| fetched / distinct-page bytes | {fetch_b / distinct:.3f} |",
+        f"| fetched / logical bytes | {fetch_b / alg:.3f} |",
+        f"| logical rate | {alg / avg_ns:.1f} GB/s |",
+        f"| DRAM-side rate (fetched bytes / kernel time) | {fetch_b / avg_ns:.1f} GB/s = "
+        f"{fetch_b / avg_ns / HBM_PEAK_GBS:.4f} of peak |",
+        "",
+        "FETCH_SIZE counts what the L2s read from the data fabric, which the 256 MB last-level cache (MALL) "
+        "serves before HBM, so the fetched bytes bound the HBM bytes from above.  Each of the 8 XCDs has its "
+        "own L2, and sequences at different points of the prefix evict each other's lines from the 4 MB L2s, "
+        "so a shared page is fetched more than once per launch; the 64 MiB prefix itself fits the MALL.  The "
+        "logical rate (what the 128 sequences read) is above the HBM peak because most of the shared bytes "
+        "come from the caches.",
+        "",
+    ]
+    with open(SHARED_PREFIX_PROFILE_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(SHARED_PREFIX_PROFILE_MD)
 
 
 SPREAD_PROFILE_MD = os.path.join(ROOT, "profiles", "decode_spread_kernels_llama3-8b_b1.md")
@@ -1053,8 +1106,7 @@ def llama70_points(steps, warmup):
     sequence at 131072 keys.  Logical KV bytes (what every sequence reads) against the distinct pages'
     bytes; DRAM bytes of the same launch come from the profile's FETCH_SIZE counters."""
     shape = wl.LLAMA31_70B
-    rng = np.random.default_rng([SEED, 5])
-    lens = [16384 + int(x) for x in rng.integers(256, 4097, 128)]
+    lens = _shared_prefix_lens()
     out = {}
     for fp8 in (False, True):
         w = DecodeWorld(shape, lens, fp8=fp8, shared_prefix=16384, width=8192, gpu_values=True)
@@ -1182,6 +1234,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time the prefill workload only (for profilers)")
     ap.add_argument("--layer-only", action="store_true", help="time the layer operators only (for profilers)")
+    ap.add_argument("--shared-prefix-only", action="store_true",
+                    help="time the Llama-3.1-70B shared-prefix decode only (for profilers)")
+    ap.add_argument("--summarize-shared-prefix-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-spread-profile", metavar="TRACE_DIR")
@@ -1192,6 +1247,9 @@ def main():
         return
     if args.summarize_prefill_profile:
         summarize_prefill_profile(*args.summarize_prefill_profile)
+        return
+    if args.summarize_shared_prefix_profile:
+        summarize_shared_prefix_profile(*args.summarize_shared_prefix_profile)
         return
     if args.summarize_spread_profile:
         summarize_spread_profile(args.summarize_spread_profile)
@@ -1213,6 +1271,14 @@ def main():
         return
     if args.layer_only:
         print(json.dumps({"layer_ops": layer_ops(args.steps, args.warmup)}), flush=True)
+        return
+    if args.shared_prefix_only:
+        shape = wl.LLAMA31_70B
+        w = DecodeWorld(shape, _shared_prefix_lens(), shared_prefix=16384, width=8192, gpu_values=True)
+        ctx = make_ctx(shape, kv_cache_hint=ia.IA_KV_HINT_CACHED)
+        _, d_ms = time_steps(DecodeRunner(w, range(128), ctx), args.steps, args.warmup, with_append=False)
+        print(json.dumps({"shared_prefix_decode_ms": round(d_ms, 4),
+                          "logical_gbs": round(w.kv_bytes() / d_ms / 1e6, 1)}), flush=True)
         return
     shape = wl.LLAMA3_8B
     lens = wl.uniform_lens(SEED, args.batch, 512, 8192)

@@ -145,6 +145,32 @@ def test_qwen8b_prefix_cached_equals_recomputed():
     _check(cached[0][-16:], ref)
 
 
+def test_qwen8b_whole_prefill_8x4096_sampled_rows_match_oracle():
+    """The benchmark's prefill launch itself (8 prompts of 4096 tokens, Qwen3-8B shape, one call,
+    the bench's page layout): sampled rows of every prompt against the oracle -- the first rows,
+    the rows around the 64-key tile edges and the 2048-key split edge (2047 / 2048 / 2049), rows in
+    the middle of each split, and the last rows.  The oracle computes a row at position p from the
+    prompt's first p + 1 rows (what the row sees)."""
+    shape = wl.QWEN3_8B
+    n, B = 4096, 8
+    lens = [n] * B
+    seqs = wl.make_sequences(lens, first_sid=1000)
+    layout = wl.layout_pages(5, lens, shape.P)
+    ctx = gs.make_ctx(shape)
+    pages = gs.DevicePages(shape, layout.num_pages)
+    gs.fill_sequences(ctx, pages, seqs, layout, SEED)
+    q, cu = osd.queries(shape, seqs, SEED, lens)
+    out = gs.prefill(ctx, pages, q, cu, layout, lens)
+    positions = [0, 1, 15, 63, 64, 65, 1000, 2047, 2048, 2049, 3071, 4094, 4095]
+    rows, trunc = [], []
+    for b, sq in enumerate(seqs):
+        for p in sorted(set(positions[b % 2::2] + [2048, 4095])):  # alternate the sample between prompts
+            rows.append(b * n + p)
+            trunc.append(wl.Sequence(sq.sid, p + 1, sq.content[:(p + 1 + 15) // 16]))
+    ref = _oracle_rows(shape, trunc, [1] * len(trunc))
+    _check(out[rows], ref)
+
+
 def test_qwen8b_prefill_shuffled_pages():
     shape = wl.QWEN3_8B
     lens = [3000, 4096]
