@@ -41,11 +41,14 @@
  *    clamped or read as zeros) but the results are then unspecified.
  *
  * Page layout (per KV pool; element = bf16, or one e4m3 byte for fp8):
- *    K: [num_pages][num_kv_heads][head_dim/8][page_size][8]
- *    V: [num_pages][num_kv_heads][head_dim][page_size]
+ *    K: [num_pages][num_kv_heads][head_dim/8][16 slots][8]
+ *    V: [num_pages][num_kv_heads][head_dim][16 tokens]
  *  Token t of physical page pg holds logical position j with
  *  block_table[b][j / page_size] = pg and t = j % page_size; slot = pg *
- *  page_size + t.
+ *  page_size + t.  V keeps the tokens of a dim row in order; K stores token
+ *  t in slot t with bits 2 and 3 exchanged (tokens 0-3, 8-11, 4-7, 12-15 in
+ *  slots 0..15), so that the 8 tokens of a page that one MFMA score block
+ *  takes are one contiguous 128-byte run of each chunk row.
  */
 #ifndef INVATTN_H_
 #define INVATTN_H_

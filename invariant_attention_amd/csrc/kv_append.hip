@@ -10,6 +10,7 @@
 
 #include "arith.hpp"
 #include "launch.hpp"
+#include "pages.hpp"
 
 namespace ia {
 
@@ -41,14 +42,14 @@ __device__ __forceinline__ uint8_t quant_e4m3(float x) {
 // (r, c) holds row r's 8-dim chunk c of K and of V.  When the group's 16
 // slots are one whole page in order (slot[t0 + i] = 16 pg + i -- the usual
 // case when a prompt's rows are appended), the group is transposed through
-// LDS and written as whole runs: K as 16-byte units in token order inside
-// each chunk row, V as 8-token runs of each dim row.  Otherwise every row is
+// LDS and written as whole runs: K as 16-byte units filling each chunk row
+// (in K slot order), V as 8-token runs of each dim row.  Otherwise every row is
 // written to its own slot.  Either way each stored value is the row's value
 // (bf16) or its code (e4m3) at its slot.
 template <int D, bool FP8>
 __device__ __forceinline__ void store_k_unit(uint8_t* kc, size_t head, int c, int tok, uint4 w, float ks) {
   constexpr int kChunks = D / 8;
-  const size_t ke = ((head * kChunks + c) * 16 + tok) * 8;  // element index
+  const size_t ke = ((head * kChunks + c) * 16 + k_slot(tok)) * 8;  // element index
   if constexpr (FP8) {
     const bf16x8 x = __builtin_bit_cast(bf16x8, w);
     uint32_t lo = 0, hi = 0;

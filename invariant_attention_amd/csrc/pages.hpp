@@ -4,10 +4,14 @@
 // zero-padded).
 //
 // Page layout (page size 16, one page = one 16-key MFMA block):
-//   K: [num_pages][Hkv][D/8][16][8]   a 16-byte chunk = 8 dims of one token
-//   V: [num_pages][Hkv][D][16]        the 16 tokens of one dim are contiguous
+//   K: [num_pages][Hkv][D/8][16 slots][8]  a 16-byte chunk = 8 dims of one
+//      token; token t in slot k_slot(t) (bits 2 and 3 of t exchanged)
+//   V: [num_pages][Hkv][D][16]             the 16 tokens of one dim are
+//      contiguous, in token order
 // Key j of a sequence lives in page block_table[j / 16], token j % 16 (Vosti
-// App. A.1: K_X[j] = K_phys[pi(floor(j / P)), j mod P]).
+// App. A.1: K_X[j] = K_phys[pi(floor(j / P)), j mod P]).  The K slot order
+// puts the 8 tokens of one page that a score block takes (tokens 0-3 and
+// 8-11, or 4-7 and 12-15) in 8 consecutive slots: one 128-byte run per chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,15 +46,6 @@ struct Raw<true> {
   using V8 = uint2;
   static constexpr int kElemBytes = 1;
 };
-
-template <bool FP8>
-__device__ __forceinline__ typename Raw<FP8>::K load_k_raw(const uint8_t* base, size_t elem) {
-  return *reinterpret_cast<const typename Raw<FP8>::K*>(base + elem * Raw<FP8>::kElemBytes);
-}
-template <bool FP8>
-__device__ __forceinline__ typename Raw<FP8>::V load_v_raw(const uint8_t* base, size_t elem) {
-  return *reinterpret_cast<const typename Raw<FP8>::V*>(base + elem * Raw<FP8>::kElemBytes);
-}
 
 // Loads of page data that a kernel reads exactly once (the decode kernels
 // stream each split's K and V): nontemporal, so the caches treat them as
@@ -142,31 +137,26 @@ __device__ __forceinline__ bf16x8 v8_to_bf16(uint2 w, int nv) {
 
 // Operand addressing in the page layout for the key-to-slot mapping of
 // arith.hpp.  K operand of score block sb, k-step ks, lane (r, g): page block
-// 2*(sb/2) + r/8 of the tile, token k_token(sb, r), chunk 4*ks + g.  V^T
+// 2*(sb/2) + r/8 of the tile, token k_token(sb, r) (in K slot
+// 8*(sb%2) + r%8), chunk 4*ks + g.  V^T
 // operand of dim block mb, k-step ks2, lane (r, g): page block 2*ks2 + g/2,
 // dim 16*mb + r, tokens 8*(g%2) .. 8*(g%2) + 7.
 __device__ __forceinline__ int k_block(int sb, int r) { return 2 * (sb >> 1) + (r >> 3); }
 __device__ __forceinline__ int k_token(int sb, int r) { return 8 * ((r >> 2) & 1) + 4 * (sb & 1) + (r & 3); }
+// K slot of token t of a page (and, the map being its own inverse, token of
+// slot t): bits 2 and 3 exchanged.  Score block sb's tokens of a page fill
+// slots 8 (sb % 2) .. 8 (sb % 2) + 7.
+__device__ __forceinline__ int k_slot(int t) { return (t & ~12) | ((t >> 1) & 4) | ((t << 1) & 8); }
 __device__ __forceinline__ int v_block(int ks2, int g) { return 2 * ks2 + (g >> 1); }
 // Byte offset, inside one (page, kv head) block, of a lane's K chunk and of
 // its V run.
 template <int D, bool FP8>
 __device__ __forceinline__ uint32_t k_frag_off(int sb, int ks, int r, int g) {
-  return (uint32_t)((((4 * ks + g) * 16 + k_token(sb, r)) * 8) * Raw<FP8>::kElemBytes);
+  return (uint32_t)((((4 * ks + g) * 16 + k_slot(k_token(sb, r))) * 8) * Raw<FP8>::kElemBytes);
 }
 template <int D, bool FP8>
 __device__ __forceinline__ uint32_t v_frag_off(int mb, int r, int g) {
   return (uint32_t)((((16 * mb + r) * 16) + 8 * (g & 1)) * Raw<FP8>::kElemBytes);
-}
-
-// Element offsets inside a page pool.
-template <int D>
-__device__ __forceinline__ size_t k_elem(int page, int kvh, int Hkv, int chunk, int tok) {
-  return ((((size_t)page * Hkv + kvh) * (D / 8) + chunk) * 16 + tok) * 8;
-}
-template <int D>
-__device__ __forceinline__ size_t v_elem(int page, int kvh, int Hkv, int dim, int tok) {
-  return (((size_t)page * Hkv + kvh) * D + dim) * 16 + tok;
 }
 
 // ------------------------------------------------------------ block table

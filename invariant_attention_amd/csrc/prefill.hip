@@ -21,15 +21,15 @@
 // the sequence end only in a tile that has them; e4m3 pages go through
 // registers, where they are zero filled and converted to bf16 (exactly).
 // K keeps the pages' own layout; V is staged in operand order:
-//   LDS K: [4 blocks][D/8 chunks][16 positions] x 16 B, token t of an odd
-//          page block at position t ^ 4
+//   LDS K: [4 blocks][D/8 chunks][16 positions] x 16 B, K slot s of a page
+//          at position s (even page blocks) or s ^ 8 (odd ones)
 //   LDS V: [2 k-steps][D/16 dim blocks][64 lanes] x 16 B, lane 16 g + r
 //          holding dim 16 mb + r, tokens 8 (g % 2) .. + 7 of page block
 //          2 ks2 + g / 2 (its V^T operand of the value product)
-// Every operand fragment is one 16-byte LDS read per lane.  A K read takes
-// keys of two page blocks (arith.hpp's key-to-slot mapping); the swap of
-// 64-byte quarters in odd page blocks puts them on disjoint banks.  A V read
-// is 1 KiB in lane order.
+// Every operand fragment is one 16-byte LDS read per lane.  A K read takes 8
+// consecutive slots of each of two page blocks (arith.hpp's key-to-slot
+// mapping); the swap of 128-byte halves in odd page blocks puts them on
+// disjoint banks.  A V read is 1 KiB in lane order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,9 +58,9 @@ constexpr int tile_lds_bytes() {
   return 2 * kTileKeys * D * 2;
 }
 
-// LDS position of token t in a page block's K chunk row: quarters swap in
-// odd blocks (the map is its own inverse).
-__device__ __forceinline__ int k_pos(int blk, int t) { return t ^ ((blk & 1) << 2); }
+// LDS position of K slot s in a page block's chunk row: halves swap in odd
+// blocks (the map is its own inverse).
+__device__ __forceinline__ int k_pos(int blk, int s) { return s ^ ((blk & 1) << 3); }
 
 // The page block, and the byte offset of the V run inside its (page, kv head)
 // block, held by 16-byte unit c of a tile's LDS V (unit c = run c / 64 =
@@ -156,23 +156,23 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
     const int blk = c / (S::kKUnits / 4), u = c % (S::kKUnits / 4);
     uint4 w = st.k[i];
     if constexpr (!FP8) {
-      // unit u = chunk u / 16, token u % 16: 8 dims of one token
-      const int tok = u & 15;
-      const bool keep = tok < st.knv[i];
+      // unit u = chunk u / 16, slot u % 16: 8 dims of one token
+      const int slot = u & 15;
+      const bool keep = k_slot(slot) < st.knv[i];
       w.x = keep ? w.x : 0u;
       w.y = keep ? w.y : 0u;
       w.z = keep ? w.z : 0u;
       w.w = keep ? w.w : 0u;
-      *reinterpret_cast<uint4*>(lds + ((size_t)(blk * (D / 8) + (u >> 4)) * 16 + k_pos(blk, tok)) * 16) = w;
+      *reinterpret_cast<uint4*>(lds + ((size_t)(blk * (D / 8) + (u >> 4)) * 16 + k_pos(blk, slot)) * 16) = w;
     } else {
-      // unit u = chunk u / 8, tokens 2 (u % 8) and +1: 8 codes each (their
-      // positions stay adjacent under k_pos)
-      const int chunk = u >> 3, tok = 2 * (u & 7);
+      // unit u = chunk u / 8, slots 2 (u % 8) and +1: 8 codes each (tokens
+      // k_slot(slot) and + 1; the positions stay adjacent under k_pos)
+      const int chunk = u >> 3, slot = 2 * (u & 7), tok = k_slot(slot);
       const bool k0 = tok < st.knv[i], k1 = tok + 1 < st.knv[i];
       uint2 a1, b1;
       const uint2 a0 = fp8x8_to_bf16(k0 ? w.x : 0u, k0 ? w.y : 0u, &a1);
       const uint2 b0 = fp8x8_to_bf16(k1 ? w.z : 0u, k1 ? w.w : 0u, &b1);
-      uint8_t* dst = lds + ((size_t)(blk * (D / 8) + chunk) * 16 + k_pos(blk, tok)) * 16;
+      uint8_t* dst = lds + ((size_t)(blk * (D / 8) + chunk) * 16 + k_pos(blk, slot)) * 16;
       *reinterpret_cast<uint4*>(dst) = make_uint4(a0.x, a0.y, a1.x, a1.y);
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(b0.x, b0.y, b1.x, b1.y);
     }
@@ -247,7 +247,7 @@ __device__ __forceinline__ bool tile_partial(const TilePages& tp) {
 template <int D>
 __device__ __forceinline__ void lds_k_block(const uint8_t* lds, int sb, int r, int g, bf16x8 (&kf)[D / 32]) {
   const int blk = k_block(sb, r);
-  const int pos = k_pos(blk, k_token(sb, r));
+  const int pos = k_pos(blk, k_slot(k_token(sb, r)));
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     kf[ks] = __builtin_bit_cast(

@@ -17,7 +17,8 @@
  *   softmax over keys 0..p of the scaled scores, applied to V.
  *
  * Physical page layout (a choice of this project; the pages are silent):
- *   K page: [num_pages][Hkv][d/8][P][8]   (8-element chunks, token-minor)
+ *   K page: [num_pages][Hkv][d/8][P][8]   (8-element chunks, one slot per
+ *           token: see k_slot for the order of the slots)
  *   V page: [num_pages][Hkv][d][P]        (dim-major, tokens contiguous)
  * The oracle implements its own gather for that layout.
  *
@@ -97,8 +98,17 @@ uint8_t oracle_quantize_e4m3(float x, float s) {
 
 /* ------------------------------------------------------------- page layout */
 
+/* K slot of token tok of a page: inside every whole group of 16 tokens, bits
+ * 2 and 3 of tok are exchanged (a 16-token page stores tokens 0-3, 8-11, 4-7,
+ * 12-15 in slots 0..15); tokens of a group that the page does not hold whole
+ * keep their own index (so pages of fewer than 16 tokens are in token order). */
+static int k_slot(int tok, int P) {
+  if ((tok | 15) >= P) return tok;
+  return (tok & ~12) | ((tok >> 1) & 4) | ((tok << 1) & 8);
+}
+
 static size_t k_index(int64_t page, int kvh, int tok, int dim, int Hkv, int d, int P) {
-  return ((((size_t)page * Hkv + kvh) * (size_t)(d / 8) + (size_t)(dim / 8)) * P + tok) * 8 + (dim % 8);
+  return ((((size_t)page * Hkv + kvh) * (size_t)(d / 8) + (size_t)(dim / 8)) * P + k_slot(tok, P)) * 8 + (dim % 8);
 }
 
 static size_t v_index(int64_t page, int kvh, int tok, int dim, int Hkv, int d, int P) {

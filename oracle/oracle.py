@@ -95,7 +95,8 @@ def max_threads() -> int:
 # -------------------------------------------------------- array functions
 
 def kv_cache_shapes(num_pages: int, Hkv: int, d: int, P: int):
-    """Element counts of the K and V page pools ([np][Hkv][d/8][P][8] and [np][Hkv][d][P])."""
+    """Shapes of the K and V page pools ([np][Hkv][d/8][P][8] and [np][Hkv][d][P]); K's slots
+    within a page follow the oracle's k_slot order, V's tokens are in order."""
     return (num_pages, Hkv, d // 8, P, 8), (num_pages, Hkv, d, P)
 
 

@@ -221,9 +221,15 @@ def test_fp8_pages_match_dequantised_dense(oracle_lib, pow2):
     assert _close(out, ref) < 1e-12
 
 
+# K slot of each token of a 16-token page: tokens 0-3, 8-11, 4-7, 12-15 fill slots 0..15, so that
+# the 8 tokens one MFMA score block takes from a page (0-3 with 8-11, or 4-7 with 12-15) are 8
+# consecutive 16-byte units.
+K_SLOT_16 = [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+
+
 def test_kv_append_layout(oracle_lib):
     """Byte placement of the page layout, read back with numpy indexing rather than index
-    arithmetic: K[page][head][dim // 8][token][dim % 8], V[page][head][dim][token]."""
+    arithmetic: K[page][head][dim // 8][K_SLOT_16[token]][dim % 8], V[page][head][dim][token]."""
     shape = wl.AttnShape(Hq=4, Hkv=2, d=32, P=16, S=64)
     rng = np.random.default_rng(2)
     T = 40
@@ -236,13 +242,32 @@ def test_kv_append_layout(oracle_lib):
     for t in range(T):
         page, tok = divmod(int(slots[t]), 16)
         for h in range(2):
-            assert np.array_equal(kc[page, h, :, tok, :].reshape(-1), kb[t, h])
+            assert np.array_equal(kc[page, h, :, K_SLOT_16[tok], :].reshape(-1), kb[t, h])
             assert np.array_equal(vc[page, h, :, tok], vb[t, h])
     # untouched slots stay zero
     written = np.zeros(8 * 16, bool); written[slots] = True
     for s in np.nonzero(~written)[0]:
         page, tok = divmod(int(s), 16)
-        assert not kc[page, :, :, tok, :].any() and not vc[page, :, :, tok].any()
+        assert not kc[page, :, :, K_SLOT_16[tok], :].any() and not vc[page, :, :, tok].any()
+
+
+@pytest.mark.parametrize("P", [4, 8, 32])
+def test_kv_append_layout_other_page_sizes(oracle_lib, P):
+    """Pages of fewer than 16 tokens keep K in token order; a 32-token page applies the 16-token
+    slot order to each of its two groups of 16."""
+    shape = wl.AttnShape(Hq=2, Hkv=1, d=16, P=P, S=64)
+    rng = np.random.default_rng(3)
+    T = 4 * P
+    k = _bf16(rng.standard_normal((T, 1, 16)))
+    v = _bf16(rng.standard_normal((T, 1, 16)))
+    slots = np.arange(T, dtype=np.int64)
+    kc, vc = osd.host_pools(shape, 4)
+    oracle.kv_append(osd.bits16(k), osd.bits16(v), slots, kc, vc, Hkv=1, d=16, P=P)
+    kb = osd.bits16(k)
+    for t in range(T):
+        page, tok = divmod(t, P)
+        want = tok if P < 16 else 16 * (tok // 16) + K_SLOT_16[tok % 16]
+        assert np.array_equal(kc[page, 0, :, want, :].reshape(-1), kb[t, 0])
 
 
 # ------------------------------------------------------ sliding window (Vosti App. A.5)
