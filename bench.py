@@ -706,6 +706,12 @@ def _prefill_world(shape, lens, layout_seed):
     return seqs, layout, ctx, k, v
 
 
+def prefill_workspace(ctx, total_q, max_seq_len):
+    """The prefill workspace for a launch (None when its rows see one split only)."""
+    n = ia.ia_prefill_workspace_bytes(ctx, int(total_q), int(max_seq_len))
+    return torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+
+
 def _prefill_rows(shape, seqs, layout, ctx, k, v, p0, p1):
     """Rows p0 .. p1 - 1 of every prompt in one prefill call (key length p1)."""
     q = torch.cat([s.q(SEED, shape, p0, p1) for s in seqs]).to(DEV)
@@ -714,7 +720,8 @@ def _prefill_rows(shape, seqs, layout, ctx, k, v, p0, p1):
     sl = torch.as_tensor(np.full(B, p1, np.int32), device=DEV)
     bt = torch.as_tensor(layout.block_table, device=DEV)
     out = torch.empty_like(q)
-    ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, p1 - p0, p1, out)
+    ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, p1 - p0, p1, out,
+                             workspace=prefill_workspace(ctx, q.shape[0], p1))
     return out.view(B, p1 - p0, shape.Hq, shape.d)
 
 
@@ -743,7 +750,8 @@ def invariance_variations(lens):
     cu = torch.as_tensor(np.arange(0, 8 * 16 + 1, 16, dtype=np.int32), device=DEV)
     sl = torch.as_tensor(np.array(lens8, np.int32), device=DEV)
     pre = torch.empty((8 * 16, shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
-    ia.ia_paged_attn_prefill(w1.ctx, q16, cu, sl, w1.k, w1.v, w1.bt, 16, max(lens8), pre)
+    ia.ia_paged_attn_prefill(w1.ctx, q16, cu, sl, w1.k, w1.v, w1.bt, 16, max(lens8), pre,
+                             workspace=prefill_workspace(w1.ctx, q16.shape[0], max(lens8)))
     pre = pre.view(8, 16, shape.Hq, shape.d)
     ws = torch.empty(ia.ia_decode_workspace_bytes(w1.ctx, 8, max(lens8)), dtype=torch.uint8, device=DEV)
     for j in range(16):
@@ -826,10 +834,11 @@ def prefill_tflops(steps: int, warmup: int):
     sl = torch.as_tensor(np.array(lens, np.int32), device=DEV)
     bt = torch.as_tensor(layout.block_table, device=DEV)
     out = torch.empty_like(q)
+    ws = prefill_workspace(ctx, q.shape[0], 4096)
     stream = torch.cuda.current_stream()
 
     def run():
-        ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, 4096, 4096, out, stream=stream)
+        ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, 4096, 4096, out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         run()
@@ -1084,10 +1093,11 @@ def qwen235_points(steps, warmup):
     sl = torch.as_tensor(np.array([32768] * 16 + [nq] * 4, np.int32), device=DEV)
     btd = torch.as_tensor(bt, device=DEV)
     o = torch.empty_like(q)
+    ws = prefill_workspace(w.ctx, q.shape[0], 32768)
     stream = torch.cuda.current_stream()
 
     def mixed():
-        ia.ia_paged_attn_prefill(w.ctx, q, cu, sl, kk, vv, btd, nq, 32768, o, stream=stream)
+        ia.ia_paged_attn_prefill(w.ctx, q, cu, sl, kk, vv, btd, nq, 32768, o, workspace=ws, stream=stream)
 
     ms = _timed(mixed, steps, warmup)
     flops = 4.0 * shape.d * shape.Hq * (16 * 32768 + 4 * nq * (nq + 1) / 2)
@@ -1170,12 +1180,13 @@ def prefill_chunked(steps, warmup):
             qc = q[:, p0:p1].reshape(-1, shape.Hq, shape.d).contiguous()
             cu = torch.as_tensor(np.arange(0, B * (p1 - p0) + 1, p1 - p0, dtype=np.int32), device=DEV)
             sl = torch.as_tensor(np.full(B, p1, np.int32), device=DEV)
-            prepared.append((qc, cu, sl, torch.empty_like(qc), p1 - p0, p1))
+            prepared.append((qc, cu, sl, torch.empty_like(qc), p1 - p0, p1,
+                             prefill_workspace(ctx, qc.shape[0], p1)))
         return prepared
 
     def run(prepared):
-        for qc, cu, sl, o, ql, kl in prepared:
-            ia.ia_paged_attn_prefill(ctx, qc, cu, sl, k, v, bt, ql, kl, o, stream=stream)
+        for qc, cu, sl, o, ql, kl, ws in prepared:
+            ia.ia_paged_attn_prefill(ctx, qc, cu, sl, k, v, bt, ql, kl, o, workspace=ws, stream=stream)
 
     def flops(p0, p1):
         return 4.0 * shape.d * shape.Hq * B * sum(p + 1 for p in range(p0, p1))

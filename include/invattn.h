@@ -176,9 +176,12 @@ const char* ia_version(void);
  * the score slots runs the split kernel (the same bits). */
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
-/* Device workspace for ia_paged_attn_prefill.  Returns 0: prefill folds each
- * row's split partials in registers and needs no workspace, so its
- * workspace / ws_bytes arguments are accepted and ignored (NULL / 0 is fine). */
+/* Device workspace for ia_paged_attn_prefill: 0 when max_seq_len <=
+ * split_tokens (no row can see keys of two splits; NULL / 0 is then fine);
+ * otherwise, for every (query row, query head), the fp32 merge of the splits
+ * folded so far: total_q * Hq * d floats of U, then total_q * Hq * 2 floats of
+ * (M, Z), each array rounded up to 256 bytes.  A row that sees one split only
+ * never touches it. */
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len);
 
 /*
@@ -205,13 +208,21 @@ ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, 
  * (its own K/V already appended).  Keys are cut into splits at absolute
  * multiples of split_tokens; each split is walked in 64-key tiles in
  * ascending order with the online-softmax update of Vosti App. A.2 (fp32
- * state m, z, U; z sums the fp32 weights).  One deliberate departure from
- * App. A.2, which casts the weights once to the cache type before the PV
- * product: each fp32 weight w enters the PV product as two bf16 numbers,
- * hi = bf16(w) and lo = bf16(w - hi), in two MFMAs (hi first), so a weight
- * carries about 16 significant bits instead of 8 (a single cast misses the
- * 2e-3 + 1e-2 |ref| tolerance on rows over a few keys whose values cancel).
- * Every kernel does the same, so invariance is unaffected.  The split states
+ * state m, z, U; z sums the fp32 weights).  Departures from App. A.2, each
+ * taken by every kernel alike (so invariance is unaffected):
+ *  - it casts the weights once to the cache type before the PV product;
+ *    here each fp32 weight w enters the PV product as two bf16 numbers,
+ *    hi = bf16(w) and lo = bf16(w - hi), in two MFMAs (hi first), so a
+ *    weight carries about 16 significant bits instead of 8 (a single cast
+ *    misses the 2e-3 + 1e-2 |ref| tolerance on rows over a few keys whose
+ *    values cancel);
+ *  - the running reference m is raised only when a tile's maximum scaled
+ *    score exceeds it by more than 8 (base-2 units), so weights are at most
+ *    2^8 and most tiles have alpha = 1 (the same softmax in exact
+ *    arithmetic);
+ *  - a weight's exponent is one fused multiply-add, exp2(fma(s, c, -m)), of
+ *    the raw score s (one rounding where scaling then subtracting rounds
+ *    twice).  The split states
  * are then folded in ascending split order and the row is finalised as
  * O = bf16(U * select(z > 0, 1/z, 0)).
  *   q            dev [B][Hq][d] bf16
@@ -268,7 +279,9 @@ size_t ia_decode_noalloc_scratch_bytes(void);
  *   max_q_len    host upper bound of q lengths (grid only)
  *   max_seq_len  host upper bound of seq_lens (grid only)
  *   out          dev [total_q][Hq][d] bf16
- *   workspace    ignored (ia_prefill_workspace_bytes returns 0)
+ *   workspace    dev, >= ia_prefill_workspace_bytes(ctx, total_q, max_seq_len)
+ *                bytes, 16-byte aligned (NULL when that is 0); a smaller one
+ *                is refused with IA_ERR_WORKSPACE_TOO_SMALL
  */
 ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
                                 const int32_t* seq_lens, const void* k_cache, const void* v_cache,

@@ -23,6 +23,14 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source device flags.  The prefill kernel runs one wave per SIMD with two
+# 16-row blocks per wave and holds more state than the 256 architectural VGPRs;
+# with its MFMA accumulators forced to architectural VGPRs, the per-tile
+# rescale and the split merge touch no accumulation registers (AGPRs), and
+# the merged split state is what lives there.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     cand = os.path.join(rocm, "bin", "hipcc")
@@ -31,19 +39,41 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source into libinvattn.so (always rebuilds)."""
+    import shutil
+    import tempfile
     include = os.path.join(os.path.dirname(HERE), "include")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", include, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(line for line in proc.stderr.splitlines() if noise not in line)
-    if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    objdir = tempfile.mkdtemp(prefix="invattn_build_")
+    try:
+        # One object per source (compiled in parallel, each with its own flags), then one link.
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(objdir, src + ".o")
+            cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-I", include, "-c", "-o", obj,
+                   os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        errs = []
+        for src, p in procs:
+            _, e = p.communicate()
+            e = "\n".join(line for line in e.splitlines() if noise not in line)
+            if p.returncode != 0:
+                errs.append(f"{src}:\n{e}")
+            elif verbose and e.strip():
+                print(e, file=sys.stderr)
+        if errs:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + proc.stderr)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     os.replace(tmp, LIB)
     _write_build_info()
     return LIB

@@ -131,11 +131,16 @@ __device__ __forceinline__ f32x4 block_scores(const bf16x8 (&kf)[D / 32], const 
   return acc;
 }
 
-// The softmax half of one tile's update for one row (Vosti App. A.2):
-//   G  = dot(Q, K^T) * c,  masked lanes -> -inf
-//   m^ = max(m, max_b G),  alpha = exp2(m - m^)
-//   A  = select(mask, exp2(G - m^), 0)
+// The softmax half of one tile's update for one row (Vosti App. A.2, with
+// the lazy reference of raise_max):
+//   s  = dot(Q, K^T),  masked lanes -> -inf
+//   m^ = raise_max(m, max_b(s) * c),  alpha = exp2(m - m^)
+//   A  = select(mask, exp2(fma(s, c, -m^)), 0)
 //   z^ = z * alpha + sum_b A
+// c > 0, so max_b(s) * c is the maximum of the rounded scaled scores s * c
+// (rounding is monotone) and one multiply per row serves the maximum.  The
+// exponent's argument s * c - m^ is one fused multiply-add (one rounding,
+// where App. A.2's G = s * c then G - m^ rounds twice).
 // The row sees keys lo..limit: limit is its position p (keys beyond it, and
 // every key of a row that does not exist, limit < 0, are masked) and lo is 0,
 // or p - w + 1 under a sliding window of w keys (Vosti App. A.5: the mask
@@ -154,19 +159,27 @@ struct TileStep {
   bf16x8 phi[2], plo[2];
 };
 
-// Splits weights w0, w1 into bf16 hi parts and bf16 lo parts (w - hi is exact
-// in fp32), both rounded to nearest even.
+// Splits weights w0, w1 into bf16 hi parts and bf16 lo parts, both rounded
+// to nearest even.  The residual w - hi is exact in fp32; it is formed by
+// v_dot2_f32_bf16 as hi . (-1, -0) + w0 and hi . (-0, -1) + w1, whose products
+// and sums are exact here, so no unpacking of hi to fp32 is needed.  (The
+// zero halves are -0 so that neither constant is an inline constant: for
+// packed bf16 operands the compiler's reading of the inline constant -1.0
+// differs from the hardware's.)
 __device__ __forceinline__ void split_hi_lo(float w0, float w1, bf16x2& hi, bf16x2& lo) {
   hi = __builtin_convertvector((f32x2{w0, w1}), bf16x2);
-  const float r0 = w0 - (float)hi[0];
-  const float r1 = w1 - (float)hi[1];
+  const bf16x2 neg0 = {(__bf16)-1.0f, (__bf16)-0.0f};
+  const bf16x2 neg1 = {(__bf16)-0.0f, (__bf16)-1.0f};
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hi, neg0, w0, false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hi, neg1, w1, false);
   lo = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
 }
 
-// The row maximum half of a tile step: x = masked scaled scores, mx = their
-// maximum over the row's 64 keys (lane values first, then the butterfly).
+// The row maximum half of a tile step: s = masked scores (unscaled), mx =
+// the maximum of the scaled scores over the row's 64 keys (lane values first,
+// then the butterfly, then the scale).
 struct TileMax {
-  float x[4][4];
+  float s[4][4];
   float mx;
   bool any_visible;  // the tile holds a key the row sees
 };
@@ -186,19 +199,28 @@ __device__ __forceinline__ TileMax tile_max(const f32x4 (&s)[4], float c, int ti
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = tile_key0 + tile_key(blk, lane_group, j);
-      const float g = s[blk][j] * c;
-      tm.x[blk][j] = (!MASK || key_visible(key, lo, limit)) ? g : neg_inf();
-      mx = fmaxf(mx, tm.x[blk][j]);
+      tm.s[blk][j] = (!MASK || key_visible(key, lo, limit)) ? s[blk][j] : neg_inf();
+      mx = fmaxf(mx, tm.s[blk][j]);
     }
   }
-  tm.mx = row_max(mx);
+  tm.mx = row_max(mx) * c;
   tm.any_visible = !MASK || (tile_key0 <= limit && tile_key0 + kTileKeys - 1 >= lo);
   return tm;
 }
 
-// The running maximum after a tile: unchanged by a tile the row does not see.
+// The running reference m after a tile whose maximum scaled score is mx.
+// Vosti App. A.2 takes m^ = max(m, mx) at every tile; here m is raised only
+// when mx exceeds it by more than kMaxSlack (base-2 units), to mx.  The
+// result is the same softmax in exact arithmetic (every weight and sum is
+// relative to m); the weights are bounded by 2^kMaxSlack instead of 1, and a
+// tile that does not raise m has alpha = exp2(0) = 1, so a kernel can skip
+// rescaling U (U * 1 = U exactly).  The first visible tile always sets m
+// (m = -inf before it).  A tile the row does not see leaves m unchanged
+// (mx = -inf, or any_visible = false).
+constexpr float kMaxSlack = 8.0f;
+__device__ __forceinline__ float raise_max(float m, float mx) { return mx > m + kMaxSlack ? mx : m; }
 __device__ __forceinline__ float max_update(float m, float mx, bool any_visible) {
-  return any_visible ? fmaxf(m, mx) : m;
+  return any_visible ? raise_max(m, mx) : m;
 }
 
 // The running sum after a tile: z^ = z * alpha + sum_b A (two roundings).
@@ -212,20 +234,23 @@ __device__ __forceinline__ float z_update(float z, float alpha, float sum) {
 // z_new is left to the caller (z_update), so a kernel that has m before each
 // tile but not yet z can form the weights of many tiles at once.
 template <bool MASK>
-__device__ __forceinline__ TileStep tile_weights(float m, const TileMax& tm, int tile_key0, int lo, int limit,
-                                                 int lane_group, float& row_sum_out) {
+__device__ __forceinline__ TileStep tile_weights(float m, const TileMax& tm, float c, int tile_key0, int lo,
+                                                 int limit, int lane_group, float& row_sum_out) {
   TileStep ts;
   ts.any_visible = tm.any_visible;
-  ts.m_new = fmaxf(m, tm.mx);
+  ts.m_new = raise_max(m, tm.mx);
   ts.alpha = ia_exp2(m - ts.m_new);
+  const float neg_m = -ts.m_new;
   float a[4][4];
   float sum = 0.f;
+  // A masked key's score is -inf: when the tile has a key the row sees, m^
+  // is finite and its weight exp2(-inf) = 0 exactly.  When it has none, the
+  // step is discarded (any_visible), whatever the weights are.
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = tile_key0 + tile_key(blk, lane_group, j);
-      a[blk][j] = (!MASK || key_visible(key, lo, limit)) ? ia_exp2(tm.x[blk][j] - ts.m_new) : 0.f;
+      a[blk][j] = ia_exp2(__builtin_fmaf(tm.s[blk][j], c, neg_m));
       sum = sum + a[blk][j];
     }
   }
@@ -254,7 +279,7 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
                                                  int lo, int limit, int lane_group) {
   const TileMax tm = tile_max<MASK>(s, c, tile_key0, lo, limit, lane_group);
   float sum;
-  TileStep ts = tile_weights<MASK>(m, tm, tile_key0, lo, limit, lane_group, sum);
+  TileStep ts = tile_weights<MASK>(m, tm, c, tile_key0, lo, limit, lane_group, sum);
   ts.z_new = z_update(z, ts.alpha, sum);
   return ts;
 }
@@ -263,11 +288,19 @@ __device__ __forceinline__ TileStep tile_softmax(float m, float z, const f32x4 (
 //   U^ = U * alpha, then per key k-step ks2 (ascending) U^ += V^T A_hi, U^ += V^T A_lo
 // (one MFMA each, hi first); the block keeps U when the tile is fully masked.
 // MASK = false: a tile every stored row sees, so the update always applies.
+// pv_rescale and pv_accumulate are its two halves, for a kernel that skips
+// the rescale of a wave whose rows all have alpha = 1 (U * 1 = U exactly).
 template <bool MASK = true>
-__device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2], const TileStep& ts) {
+__device__ __forceinline__ f32x4 pv_rescale(const f32x4& u, const TileStep& ts) {
   f32x4 un;
 #pragma unroll
   for (int j = 0; j < 4; ++j) un[j] = u[j] * ts.alpha;
+  if constexpr (MASK) return ts.any_visible ? un : u;
+  return un;
+}
+template <bool MASK = true>
+__device__ __forceinline__ f32x4 pv_accumulate(const f32x4& u, const bf16x8 (&vf)[2], const TileStep& ts) {
+  f32x4 un = u;
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
     un = mfma(vf[ks2], ts.phi[ks2], un);
@@ -275,6 +308,17 @@ __device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2],
   }
   if constexpr (MASK) return ts.any_visible ? un : u;
   return un;
+}
+template <bool MASK = true>
+__device__ __forceinline__ f32x4 pv_block(const f32x4& u, const bf16x8 (&vf)[2], const TileStep& ts) {
+  return pv_accumulate<MASK>(pv_rescale<MASK>(u, ts), vf, ts);
+}
+// Whether this lane's row needs pv_rescale for this tile: a visible tile
+// whose alpha is not 1.  A kernel skips the rescale only when no lane of the
+// wave needs it (a wave-uniform branch).
+template <bool MASK = true>
+__device__ __forceinline__ bool rescale_lane(const TileStep& ts) {
+  return (!MASK || ts.any_visible) && ts.alpha != 1.0f;
 }
 
 // Commits the scalar half of a tile step.

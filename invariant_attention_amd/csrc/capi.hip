@@ -229,11 +229,22 @@ size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_s
   return u + ml + ord + x + mx;
 }
 
+// Prefill workspace: for every query row and head, the fp32 merge (U, then
+// (M, Z)) of the splits folded so far.  Only a launch in which some row can
+// see keys of more than one split (max_seq_len > split_tokens) needs one.
+static void prefill_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len, size_t* u, size_t* mz) {
+  *u = *mz = 0;
+  if (max_seq_len <= ctx->cfg.split_tokens) return;
+  const size_t rows = (size_t)total_q * ctx->cfg.num_q_heads;
+  *u = align_up(rows * ctx->cfg.head_dim * sizeof(float));
+  *mz = align_up(rows * 2 * sizeof(float));
+}
+
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
-  (void)ctx;
-  (void)total_q;
-  (void)max_seq_len;
-  return 0;
+  if (!ctx || total_q <= 0 || max_seq_len <= 0) return 0;
+  size_t u, mz;
+  prefill_ws_parts(ctx, total_q, max_seq_len, &u, &mz);
+  return u + mz;
 }
 
 ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -378,8 +389,6 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
                                 const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t total_q,
                                 int32_t max_q_len, int32_t max_seq_len, void* out, void* workspace,
                                 size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!ctx) return fail(IA_ERR_INVALID_ARG, "ctx is NULL");
   if (B < 0 || total_q < 0 || max_q_len < 0)
     return fail(IA_ERR_INVALID_ARG, "B, total_q and max_q_len must be >= 0");
@@ -394,9 +403,17 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
     return fail(IA_ERR_INVALID_ARG, "max_q_len and max_seq_len must be positive when total_q > 0");
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  const int64_t row_blocks = ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group));
+  const int64_t row_blocks = ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3));
   if ((int64_t)B * row_blocks * ctx->cfg.num_kv_heads >= ((int64_t)1 << 31))
     return fail(IA_ERR_INVALID_ARG, "grid too large");
+  size_t u_bytes, mz_bytes;
+  prefill_ws_parts(ctx, total_q, max_seq_len, &u_bytes, &mz_bytes);
+  if (u_bytes + mz_bytes > 0) {
+    if (!workspace || ws_bytes < u_bytes + mz_bytes)
+      return fail(IA_ERR_WORKSPACE_TOO_SMALL, "prefill workspace needs %zu bytes (got %zu)", u_bytes + mz_bytes,
+                  ws_bytes);
+    if (!aligned(workspace, 16)) return fail(IA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   ia::PrefillArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.cu_q_lens = cu_q_lens;
@@ -407,6 +424,8 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
   a.v_scale = v_scale;
   a.block_table = block_table;
   a.out = static_cast<__bf16*>(out);
+  a.ws_u = u_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.ws_mz = u_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes) : nullptr;
   a.c = ctx->c;
   a.B = B;
   a.Hq = ctx->cfg.num_q_heads;

@@ -400,8 +400,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_wide_kernel(DecodeArgs
       float mp = m;
       for (int i = 0; i < w; ++i) mp = max_update(mp, mxs[i][r], visible(k_begin + kTileKeys * (c0 + i)));
       float sum;
-      const TileStep ts = full(tw0) ? tile_weights<false>(mp, tm, tw0, lo, limit, g, sum)
-                                    : tile_weights<true>(mp, tm, tw0, lo, limit, g, sum);
+      const TileStep ts = full(tw0) ? tile_weights<false>(mp, tm, c, tw0, lo, limit, g, sum)
+                                    : tile_weights<true>(mp, tm, c, tw0, lo, limit, g, sum);
       pw[w][0][lane] = __builtin_bit_cast(uint4, ts.phi[0]);
       pw[w][1][lane] = __builtin_bit_cast(uint4, ts.plo[0]);
       pw[w][2][lane] = __builtin_bit_cast(uint4, ts.phi[1]);
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
       *reinterpret_cast<f32x4*>(a.ws_x + spread_x_off(slot, a.group, blk, g, r)) =
-          f32x4{tm.x[blk][0], tm.x[blk][1], tm.x[blk][2], tm.x[blk][3]};
+          f32x4{tm.s[blk][0], tm.s[blk][1], tm.s[blk][2], tm.s[blk][3]};
     if (g == 0) a.ws_mx[slot * 16 + r] = tm.mx;
   }
 }
@@ -613,19 +613,19 @@ __global__ __launch_bounds__(64) void decode_score_kernel(DecodeArgs a) {
 // The weights of one tile from its stored scores and the running maximum m
 // before it; MASK as in the split kernel's step.
 template <bool MASK>
-__device__ __forceinline__ void spread_weights(const DecodeArgs& a, size_t slot, float m, int t0, int lo, int limit,
-                                               int rr, bool row_ok, int g, int r) {
+__device__ __forceinline__ void spread_weights(const DecodeArgs& a, size_t slot, float m, float c, int t0, int lo,
+                                               int limit, int rr, bool row_ok, int g, int r) {
   TileMax tm;
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_x + spread_x_off(slot, a.group, blk, g, rr));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tm.x[blk][j] = x[j];
+    for (int j = 0; j < 4; ++j) tm.s[blk][j] = x[j];
   }
   tm.mx = a.ws_mx[slot * 16 + rr];
   tm.any_visible = !MASK || (t0 <= limit && t0 + kTileKeys - 1 >= lo);
   float sum;
-  const TileStep ts = tile_weights<MASK>(m, tm, t0, lo, limit, g, sum);
+  const TileStep ts = tile_weights<MASK>(m, tm, c, t0, lo, limit, g, sum);
   if (row_ok) {
     // The scores were read above into registers the weights depend on; the
     // slot's 256 bytes per row now take the four weight operands.
@@ -649,6 +649,8 @@ __global__ __launch_bounds__(64) void decode_weight_kernel(DecodeArgs a) {
   const bool row_ok = r < a.group;
   const int rr = row_ok ? r : 0;  // padding lanes read row 0's slots (never stored)
   const int limit = row_ok ? sp.p : -1;
+  float c = a.c;
+  if constexpr (FP8) c = c * a.k_scale[un.kvh];
   // The running maximum before this tile: the split kernel's max updates
   // over the split's earlier tiles, in order.
   const size_t slot0 = slot - lt;
@@ -666,9 +668,9 @@ __global__ __launch_bounds__(64) void decode_weight_kernel(DecodeArgs a) {
   }
   const int t0 = sp.k_begin + kTileKeys * lt;
   if (tile_full(t0, sp.lo, sp.n))
-    spread_weights<false>(a, slot, m, t0, sp.lo, limit, rr, row_ok, g, r);
+    spread_weights<false>(a, slot, m, c, t0, sp.lo, limit, rr, row_ok, g, r);
   else
-    spread_weights<true>(a, slot, m, t0, sp.lo, limit, rr, row_ok, g, r);
+    spread_weights<true>(a, slot, m, c, t0, sp.lo, limit, rr, row_ok, g, r);
 }
 
 template <bool FP8>
@@ -691,7 +693,7 @@ __device__ __forceinline__ void spread_chain(const SpreadFrag<FP8>& f, int valid
   ts.plo[0] = __builtin_bit_cast(bf16x8, f.w[1]);
   ts.phi[1] = __builtin_bit_cast(bf16x8, f.w[2]);
   ts.plo[1] = __builtin_bit_cast(bf16x8, f.w[3]);
-  ts.m_new = fmaxf(m, f.asm4[2]);
+  ts.m_new = raise_max(m, f.asm4[2]);
   ts.z_new = z_update(z, f.asm4[0], f.asm4[1]);
   bf16x8 vf[2];
 #pragma unroll

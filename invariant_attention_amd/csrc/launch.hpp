@@ -56,6 +56,8 @@ struct PrefillArgs {
   const float* v_scale;
   const int32_t* block_table;
   __bf16* out;
+  float* ws_u;                // [total_q][Hq][D]: merge of a row's splits so far (rows that see > 1 split)
+  float* ws_mz;               // [total_q][Hq][2]: its (M, Z)
   float c;
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;
@@ -70,7 +72,7 @@ hipError_t launch_decode(int D, bool fp8, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st);
 // Query positions one prefill workgroup covers (its grid has
 // ceil(max_q_len / this) row blocks per (sequence, kv head)).
-int prefill_positions_per_block(int group);
+int prefill_positions_per_block(int group, bool fp8);
 
 // Layer operators (layer_ops.hip).
 hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, int H, float eps, hipStream_t st);

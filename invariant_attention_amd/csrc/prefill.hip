@@ -3,16 +3,22 @@
 // value-relevant arithmetic is in arith.hpp; each row runs exactly the
 // decode row's operations at its position (Vosti §5.3, App. A.1-A.5).
 //
-// Rows.  A wave owns 16 rows = 16/g consecutive positions x the g query
-// heads of one kv head; a workgroup of 4 waves owns 4 * 16/g consecutive
-// positions of one sequence.  Two workgroups share a compute unit (2 x 64 KiB
-// of LDS, 2 waves per SIMD) and run out of step with each other, so one's
-// value products overlap the other's softmax; one workgroup of 8 waves per
-// compute unit, whose waves meet at every tile's barrier, measured ~3% slower.  The workgroup walks 64-key tiles 0..T of the
-// keys its last row can see; splits of S keys start a fresh state, and at a
-// split's end every row that reaches into it folds the split's state into its
-// running merge (ascending order, as in decode).  Tiles past all of a wave's
-// positions are skipped, which is the identity on its rows' states.
+// Rows.  A row block is 16 rows = 16/g consecutive positions x the g query
+// heads of one kv head.  A wave owns two consecutive row blocks (bf16 pages;
+// one for e4m3 pages), and every K and V fragment it reads from LDS feeds the
+// MFMAs of both, which halves the LDS reads per flop; a workgroup of 4 waves
+// owns 4 x 2 x 16/g consecutive positions of one sequence, so each staged
+// tile serves 128 rows.  Two workgroups share a compute unit (2 x 64 KiB of
+// LDS, 2 waves per SIMD, <= 256 VGPRs each) and run out of step with each
+// other, so one's value products overlap the other's softmax.  The workgroup
+// walks 64-key tiles 0..T of the keys its last row can see; splits of S keys
+// start a fresh state, and at a split's end every row that reaches into it
+// folds the split's state into its merge (ascending order, as in decode).
+// The merge so far of a row that sees several splits waits in the workspace
+// between its splits (holding it in registers would not fit two row blocks
+// in 256 VGPRs); the fold of a row's last split writes the row.  Tiles past
+// all of a wave's positions are skipped, which is the identity on its rows'
+// states.
 //
 // Staging.  Tiles pass through two LDS slots: while the waves compute tile t,
 // the workgroup's loads of tile t+1 are in flight into the other slot; one
@@ -41,8 +47,16 @@
 
 namespace ia {
 
-constexpr int kPrefillWaves = 4;  // per workgroup; 2 workgroups per compute unit
+constexpr int kPrefillWaves = 4;       // per workgroup; two workgroups per compute unit
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+// 16-row blocks per wave, sharing every K/V fragment read: two for bf16
+// pages; one for e4m3 pages, whose staging registers leave no room for a
+// second block within the 256 VGPRs of two waves per SIMD.
+template <bool FP8>
+constexpr int row_blocks_per_wave() {
+  return FP8 ? 1 : 2;
+}
+constexpr int kStageTiles = 1;         // tiles per LDS slot (two slots)
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
 // First key position p sees: 0, or p - w + 1 under a sliding window of w keys
@@ -184,6 +198,16 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const Stage<D, FP8>& s
   }
 }
 
+// A wave-uniform pointer made opaque to the optimiser (an empty asm on its
+// SGPR pair), so that a lane offset added to it is not folded into a 64-bit
+// per-lane address hoisted out of the tile loop: such hoisted addresses cost
+// two VGPRs each for the whole loop.
+__device__ __forceinline__ const uint8_t* sgpr_base(const uint8_t* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<const uint8_t*>(v);
+}
+
 // ---- bf16 tiles: direct global -> LDS loads (global_load_lds) --------------
 // The data moves from the pages to LDS without passing through registers.
 // Each instruction of a wave fills a contiguous 1 KiB LDS run, 16 bytes per
@@ -200,19 +224,26 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
   constexpr int kKBytes = kTileKeys * D * 2;
   static_assert(kChunks % kPrefillWaves == 0, "chunks must divide over waves");
   auto head = [&](const uint8_t* pool, int pg) { return pool + ((size_t)pg * Hkv + kvh) * kHeadBytes; };
-  const int kl = (lane & ~15) | k_pos(1, lane & 15);  // the source position of an odd block's lane
+  // Each address is a wave-uniform base plus a 32-bit lane offset.  The lane
+  // offset of a K copy: the lane's 16 bytes of the 1 KiB run, in k_pos order
+  // for an odd page block.  A V copy's lane takes its run from page block
+  // 2 ks2 + (lane / 32) at v_frag_off.
+  __builtin_assume(w >= 0 && w < kPrefillWaves);  // so that the chunk -> page block map folds
+  const uint32_t k_even = (uint32_t)lane * 16;
+  const uint32_t k_odd = (uint32_t)((lane & ~15) | k_pos(1, lane & 15)) * 16;
+  const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < kChunks / kPrefillWaves; ++i) {
     const int ch = i * kPrefillWaves + w;  // wave-uniform
     const int blk = ch / (kChunks / 4), part = ch % (kChunks / 4);
     const int pg = blk == 0 ? tp.page[0] : (blk == 1 ? tp.page[1] : (blk == 2 ? tp.page[2] : tp.page[3]));
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(kc, pg) + part * 1024 + ((blk & 1) ? kl : lane) * 16),
-                                     (lds_void_t*)(slot + ch * 1024), 16, 0, 0);
-    // V: run ch; the lane's run lies in page block 2 ks2 + (lane / 32).
-    int vb, first;
-    uint32_t off;
-    v_unit<D, false>(ch * 64 + lane, vb, off, first);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(head(vc, select4(vb, tp.page)) + off),
+    const uint8_t* kb = sgpr_base(head(kc, pg) + part * 1024);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(kb + ((blk & 1) ? k_odd : k_even)), (lds_void_t*)(slot + ch * 1024),
+                                     16, 0, 0);
+    const int ks2 = ch / (D / 16), mb = ch % (D / 16);
+    const uint8_t* vb0 = sgpr_base(head(vc, ks2 == 0 ? tp.page[0] : tp.page[2]));
+    const uint8_t* vb1 = sgpr_base(head(vc, ks2 == 0 ? tp.page[1] : tp.page[3]));
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)((lane < 32 ? vb0 : vb1) + v_frag_off<D, false>(mb, r, g)),
                                      (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
   }
 }
@@ -253,6 +284,21 @@ __device__ __forceinline__ void lds_k_block(const uint8_t* lds, int sb, int r, i
     kf[ks] = __builtin_bit_cast(
         bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + pos) * 16));
 }
+// One K fragment (k-step ks of score block sb) and one V fragment (k-step
+// ks2 of dim block mb).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_k_frag(const uint8_t* lds, int sb, int ks, int r, int g) {
+  const int blk = k_block(sb, r);
+  const int pos = k_pos(blk, k_slot(k_token(sb, r)));
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + pos) * 16));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_v_frag(const uint8_t* lds, int mb, int ks2, int r, int g) {
+  constexpr int kKBytes = kTileKeys * D * 2;
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + (ks2 * (D / 16) + mb) * 1024 + (16 * g + r) * 16));
+}
 template <int D>
 __device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, int g, bf16x8 (&vf)[2]) {
   constexpr int kKBytes = kTileKeys * D * 2;
@@ -274,21 +320,66 @@ __device__ __forceinline__ void lds_tile_scores(const uint8_t* tile, const QFrag
   }
 }
 
+// Folds the state of one split into the merge of the lane's row (row index
+// ridx = query row * Hq + query head): the first split seeds the merge
+// (M, Z, U) = (m, z, u); a later one merges into the merge so far, which
+// waits in the workspace between splits (Vosti App. A.3: the split states
+// are folded in ascending order).  After the row's last split the merge is
+// finalised into the output row; otherwise it goes (back) to the workspace.
+// Only rows that see more than one split touch the workspace.
+template <int D>
+__device__ __forceinline__ void fold_split(const PrefillArgs& a, RowState<D>& st, size_t ridx, bool first, bool last,
+                                           float vs, int g) {
+  // The merge is formed in place in st (which the caller then resets), one
+  // dim block at a time.  (The empty asm keeps the row's addresses from being
+  // computed ahead of the tile loop and held through it.)
+  asm volatile("" : "+v"(ridx));
+  float M = st.m, Z = st.z, wa = 0.f, wb = 0.f;
+  float* wu = a.ws_u + ridx * D + 4 * g;
+  if (!first) {
+    const f32x2 mz = *reinterpret_cast<const f32x2*>(a.ws_mz + 2 * ridx);
+    M = mz[0];
+    Z = mz[1];
+    merge_scalars(M, Z, st.m, st.z, wa, wb);
+  }
+  const float rz = final_rz(Z);
+  __bf16* out = a.out + ridx * D + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    if (!first) {
+      const f32x4 prev = *reinterpret_cast<const f32x4*>(wu + 16 * mb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.u[mb][j] = merge_value(prev[j], st.u[mb][j], wa, wb);
+    }
+    if (last) {
+      bf16x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = finalize(st.u[mb][j], vs, rz);
+      *reinterpret_cast<bf16x4*>(out + 16 * mb) = o;
+    } else {
+      *reinterpret_cast<f32x4*>(wu + 16 * mb) = st.u[mb];
+    }
+  }
+  if (!last && g == 0) *reinterpret_cast<f32x2*>(a.ws_mz + 2 * ridx) = f32x2{M, Z};
+}
+
 template <int D, bool FP8>
-__global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int kRB = row_blocks_per_wave<FP8>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   constexpr int kTileBytes = tile_lds_bytes<D>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  // Block index -> (sequence b, kv head, row block).  Workgroups go to the 8
-  // XCDs round robin (block i to XCD i mod 8), each XCD with its own L2.  The
-  // (b, kvh) pairs are dealt to the XCDs, and each XCD runs its pairs one
-  // after another, every pair's row blocks heaviest (last) first: the
+  // Block index -> (sequence b, kv head, workgroup row block).  Workgroups go
+  // to the 8 XCDs round robin (block i to XCD i mod 8), each XCD with its own
+  // L2.  The (b, kvh) pairs are dealt to the XCDs, and each XCD runs its pairs
+  // one after another, every pair's row blocks heaviest (last) first: the
   // workgroups resident on an XCD at a time are mostly row blocks of one pair
-  // and walk the same K/V tiles, which its L2 then serves.  When the pair count
-  // is not a multiple of 8 the order is simply row block (from the end), b, kvh.
+  // and walk the same K/V tiles, which its L2 then serves.  When the pair
+  // count is not a multiple of 8 the order is simply row block (from the
+  // end), b, kvh.
   const int pairs = a.B * a.Hkv;
   int pair, rbi;
   if (pairs % kXcds == 0) {
@@ -301,31 +392,38 @@ __global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_ke
   }
   const int kvh = pair % a.Hkv;
   const int b = pair / a.Hkv;
-  const int rb = a.max_row_blocks - 1 - rbi;
+  const int wrb = a.max_row_blocks - 1 - rbi;
   const int q0 = a.cu_q_lens[b];
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   int ql = a.cu_q_lens[b + 1] - q0;
   ql = ql < 0 ? 0 : (ql > a.max_q_len ? a.max_q_len : ql);
   if (q0 < 0 || q0 > a.total_q - ql) return;  // inconsistent cu_q_lens: stay in bounds
-  const int ppw = kRows / a.group;         // positions per wave
-  const int ppg = ppw * kPrefillWaves;     // positions per workgroup
-  const int i0 = rb * ppg;
+  const int ppr = kRows / a.group;                 // positions per row block
+  const int ppw = ppr * kRB;         // positions per wave
+  const int ppg = ppw * kPrefillWaves;             // positions per workgroup
+  const int i0 = wrb * ppg;
   if (i0 >= ql || n - ql + i0 < 0) return;  // uniform over the workgroup
   const int pmax_wg = n - ql + min(i0 + ppg, ql) - 1;
 
-  // This wave's rows.
-  const int iw = i0 + w * ppw;             // first position of the wave
-  const int i = iw + r / a.group;
-  const bool row_ok = r < ppw * a.group && i < ql;
-  const int p = n - ql + i;
-  const int limit = row_ok ? p : -1;
+  // This wave's rows: row block k holds positions iw + k ppr .. + ppr - 1.
+  const int iw = i0 + w * ppw;  // first position of the wave
   const int hq = kvh * a.group + r % a.group;
-  const QFrag<D> q = load_q<D>(a.q + ((size_t)(q0 + (row_ok ? i : i0)) * a.Hq + hq) * D, row_ok, g);
+  int limit[kRB], lo[kRB], ii[kRB];
+  bool row_ok[kRB];
+  QFrag<D> q[kRB];
+#pragma unroll
+  for (int k = 0; k < kRB; ++k) {
+    ii[k] = iw + k * ppr + r / a.group;
+    row_ok[k] = r < ppr * a.group && ii[k] < ql;
+    const int p = n - ql + ii[k];
+    limit[k] = row_ok[k] ? p : -1;
+    // Visible keys: lo..p per row, lo = 0 or p - w + 1 under a sliding
+    // window of w keys (Vosti App. A.5).
+    lo[k] = first_key(p, a.window);
+    q[k] = load_q<D>(a.q + ((size_t)(q0 + (row_ok[k] ? ii[k] : i0)) * a.Hq + hq) * D, row_ok[k], g);
+  }
   const int pmax_w = iw < ql ? n - ql + min(iw + ppw, ql) - 1 : -1;  // last position of the wave
   const int p_first = n - ql + iw;                                     // first position of the wave
-  // Visible keys: lo..p per row, lo = 0 or p - w + 1 under a sliding window
-  // of w keys (Vosti App. A.5).  lo_first / lo_last bound the wave's rows.
-  const int lo = first_key(p, a.window);
   const int lo_first = first_key(p_first, a.window);
   const int lo_last = first_key(pmax_w, a.window);
   // Whether the wave has a row that sees some key of tile t.
@@ -336,15 +434,20 @@ __global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_ke
 
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
-  const int T = pmax_wg / kTileKeys;                                   // last tile
-  const int T0 = first_key(n - ql + i0, a.window) / kTileKeys;         // first tile
-  // Pipeline.  LDS holds two tiles.  While the waves compute tile t from one
-  // slot, tile t+1 loads into the other: bf16 pages straight from memory into
+  const int T = pmax_wg / kTileKeys;                            // last tile
+  const int T0 = first_key(n - ql + i0, a.window) / kTileKeys;  // first tile
+  // Pipeline.  Tiles go in stages of kStageTiles (stage s = tiles 2s, 2s + 1)
+  // through two LDS slots: while the waves compute stage s from one slot,
+  // stage s + 1 loads into the other -- bf16 pages straight from memory into
   // LDS, e4m3 pages through registers (converted to bf16 after the compute).
-  // One barrier per tile publishes the next tile; a tile reaching past the
-  // sequence end gets its K and V zero filled between two barriers.
-  // Block-table entries run one tile ahead of the loads.
-  auto buf = [&](int t) { return lds_raw + (t & 1) * kTileBytes; };
+  // One barrier per stage publishes the next stage; a tile reaching past the
+  // sequence end gets its V zero filled between two barriers.  Tiles outside
+  // T0..T are never loaded nor computed.  Block-table entries run one stage
+  // ahead of the loads.
+  auto buf = [&](int t) {
+    return lds_raw + ((t / kStageTiles) & 1) * (kStageTiles * kTileBytes) + (t % kStageTiles) * kTileBytes;
+  };
+  auto in_range = [&](int t) { return t >= T0 && t <= T; };
   auto bt_of = [&](int t) { return load_tile_bt(bt_row, kTileKeys * (t < T ? t : T), nblk, lane); };
   auto pages_of = [&](int btv, int t) {
     const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
@@ -352,129 +455,150 @@ __global__ __launch_bounds__(kPrefillThreads, 8 / kPrefillWaves) void prefill_ke
     return tile_pages_of(e, t * kTileKeys, n, a.num_pages);
   };
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  Stage<D, FP8> stg;
-  {
-    const int bt0 = bt_of(T0);
-    const TilePages tp0 = pages_of(bt0, T0);
+  const int S0 = T0 / kStageTiles, S1 = T / kStageTiles;
+  Stage<D, FP8> stg[kStageTiles];
+  // Issues the loads of stage s (its tiles in T0..T); e4m3 pages land in stg.
+  auto issue = [&](int s, const int (&btv)[kStageTiles]) {
+#pragma unroll
+    for (int k = 0; k < kStageTiles; ++k) {
+      const int t = s * kStageTiles + k;
+      if (!in_range(t)) continue;  // uniform
+      if constexpr (FP8)
+        stage_load<D, FP8>(stg[k], a.k_cache, a.v_cache, btv[k], t * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
+      else
+        direct_issue<D>(buf(t), a.k_cache, a.v_cache, pages_of(btv[k], t), kvh, a.Hkv, wu, lane);
+    }
+  };
+  // After the stage's loads have landed and a barrier: e4m3 tiles are stored
+  // (FP8), bf16 tiles reaching past the sequence end are zero filled.
+  auto land = [&](int s, const int (&btv)[kStageTiles]) {
     if constexpr (FP8) {
-      stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt0, T0 * kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-      stage_store<D, FP8>(buf(T0), stg, tid);
+#pragma unroll
+      for (int k = 0; k < kStageTiles; ++k)
+        if (in_range(s * kStageTiles + k)) stage_store<D, FP8>(buf(s * kStageTiles + k), stg[k], tid);
+    } else {
+      bool partial = false;
+#pragma unroll
+      for (int k = 0; k < kStageTiles; ++k) {
+        const int t = s * kStageTiles + k;
+        if (in_range(t) && tile_partial(pages_of(btv[k], t))) {
+          direct_fixup<D>(buf(t), pages_of(btv[k], t), tid);
+          partial = true;
+        }
+      }
+      if (partial) __syncthreads();
+    }
+  };
+  int btn[kStageTiles];
+  {
+    int bt0[kStageTiles];
+#pragma unroll
+    for (int k = 0; k < kStageTiles; ++k) bt0[k] = bt_of(S0 * kStageTiles + k);
+    issue(S0, bt0);
+    __syncthreads();
+    if constexpr (FP8) {
+      land(S0, bt0);
       __syncthreads();
     } else {
-      direct_issue<D>(buf(T0), a.k_cache, a.v_cache, tp0, kvh, a.Hkv, wu, lane);
-      __syncthreads();
-      if (tile_partial(tp0)) {
-        direct_fixup<D>(buf(T0), tp0, tid);
-        __syncthreads();
-      }
+      land(S0, bt0);
     }
+#pragma unroll
+    for (int k = 0; k < kStageTiles; ++k) btn[k] = bt_of((S0 + 1) * kStageTiles + k);
   }
-  int bt_next = bt_of(T0 + 1);
 
-  RowState<D> st;
-  st.init();
-  float M = 0.f, Z = 0.f;
-  f32x4 U[D / 16];
+  RowState<D> st[kRB];
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) U[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int t = T0; t <= T; ++t) {
-    const int t0 = t * kTileKeys;
-    const bool more = t < T;
-    const int bt_after = bt_of(t + 2);
-    const TilePages tpn = pages_of(bt_next, t + 1);
-    const uint8_t* tile = buf(t);
-    if (more) {
-      if constexpr (FP8)
-        stage_load<D, FP8>(stg, a.k_cache, a.v_cache, bt_next, t0 + kTileKeys, n, a.num_pages, kvh, a.Hkv, tid);
-      else
-        direct_issue<D>(buf(t + 1), a.k_cache, a.v_cache, tpn, kvh, a.Hkv, wu, lane);
-    }
-    // The tile is whole for the wave when all its keys are visible to every
-    // stored row: its last key to the first position, its first key to the
-    // last position's window.
-    const bool whole = t0 + kTileKeys - 1 <= p_first && t0 >= lo_last;
-    // One tile step of the wave's rows; MASK = false for a whole tile.  LDS
-    // reads run one block ahead of the MFMAs that use them; the first V block
-    // is read before the softmax.
-    auto step = [&](auto mask) {
-      constexpr bool MASK = decltype(mask)::value;
-      f32x4 sc[4];
-      bf16x8 kf[2][D / 32];
-      lds_k_block<D>(tile, 0, r, g, kf[0]);
-      // A wave issuing its score or value MFMAs takes precedence over the
-      // other wave of its SIMD (another workgroup's), whose softmax then
-      // fills the issue slots between the MFMAs.
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        if (blk < 3) lds_k_block<D>(tile, blk + 1, r, g, kf[(blk + 1) & 1]);
-        sc[blk] = block_scores<D>(kf[blk & 1], q);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      bf16x8 vf[2][2];
-      lds_v_block<D>(tile, 0, r, g, vf[0]);
-      const TileStep ts = tile_softmax<MASK>(st.m, st.z, sc, c, t0, lo, limit, g);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int mb = 0; mb < D / 16; ++mb) {
-        if (mb + 1 < D / 16) lds_v_block<D>(tile, mb + 1, r, g, vf[(mb + 1) & 1]);
-        st.u[mb] = pv_block<MASK>(st.u[mb], vf[mb & 1], ts);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      commit_scalars<MASK>(st.m, st.z, ts);
-    };
-    if (needs(t)) {
-      if (whole)
-        step(std::false_type{});
-      else
-        step(std::true_type{});
-    }
-    if constexpr (FP8) {
-      if (more) stage_store<D, FP8>(buf(t + 1), stg, tid);
-    }
-    // Split end: fold this split's state into the rows that see a key of it;
-    // a row's first such split seeds its merge.
-    const int s = t0 / S;
-    if (t == T || (t0 + kTileKeys) % S == 0) {
-      if (limit >= s * S && lo < s * S + S) {
-        if (s == lo / S) {
-          M = st.m;
-          Z = st.z;
-#pragma unroll
-          for (int mb = 0; mb < D / 16; ++mb) U[mb] = st.u[mb];
-        } else {
-          float wa, wb;
-          merge_scalars(M, Z, st.m, st.z, wa, wb);
-#pragma unroll
-          for (int mb = 0; mb < D / 16; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) U[mb][j] = merge_value(U[mb][j], st.u[mb][j], wa, wb);
-        }
-      }
-      st.init();
-    }
-    if (more) {
-      __syncthreads();
-      if constexpr (!FP8) {
-        if (tile_partial(tpn)) {
-          direct_fixup<D>(buf(t + 1), tpn, tid);
-          __syncthreads();
-        }
-      }
-    }
-    bt_next = bt_after;
-  }
-  if (!row_ok) return;
-  const float rz = final_rz(Z);
+  for (int k = 0; k < kRB; ++k) st[k].init();
   const float vs = FP8 ? a.v_scale[kvh] : 1.0f;
-  __bf16* out = a.out + ((size_t)(q0 + i) * a.Hq + hq) * D;
+
+  for (int s = S0; s <= S1; ++s) {
+    const bool more = s < S1;
+    int bta[kStageTiles];
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) {
-    bf16x4 o;
+    for (int k = 0; k < kStageTiles; ++k) bta[k] = bt_of((s + 2) * kStageTiles + k);
+    if (more) issue(s + 1, btn);
+#pragma unroll 1
+    for (int kt = 0; kt < kStageTiles; ++kt) {
+      const int t = s * kStageTiles + kt;
+      if (!in_range(t)) continue;  // uniform
+      const int t0 = t * kTileKeys;
+      const uint8_t* tile = buf(t);
+      // The tile is whole for the wave when all its keys are visible to every
+      // stored row: its last key to the first position, its first key to the
+      // last position's window.
+      const bool whole = t0 + kTileKeys - 1 <= p_first && t0 >= lo_last;
+      // One tile step of the wave's row blocks; MASK = false for a whole tile.
+      // Each K and V fragment read from LDS feeds the MFMAs of both row
+      // blocks; LDS reads run one block ahead of the MFMAs that use them.
+      auto step = [&](auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
+        // Scores: each row block's chain over the head dim in ascending k-steps
+        // (block_scores' order), one K fragment feeding both chains.
+        f32x4 sc[kRB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = finalize(U[mb][j], vs, rz);
-    *reinterpret_cast<bf16x4*>(out + 16 * mb + 4 * g) = o;
+        for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+          for (int k = 0; k < kRB; ++k) sc[k][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 kf = lds_k_frag<D>(tile, blk, ks, r, g);
+#pragma unroll
+            for (int k = 0; k < kRB; ++k) sc[k][blk] = mfma(kf, q[k].f[ks], sc[k][blk]);
+          }
+        }
+        TileStep ts[kRB];
+        bool need = false;
+#pragma unroll
+        for (int k = 0; k < kRB; ++k) {
+          ts[k] = tile_softmax<MASK>(st[k].m, st[k].z, sc[k], c, t0, lo[k], limit[k], g);
+          need = need || rescale_lane<MASK>(ts[k]);
+        }
+        // Once a row's maximum settles its alpha is 1 and the rescale is the
+        // identity; a wave whose rows all have alpha = 1 skips it.
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+          for (int k = 0; k < kRB; ++k)
+#pragma unroll
+            for (int mb = 0; mb < D / 16; ++mb) st[k].u[mb] = pv_rescale<MASK>(st[k].u[mb], ts[k]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb) {
+          bf16x8 vf[2];
+#pragma unroll
+          for (int ks2 = 0; ks2 < 2; ++ks2) vf[ks2] = lds_v_frag<D>(tile, mb, ks2, r, g);
+#pragma unroll
+          for (int k = 0; k < kRB; ++k) st[k].u[mb] = pv_accumulate<MASK>(st[k].u[mb], vf, ts[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kRB; ++k) commit_scalars<MASK>(st[k].m, st[k].z, ts[k]);
+      };
+      if (needs(t)) {
+        if (whole)
+          step(std::false_type{});
+        else
+          step(std::true_type{});
+      }
+      // Split end: fold this split's state into the rows that see a key of
+      // it.  A row's first such split seeds its merge; a row that sees a
+      // later split finds the merge so far in the workspace.  The fold of a
+      // row's last split finalises the row.
+      const int sp = t0 / S;
+      if (t == T || (t0 + kTileKeys) % S == 0) {
+#pragma unroll
+        for (int k = 0; k < kRB; ++k) {
+          if (limit[k] >= sp * S && lo[k] < sp * S + S)
+            fold_split<D>(a, st[k], (size_t)(q0 + ii[k]) * a.Hq + hq, sp == lo[k] / S, sp == limit[k] / S, vs, g);
+          st[k].init();
+        }
+      }
+    }
+    if (more) {
+      __syncthreads();
+      land(s + 1, btn);
+      if constexpr (FP8) __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kStageTiles; ++k) btn[k] = bta[k];
   }
 }
 
@@ -482,7 +606,7 @@ template <int D, bool FP8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (a.B == 0 || a.max_q_len == 0) return hipSuccess;
   const int64_t units = (int64_t)a.B * a.max_row_blocks * a.Hkv;
-  const int lds = 2 * tile_lds_bytes<D>();  // two tile slots (64 KiB at head_dim 128)
+  const int lds = 2 * kStageTiles * tile_lds_bytes<D>();  // two slots of a stage (64 KiB at head_dim 128)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
@@ -490,7 +614,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-int prefill_positions_per_block(int group) { return (kRows / group) * kPrefillWaves; }
+int prefill_positions_per_block(int group, bool fp8) {
+  return (kRows / group) * (fp8 ? row_blocks_per_wave<true>() : row_blocks_per_wave<false>()) * kPrefillWaves;
+}
 
 hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st) {
   if (D == 128 && fp8) return launch_prefill_t<128, true>(a, st);

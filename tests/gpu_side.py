@@ -94,8 +94,10 @@ def prefill(ctx, pages: DevicePages, q: torch.Tensor, cu: np.ndarray, layout: wl
     mql = int(q_lens.max(initial=0)) if max_q_len is None else int(max_q_len)
     msl = int(max(seq_lens)) if max_seq_len is None else int(max_seq_len)
     out = torch.empty((q.shape[0], shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
+    nws = ia.ia_prefill_workspace_bytes(ctx, int(q.shape[0]), msl)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV) if nws else None
     ia.ia_paged_attn_prefill(ctx, qd, cu_d, sl, pages.k, pages.v, bt, mql, msl, out, pages.k_scale,
-                             pages.v_scale, stream=stream)
+                             pages.v_scale, workspace=ws, stream=stream)
     return out
 
 

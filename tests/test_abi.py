@@ -80,6 +80,11 @@ def test_workspace_size_formula():
                                                        + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 4 * 4))
     assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
                                                           + up(4 * 64 * 4))
+    # prefill: none while no row can see keys of two splits; else per (query row, head) the merge
+    # so far, d + 2 floats, in two arrays rounded up to 256 bytes
+    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2048) == 0
+    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2049) == up(1000 * 32 * 128 * 4) + up(1000 * 32 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 0, 4096) == 0
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
@@ -127,6 +132,13 @@ def test_append_and_prefill_argument_errors():
                None) == ia.IA_ERR_INVALID_ARG
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 0, 100, FAKE, None, 0,
                None) == ia.IA_ERR_INVALID_ARG  # rows but max_q_len 0
+    # keys past one split (128) need the workspace
+    assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, None, 0,
+               None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in ia.ia_last_error()
+    need = ia.ia_prefill_workspace_bytes(ctx, 10, 200)
+    assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, FAKE, need - 1,
+               None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_binding_constants_match_header():

@@ -15,6 +15,14 @@ SOURCES = sorted(f for f in os.listdir(CSRC)
                  if f.endswith(".hip") and "__global__" in open(os.path.join(CSRC, f)).read())
 
 
+def _file_flags(source):
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("ia_build", os.path.join(ROOT, "invariant_attention_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.FILE_FLAGS.get(source, [])
+
+
 def _hipcc():
     cand = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     return cand if os.path.exists(cand) else shutil.which("hipcc")
@@ -27,7 +35,8 @@ def test_no_scratch_and_no_spills(source, tmp_path):
         pytest.skip("hipcc is not available")
     out = tmp_path / (source + ".s")
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *_file_flags(source),
+           "-I", os.path.join(ROOT, "include"),
            "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, source)]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     assert proc.returncode == 0, proc.stderr[-2000:]
