@@ -330,35 +330,40 @@ __device__ __forceinline__ void lds_tile_scores(const uint8_t* tile, const QFrag
 template <int D>
 __device__ __forceinline__ void fold_split(const PrefillArgs& a, RowState<D>& st, size_t ridx, bool first, bool last,
                                            float vs, int g) {
-  // The merge is formed in place in st (which the caller then resets), one
-  // dim block at a time.  (The empty asm keeps the row's addresses from being
-  // computed ahead of the tile loop and held through it.)
+  // The merge is formed in place in st (which the caller then resets).  (The
+  // empty asm keeps the row's addresses from being computed ahead of the tile
+  // loop and held through it.)
   asm volatile("" : "+v"(ridx));
   float M = st.m, Z = st.z, wa = 0.f, wb = 0.f;
   float* wu = a.ws_u + ridx * D + 4 * g;
   if (!first) {
+    // All of the row's stored merge is loaded before any of it is used or
+    // overwritten: one wait for the loads, not one per dim block.
+    f32x4 prev[D / 16];
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) prev[mb] = *reinterpret_cast<const f32x4*>(wu + 16 * mb);
     const f32x2 mz = *reinterpret_cast<const f32x2*>(a.ws_mz + 2 * ridx);
     M = mz[0];
     Z = mz[1];
     merge_scalars(M, Z, st.m, st.z, wa, wb);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.u[mb][j] = merge_value(prev[mb][j], st.u[mb][j], wa, wb);
   }
-  const float rz = final_rz(Z);
-  __bf16* out = a.out + ridx * D + 4 * g;
+  if (last) {
+    const float rz = final_rz(Z);
+    __bf16* out = a.out + ridx * D + 4 * g;
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) {
-    if (!first) {
-      const f32x4 prev = *reinterpret_cast<const f32x4*>(wu + 16 * mb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.u[mb][j] = merge_value(prev[j], st.u[mb][j], wa, wb);
-    }
-    if (last) {
+    for (int mb = 0; mb < D / 16; ++mb) {
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = finalize(st.u[mb][j], vs, rz);
       *reinterpret_cast<bf16x4*>(out + 16 * mb) = o;
-    } else {
-      *reinterpret_cast<f32x4*>(wu + 16 * mb) = st.u[mb];
     }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) *reinterpret_cast<f32x4*>(wu + 16 * mb) = st.u[mb];
   }
   if (!last && g == 0) *reinterpret_cast<f32x2*>(a.ws_mz + 2 * ridx) = f32x2{M, Z};
 }
