@@ -334,6 +334,9 @@ def summarize_spread_profile(trace_dir):
 PREFILL_KERNEL = "prefill_kernel<128, false>"
 PREFILL_SQ = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
               "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES"]
+# A second pass: issue, co-execution and waits (the SQ block takes at most 8 counters a run).
+PREFILL_SQ2 = ["SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES",
+               "SQ_INSTS_VALU_TRANS_F32", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_LDS"]
 
 
 LAYER_SHAPES = [("qkv_proj", 8192, 6144, 4096), ("down_proj", 8192, 4096, 14336), ("qkv_proj", 256, 6144, 4096),
@@ -424,7 +427,7 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
     lens = [4096] * 8
     flops = 4.0 * shape.d * shape.Hq * sum(n * (n + 1) / 2 for n in lens)
     kv_unique = sum(lens) * shape.Hkv * shape.d * 2 * 2
-    pm = {c: _pmc_mean(pmc_dir, "prefill", c, PREFILL_KERNEL) for c in PREFILL_SQ}
+    pm = {c: _pmc_mean(pmc_dir, "prefill", c, PREFILL_KERNEL) for c in PREFILL_SQ + PREFILL_SQ2}
     fetch_kib, nf = _pmc_mean(pmc_dir, "prefill", "FETCH_SIZE", PREFILL_KERNEL)
     write_kib, nw = _pmc_mean(pmc_dir, "prefill", "WRITE_SIZE", PREFILL_KERNEL)
     copy_fetch, _ = _pmc_mean(pmc_dir, "copy", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
@@ -436,10 +439,14 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
                  f"python3 bench.py --prefill-only --steps {PREFILL_PROFILE_STEPS} --warmup 30")
     cmd_sq = ("rocprofv3 --pmc " + " ".join(PREFILL_SQ) + " --output-format csv -d <out> -o pmc -- "
               "python3 bench.py --prefill-only --steps 3 --warmup 1")
+    cmd_sq2 = ("rocprofv3 --pmc " + " ".join(PREFILL_SQ2) + " --output-format csv -d <out> -o pmc -- "
+               "python3 bench.py --prefill-only --steps 3 --warmup 1")
     cmd_pmc = ("rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- "
                "python3 bench.py --prefill-only --steps 3 --warmup 1")
     cmd_copy = "rocprofv3 --pmc {C} --output-format csv -d <out> -o pmc -- python3 bench.py --copy-probe --steps 3"
     tf = flops / avg_ns / 1e3
+    ws_rows = sum(max(0, n - shape.S) for n in lens) * shape.Hq  # rows that see two splits
+    ws_bytes = ws_rows * (shape.d + 2) * 4
     lines = [
         "# prefill_kernel<128, bf16> -- Qwen3-8B-shaped whole prefill, 8 prompts x 4096 tokens, causal",
         "",
@@ -482,6 +489,21 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
         "Executed over algorithmic flops is 1.5 plus masking waste: each weight is carried as a bf16 hi/lo "
         "pair, so the value product runs two MFMAs per k-step.",
         "",
+        "Second pass (issue, co-execution and waits):",
+        "",
+        f"    {cmd_sq2}",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+    ]
+    for c in PREFILL_SQ2:
+        lines.append(f"| {c} per dispatch (mean of {pm[c][1]}) | {pm[c][0]:.4e} |")
+    coexec = pm["SQ_VALU_MFMA_COEXEC_CYCLES"][0] / pm["SQ_VALU_MFMA_BUSY_CYCLES"][0]
+    lines += [
+        f"| VALU-MFMA co-execution cycles / MFMA busy cycles | {coexec:.4f} |",
+        f"| exp2 (SQ_INSTS_VALU_TRANS_F32) / MFMA instructions | "
+        f"{pm['SQ_INSTS_VALU_TRANS_F32'][0] / pm['SQ_INSTS_MFMA'][0]:.4f} |",
+        "",
         "## HBM traffic (rocprofv3 --pmc, one counter per run)",
         "",
         f"    {cmd_pmc.format(C='FETCH_SIZE')}",
@@ -498,6 +520,7 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
         f"| HBM bytes written per launch | {write_kib * 1024 * w_scale:.4e} |",
         f"| distinct K/V bytes (read at least once) | {kv_unique:.4e} |",
         f"| Q bytes read + O bytes written | {2 * sum(lens) * shape.Hq * shape.d * 2:.4e} |",
+        f"| split-merge workspace bytes written, then read (rows past the first split) | {ws_bytes:.4e} |",
         "",
     ]
     os.makedirs(os.path.dirname(PREFILL_PROFILE_MD), exist_ok=True)
