@@ -318,11 +318,10 @@ ia_status ia_rmsnorm(const void* x, const void* weight, int32_t M, int32_t H, fl
  * row of C depends on its row of A and on W only, never on M.  Two tiles
  * (chosen from M, N and K only to fill the chip; the same bits either way):
  *  - 256 x 256 outputs, 8 waves, when it gives at least one workgroup per
- *    compute unit: K steps of 64 in a 2-slot LDS ring when K % 64 == 0, else
- *    32 in a 4-slot ring;
- *  - 64 x 64 outputs, 4 waves, otherwise: K steps of 128 when K % 128 == 0
- *    (4 slots when its tiles fit one round of the compute units, else 2),
- *    else 32 in 4 slots.
+ *    compute unit: K steps of 64 when K % 64 == 0, else 32;
+ *  - 64 x 64 outputs, 4 waves, otherwise: K steps of 128 when K % 128 == 0,
+ *    else 32.
+ * Both go through a two-slot LDS ring, one K step ahead.
  *   a  dev [M][K] bf16 (row-major activations, one row per token)
  *   w  dev [N][K] bf16 (a linear layer's weight, one row per output feature)
  *   c  dev [M][N] bf16

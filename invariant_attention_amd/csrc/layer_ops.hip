@@ -18,16 +18,17 @@
 // row's place in that tile, or on the other rows.  Two tiles, chosen from M,
 // N and K only to fill the chip (the same bits either way):
 //  - 256 x 256 outputs, 8 waves of 128 x 64 (two per SIMD), when it gives at
-//    least one workgroup per compute unit; K steps of 64 in a 2-slot LDS ring
-//    when K % 64 == 0, else 32 in a 4-slot ring;
+//    least one workgroup per compute unit; K steps of 64 when K % 64 == 0,
+//    else 32;
 //  - 64 x 64 outputs, 4 waves of 32 x 32, otherwise; K steps of 128 when
-//    K % 128 == 0 (a 4-slot ring when its tiles fit one round of the compute
-//    units, else 2 slots), else 32 in 4 slots.
-// A/W tiles go from memory straight into the LDS ring (global_load_lds),
-// slots - 1 K steps ahead; each stage is waited for with vmcnt(0) before the
-// barrier that publishes it.
+//    K % 128 == 0, else 32.
+// A/W tiles go from memory straight into a two-slot LDS ring
+// (global_load_lds), one K step ahead; each stage is waited for with
+// vmcnt(0) before the barrier that publishes it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "launch.hpp"
 
@@ -130,32 +131,14 @@ using BigTileK64 = Tile<256, 256, 2, 4, 64>;    // the same, K steps of 64 (K % 
 using SmallTile = Tile<64, 64, 2, 2, 32>;       // 4 waves of 32 x 32, for calls with few big tiles
 using SmallTileK128 = Tile<64, 64, 2, 2, 128>;  // the same with 4x the work between barriers
 
-// Issues the copies of K step kt of A rows m0.. and W rows n0.. into a slot.
-// Copy i of wave w fills the kRowsPerCopy tile rows from kRowsPerCopy (i *
-// waves + w); lane l writes row + l / kChunks, position l % kChunks, from
-// chunk swz(row, l % kChunks) of that row.  Rows past M read row M - 1 (never
-// stored).
-template <class T>
-__device__ __forceinline__ void gemm_issue(uint8_t* slot, const __bf16* a, const __bf16* wt, int M, int K, int m0,
-                                           int n0, int kt, int w, int lane) {
-  const int k0 = kt * T::BK;
-#pragma unroll
-  for (int i = 0; i < T::kALoads; ++i) {
-    const int r0 = (i * T::kWaves + w) * T::kRowsPerCopy;
-    const int row = r0 + lane / T::kChunks;
-    int m = m0 + row;
-    m = m < M ? m : M - 1;
-    const __bf16* src = a + (size_t)m * K + k0 + 8 * T::swz(row, lane % T::kChunks);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + r0 * T::kRowBytes), 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < T::kBLoads; ++i) {
-    const int r0 = (i * T::kWaves + w) * T::kRowsPerCopy;
-    const int row = r0 + lane / T::kChunks;
-    const __bf16* src = wt + (size_t)(n0 + row) * K + k0 + 8 * T::swz(row, lane % T::kChunks);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)(slot + T::kATileBytes + r0 * T::kRowBytes), 16,
-                                     0, 0);
-  }
+// A wave-uniform pointer made opaque to the optimiser (an empty asm on its
+// SGPR pair): a 32-bit lane offset added to it then stays a VGPR offset on a
+// scalar base (the loads' saddr form), instead of a 64-bit per-lane address
+// recomputed at every use.
+__device__ __forceinline__ const uint8_t* uniform_base(const uint8_t* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<const uint8_t*>(v);
 }
 
 // Waits until every copy this wave has issued has landed in LDS, then meets
@@ -167,11 +150,18 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Every address the K loop needs is formed before it: each copy is a scalar
+// base (the tile's first row at the K step) plus the lane's 32-bit offset, and
+// each fragment read is a per-lane LDS address of (slot, 16-k step) plus an
+// immediate for the 32-row block.  The loop itself then issues copies, LDS
+// reads and MFMAs with no vector address arithmetic: measured, that
+// arithmetic cost a quarter of the kernel's time, because a wave's VALU and
+// MFMA instructions here hardly overlap.
 template <class T>
 __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __restrict__ a,
                                                                const __bf16* __restrict__ wt,
                                                                __bf16* __restrict__ c, int M, int N, int K) {
-  constexpr int MI = T::kMI, NI = T::kNI;
+  constexpr int MI = T::kMI, NI = T::kNI, KS = T::BK / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,7 +171,68 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
   const int n0 = (blockIdx.x % ntn) * T::BN;
   const int m0 = (blockIdx.x / ntn) * T::BM;
   const int KT = K / T::BK;
-  auto slot = [&](int kt) { return lds + (kt % T::kStages) * T::kStageBytes; };
+
+  // Copy i of wave w fills the kRowsPerCopy tile rows from r0 = kRowsPerCopy
+  // (i * waves + w); lane l writes row r0 + l / kChunks, position l %
+  // kChunks, from chunk swz(row, l % kChunks) of that row.  Rows past M read
+  // row M - 1 (never stored).  Offsets are bytes from the tile's first row
+  // at k = 0; row * K * 2 < 2^32 for every supported K.
+  const int crow = lane / T::kChunks, cpos = lane % T::kChunks;
+  uint32_t offa[T::kALoads], offb[T::kBLoads];
+#pragma unroll
+  for (int i = 0; i < T::kALoads; ++i) {
+    const int row = (i * T::kWaves + w) * T::kRowsPerCopy + crow;
+    const int m = m0 + row < M ? row : M - 1 - m0;
+    offa[i] = ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)T::swz(row, cpos)) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kBLoads; ++i) {
+    const int row = (i * T::kWaves + w) * T::kRowsPerCopy + crow;
+    offb[i] = ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)T::swz(row, cpos)) * 2u;
+  }
+  const uint8_t* ga = reinterpret_cast<const uint8_t*>(a + (size_t)m0 * K);
+  const uint8_t* gb = reinterpret_cast<const uint8_t*>(wt + (size_t)n0 * K);
+  // Issues the copies of K step kt into slot s.
+  auto issue = [&](int s, int kt) {
+    uint8_t* slot = lds + s * T::kStageBytes;
+    const uint8_t* ba = uniform_base(ga + (size_t)kt * (T::BK * 2));
+    const uint8_t* bb = uniform_base(gb + (size_t)kt * (T::BK * 2));
+    // (The empty asm keeps each offset a 32-bit value at its use, so that the
+    // load takes the scalar base + 32-bit offset form rather than a 64-bit
+    // address formed in vector registers.)
+#pragma unroll
+    for (int i = 0; i < T::kALoads; ++i) asm volatile("" : "+v"(offa[i]));
+#pragma unroll
+    for (int i = 0; i < T::kBLoads; ++i) asm volatile("" : "+v"(offb[i]));
+#pragma unroll
+    for (int i = 0; i < T::kALoads; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(ba + offa[i]),
+                                       (lds_ptr_t*)(slot + (i * T::kWaves + w) * T::kRowsPerCopy * T::kRowBytes), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < T::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (gbl_ptr_t*)(bb + offb[i]),
+          (lds_ptr_t*)(slot + T::kATileBytes + (i * T::kWaves + w) * T::kRowsPerCopy * T::kRowBytes), 16, 0, 0);
+  };
+  // Fragment reads: the lane's 8 k of 16-k step ks sit in chunk ch = 2 ks +
+  // kh of its row, at position swz(row, ch) = ch ^ x: rows of the wave's
+  // blocks differ from the lane's first row by multiples of 32, which leave x
+  // unchanged.  The 32-row block index is an immediate offset.
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int x = (r32 / (16 / T::kChunks)) & (T::kChunks - 1);
+  uint32_t ra[2][KS], rb[2][KS];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t pos = (uint32_t)(((2 * ks + kh) ^ x) * 16);
+      ra[s][ks] = (uint32_t)(s * T::kStageBytes + (wm * 32 * MI + r32) * T::kRowBytes) + pos;
+      rb[s][ks] = (uint32_t)(s * T::kStageBytes + T::kATileBytes + (wn * 32 * NI + r32) * T::kRowBytes) + pos;
+      // Opaque to the optimiser, so that the addresses stay in registers
+      // instead of being formed again by adds inside the loop.
+      asm volatile("" : "+v"(ra[s][ks]), "+v"(rb[s][ks]));
+    }
 
   lf32x16 acc[MI][NI];
 #pragma unroll
@@ -189,31 +240,22 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = lf32x16{};
 
-  for (int s = 0; s < T::kStages - 1; ++s)
-    if (s < KT) gemm_issue<T>(slot(s), a, wt, M, K, m0, n0, s, w, lane);
-  const int r32 = lane & 31, kh = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    // Step kt's copies have landed; those of step kt + 1 are issued next,
-    // into the slot every wave has finished reading.
+  if (KT > 0) issue(0, 0);
+  // One K step from slot S (a compile-time constant: the loop is unrolled by
+  // the ring's two slots).
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int S = decltype(slot_c)::value;
+    // Step kt's copies have landed; those of step kt + 1 go to the other
+    // slot, which every wave has finished reading.
     stage_barrier();
-    if (kt + T::kStages - 1 < KT)
-      gemm_issue<T>(slot(kt + T::kStages - 1), a, wt, M, K, m0, n0, kt + T::kStages - 1, w, lane);
-    const uint8_t* sa = slot(kt);
-    const uint8_t* sb = sa + T::kATileBytes;
-    // Operand fragments of the lane's 8 k of each 16-k step; the reads of
-    // step ks + 1 are issued before the MFMAs of step ks.
+    if (kt + 1 < KT) issue(S ^ 1, kt + 1);
     auto frags = [&](int ks, lbf16x8 (&af)[MI], lbf16x8 (&bf)[NI]) {
-      const int ch = 2 * ks + kh;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * (32 * MI) + mi * 32 + r32;
-        af[mi] = *reinterpret_cast<const lbf16x8*>(sa + row * T::kRowBytes + T::swz(row, ch) * 16);
-      }
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const lbf16x8*>(lds + ra[S][ks] + mi * 32 * T::kRowBytes);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int row = wn * (32 * NI) + ni * 32 + r32;
-        bf[ni] = *reinterpret_cast<const lbf16x8*>(sb + row * T::kRowBytes + T::swz(row, ch) * 16);
-      }
+      for (int ni = 0; ni < NI; ++ni)
+        bf[ni] = *reinterpret_cast<const lbf16x8*>(lds + rb[S][ks] + ni * 32 * T::kRowBytes);
     };
     lbf16x8 af[2][MI], bf[2][NI];
     frags(0, af[0], bf[0]);
@@ -221,15 +263,15 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
     // MFMAs takes precedence over the other's fragment reads and copies.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < T::BK / 16; ++ks) {
-      if (ks + 1 < T::BK / 16) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bf[ks & 1][ni], acc[mi][ni], 0, 0, 0);
       if constexpr (MI * NI >= MI + NI) {
-        if (ks + 1 < T::BK / 16) {
+        if (ks + 1 < KS) {
           // One LDS read after each of the first MFMAs of this step.
 #pragma unroll
           for (int i = 0; i < MI + NI; ++i) {
@@ -241,6 +283,10 @@ __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __re
       }
     }
     __builtin_amdgcn_s_setprio(0);
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
   }
   // Output element (row, col) of a 32 x 32 accumulator sits in lane col +
   // 32 * ((row / 4) % 2), register 4 * (row / 8) + row % 4.  A wave whose
