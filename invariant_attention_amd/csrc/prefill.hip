@@ -26,16 +26,20 @@
 // (global_load_lds, 1 KiB runs of K and V), with a zero fill of the keys past
 // the sequence end only in a tile that has them; e4m3 pages go through
 // registers, where they are zero filled and converted to bf16 (exactly).
-// K keeps the pages' own layout; V is staged in operand order:
+// K and V keep the pages' own order, in 1 KiB runs of one page block each:
 //   LDS K: [4 blocks][D/8 chunks][16 positions] x 16 B, K slot s of a page
 //          at position s (even page blocks) or s ^ 8 (odd ones)
-//   LDS V: [2 k-steps][D/16 dim blocks][64 lanes] x 16 B, lane 16 g + r
-//          holding dim 16 mb + r, tokens 8 (g % 2) .. + 7 of page block
-//          2 ks2 + g / 2 (its V^T operand of the value product)
-// Every operand fragment is one 16-byte LDS read per lane.  A K read takes 8
-// consecutive slots of each of two page blocks (arith.hpp's key-to-slot
-// mapping); the swap of 128-byte halves in odd page blocks puts them on
-// disjoint banks.  A V read is 1 KiB in lane order.
+//   LDS V: [4 blocks][D/32 runs][64 units] x 16 B, run j holding dims 32 j ..
+//          32 j + 31 of the block; unit 2 dl + (h ^ (dl / 8 % 2)) holds
+//          tokens 8 h .. 8 h + 7 of dim 32 j + dl
+// so every copy reads one page block (a scalar page base and a fixed lane
+// offset), and every operand fragment is one 16-byte LDS read per lane.  A K
+// read takes 8 consecutive slots of each of two page blocks (arith.hpp's
+// key-to-slot mapping); the swap of 128-byte halves in odd page blocks puts
+// them on disjoint banks.  A V read (lane 16 g + r: dim 16 mb + r, tokens
+// 8 (g % 2) .. of page block 2 ks2 + g / 2, its V^T operand of the value
+// product) takes in each quarter-wave 16 dims of one run, whose alternating
+// unit order puts the two halves of the run on disjoint banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,17 +80,20 @@ constexpr int tile_lds_bytes() {
 // blocks (the map is its own inverse).
 __device__ __forceinline__ int k_pos(int blk, int s) { return s ^ ((blk & 1) << 3); }
 
-// The page block, and the byte offset of the V run inside its (page, kv head)
-// block, held by 16-byte unit c of a tile's LDS V (unit c = run c / 64 =
-// (ks2, mb), lane c % 64 of that run's operand).
+// Token half h and dim (within its 32-dim run) held by unit l of an LDS V run.
+__device__ __forceinline__ int v_run_dim(int l) { return l >> 1; }
+__device__ __forceinline__ int v_run_half(int l) { return (l & 1) ^ ((l >> 4) & 1); }
+
+// The page block, and the byte offset inside its (page, kv head) block, of
+// the 8 tokens held by 16-byte unit c of a tile's LDS V (run c / 64 = block
+// p, dims 32 j..; unit c % 64 of the run).
 template <int D, bool FP8>
 __device__ __forceinline__ void v_unit(int c, int& blk, uint32_t& off, int& first_tok) {
   const int run = c >> 6, l = c & 63;
-  const int ks2 = run / (D / 16), mb = run % (D / 16);
-  const int r = l & 15, g = l >> 4;
-  blk = v_block(ks2, g);
-  off = v_frag_off<D, FP8>(mb, r, g);
-  first_tok = 8 * (g & 1);
+  blk = run / (D / 32);
+  const int dim = 32 * (run % (D / 32)) + v_run_dim(l);
+  first_tok = 8 * v_run_half(l);
+  off = (uint32_t)((dim * 16 + first_tok) * Raw<FP8>::kElemBytes);
 }
 
 // Staging registers of one thread for one tile (e4m3 pages).
@@ -229,9 +236,12 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
   // for an odd page block.  A V copy's lane takes its run from page block
   // 2 ks2 + (lane / 32) at v_frag_off.
   __builtin_assume(w >= 0 && w < kPrefillWaves);  // so that the chunk -> page block map folds
-  const uint32_t k_even = (uint32_t)lane * 16;
-  const uint32_t k_odd = (uint32_t)((lane & ~15) | k_pos(1, lane & 15)) * 16;
-  const int r = lane & 15, g = lane >> 4;
+  uint32_t k_even = (uint32_t)lane * 16;
+  uint32_t k_odd = (uint32_t)((lane & ~15) | k_pos(1, lane & 15)) * 16;
+  uint32_t v_lane = (uint32_t)((v_run_dim(lane) * 16 + 8 * v_run_half(lane)) * 2);
+  // Opaque 32-bit offsets: each copy then takes the scalar base + 32-bit
+  // offset form, instead of a 64-bit address formed in vector registers.
+  asm volatile("" : "+v"(k_even), "+v"(k_odd), "+v"(v_lane));
 #pragma unroll
   for (int i = 0; i < kChunks / kPrefillWaves; ++i) {
     const int ch = i * kPrefillWaves + w;  // wave-uniform
@@ -240,11 +250,11 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
     const uint8_t* kb = sgpr_base(head(kc, pg) + part * 1024);
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(kb + ((blk & 1) ? k_odd : k_even)), (lds_void_t*)(slot + ch * 1024),
                                      16, 0, 0);
-    const int ks2 = ch / (D / 16), mb = ch % (D / 16);
-    const uint8_t* vb0 = sgpr_base(head(vc, ks2 == 0 ? tp.page[0] : tp.page[2]));
-    const uint8_t* vb1 = sgpr_base(head(vc, ks2 == 0 ? tp.page[1] : tp.page[3]));
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)((lane < 32 ? vb0 : vb1) + v_frag_off<D, false>(mb, r, g)),
-                                     (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
+    // V run ch: dims 32 j .. of page block p, 1 KiB of one page.
+    const int p = ch / (D / 32), j = ch % (D / 32);
+    const int vpg = p == 0 ? tp.page[0] : (p == 1 ? tp.page[1] : (p == 2 ? tp.page[2] : tp.page[3]));
+    const uint8_t* vb = sgpr_base(head(vc, vpg) + j * 1024);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(vb + v_lane), (lds_void_t*)(slot + kKBytes + ch * 1024), 16, 0, 0);
   }
 }
 
@@ -272,20 +282,9 @@ __device__ __forceinline__ bool tile_partial(const TilePages& tp) {
   return (tp.valid[0] & tp.valid[1] & tp.valid[2] & tp.valid[3]) != 16;
 }
 
-// Operand fragments of one tile from LDS: the K of score block sb (the key
-// of MFMA row r lies in page block k_block(sb, r)), and the V^T runs of dim
-// block mb (lane order).
-template <int D>
-__device__ __forceinline__ void lds_k_block(const uint8_t* lds, int sb, int r, int g, bf16x8 (&kf)[D / 32]) {
-  const int blk = k_block(sb, r);
-  const int pos = k_pos(blk, k_slot(k_token(sb, r)));
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    kf[ks] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + ((size_t)(blk * (D / 8) + 4 * ks + g) * 16 + pos) * 16));
-}
-// One K fragment (k-step ks of score block sb) and one V fragment (k-step
-// ks2 of dim block mb).
+// Operand fragments of one tile from LDS: the K of k-step ks of score block
+// sb (the key of MFMA row r lies in page block k_block(sb, r)), and the V^T
+// run of k-step ks2 of dim block mb.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_k_frag(const uint8_t* lds, int sb, int ks, int r, int g) {
   const int blk = k_block(sb, r);
@@ -296,28 +295,9 @@ __device__ __forceinline__ bf16x8 lds_k_frag(const uint8_t* lds, int sb, int ks,
 template <int D>
 __device__ __forceinline__ bf16x8 lds_v_frag(const uint8_t* lds, int mb, int ks2, int r, int g) {
   constexpr int kKBytes = kTileKeys * D * 2;
-  return __builtin_bit_cast(
-      bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + (ks2 * (D / 16) + mb) * 1024 + (16 * g + r) * 16));
-}
-template <int D>
-__device__ __forceinline__ void lds_v_block(const uint8_t* lds, int mb, int r, int g, bf16x8 (&vf)[2]) {
-  constexpr int kKBytes = kTileKeys * D * 2;
-#pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2)
-    vf[ks2] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + (ks2 * (D / 16) + mb) * 1024 + (16 * g + r) * 16));
-}
-
-// Scores of one tile for the wave's rows, from the LDS copy of its K.
-template <int D>
-__device__ __forceinline__ void lds_tile_scores(const uint8_t* tile, const QFrag<D>& q, int r, int g,
-                                                f32x4 (&sc)[4]) {
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    bf16x8 kf[D / 32];
-    lds_k_block<D>(tile, blk, r, g, kf);
-    sc[blk] = block_scores<D>(kf, q);
-  }
+  const int run = v_block(ks2, g) * (D / 32) + (mb >> 1);
+  const int unit = 2 * (16 * (mb & 1) + r) + ((g & 1) ^ ((r >> 3) & 1));
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + run * 1024 + unit * 16));
 }
 
 // Folds the state of one split into the merge of the lane's row (row index
