@@ -29,17 +29,18 @@
 // K and V keep the pages' own order, in 1 KiB runs of one page block each:
 //   LDS K: [4 blocks][D/8 chunks][16 positions] x 16 B, K slot s of a page
 //          at position s (even page blocks) or s ^ 8 (odd ones)
-//   LDS V: [4 blocks][D/32 runs][64 units] x 16 B, run j holding dims 32 j ..
-//          32 j + 31 of the block; unit 2 dl + (h ^ (dl / 8 % 2)) holds
-//          tokens 8 h .. 8 h + 7 of dim 32 j + dl
+//   LDS V: [4 blocks][D/32 runs][2 dim halves][2 token halves][16 dims]
+//          x 16 B: run j holds dims 32 j .. 32 j + 31 of the block, unit
+//          32 (dl / 16) + 16 h + dl % 16 tokens 8 h .. 8 h + 7 of dim 32 j + dl
 // so every copy reads one page block (a scalar page base and a fixed lane
 // offset), and every operand fragment is one 16-byte LDS read per lane.  A K
 // read takes 8 consecutive slots of each of two page blocks (arith.hpp's
 // key-to-slot mapping); the swap of 128-byte halves in odd page blocks puts
 // them on disjoint banks.  A V read (lane 16 g + r: dim 16 mb + r, tokens
 // 8 (g % 2) .. of page block 2 ks2 + g / 2, its V^T operand of the value
-// product) takes in each quarter-wave 16 dims of one run, whose alternating
-// unit order puts the two halves of the run on disjoint banks.
+// product) takes 512 contiguous bytes of one run in each half-wave, which
+// the LDS serves as fast as a read in lane order (measured on MI355X: a
+// 32-byte lane stride inside the run halves the rate).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,9 +81,9 @@ constexpr int tile_lds_bytes() {
 // blocks (the map is its own inverse).
 __device__ __forceinline__ int k_pos(int blk, int s) { return s ^ ((blk & 1) << 3); }
 
-// Token half h and dim (within its 32-dim run) held by unit l of an LDS V run.
-__device__ __forceinline__ int v_run_dim(int l) { return l >> 1; }
-__device__ __forceinline__ int v_run_half(int l) { return (l & 1) ^ ((l >> 4) & 1); }
+// Dim (within its 32-dim run) and token half held by unit l of an LDS V run.
+__device__ __forceinline__ int v_run_dim(int l) { return 16 * (l >> 5) + (l & 15); }
+__device__ __forceinline__ int v_run_half(int l) { return (l >> 4) & 1; }
 
 // The page block, and the byte offset inside its (page, kv head) block, of
 // the 8 tokens held by 16-byte unit c of a tile's LDS V (run c / 64 = block
@@ -296,7 +297,7 @@ template <int D>
 __device__ __forceinline__ bf16x8 lds_v_frag(const uint8_t* lds, int mb, int ks2, int r, int g) {
   constexpr int kKBytes = kTileKeys * D * 2;
   const int run = v_block(ks2, g) * (D / 32) + (mb >> 1);
-  const int unit = 2 * (16 * (mb & 1) + r) + ((g & 1) ^ ((r >> 3) & 1));
+  const int unit = 32 * (mb & 1) + 16 * (g & 1) + r;
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + kKBytes + run * 1024 + unit * 16));
 }
 
@@ -456,6 +457,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   };
   // After the stage's loads have landed and a barrier: e4m3 tiles are stored
   // (FP8), bf16 tiles reaching past the sequence end are zero filled.
+  // Whether tile t needs a V zero fill: tile_partial of its pages, tested on
+  // the entries directly (scalar compares: a tile is whole when it ends
+  // inside the sequence and all four of its entries are in range).
+  auto tile_short = [&](int btv, int t) {
+    bool bad = (t + 1) * kTileKeys > n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = __builtin_amdgcn_readlane(btv, j);
+      bad = bad || e < 0 || e >= a.num_pages;
+    }
+    return bad;
+  };
   auto land = [&](int s, const int (&btv)[kStageTiles]) {
     if constexpr (FP8) {
 #pragma unroll
@@ -466,7 +479,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 #pragma unroll
       for (int k = 0; k < kStageTiles; ++k) {
         const int t = s * kStageTiles + k;
-        if (in_range(t) && tile_partial(pages_of(btv[k], t))) {
+        if (in_range(t) && tile_short(btv[k], t)) {
           direct_fixup<D>(buf(t), pages_of(btv[k], t), tid);
           partial = true;
         }
