@@ -126,13 +126,11 @@ __device__ __forceinline__ int select4(int blk, const int (&x)[4]) {
 // Issues the global loads of the tile at t0 for this thread's share.  btv
 // holds the tile's block-table entries in lanes 0..3.
 template <int D, bool FP8>
-__device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc, const uint8_t* vc, int btv, int t0,
+__device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc, const uint8_t* vc, const int4& e, int t0,
                                            int n, int num_pages, int kvh, int Hkv, int tid) {
   using S = Stage<D, FP8>;
   constexpr int EB = Raw<FP8>::kElemBytes;
   constexpr size_t kHeadBytes = (size_t)D * 16 * EB;
-  const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
-                           __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
   const TilePages tp = tile_pages_of(e, t0, n, num_pages);
 #pragma unroll
   for (int i = 0; i < S::kKPer; ++i) {
@@ -434,17 +432,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
     return lds_raw + ((t / kStageTiles) & 1) * (kStageTiles * kTileBytes) + (t % kStageTiles) * kTileBytes;
   };
   auto in_range = [&](int t) { return t >= T0 && t <= T; };
-  auto bt_of = [&](int t) { return load_tile_bt(bt_row, kTileKeys * (t < T ? t : T), nblk, lane); };
-  auto pages_of = [&](int btv, int t) {
-    const int4 e = make_int4(__builtin_amdgcn_readlane(btv, 0), __builtin_amdgcn_readlane(btv, 1),
-                             __builtin_amdgcn_readlane(btv, 2), __builtin_amdgcn_readlane(btv, 3));
-    return tile_pages_of(e, t * kTileKeys, n, a.num_pages);
+  // A tile's 4 block-table entries, by scalar loads (wave-uniform indices,
+  // clamped to the sequence's last block: blocks past it hold no keys).  The
+  // table is read through the constant address space, which is what lets the
+  // loads be scalar: nothing writes it during the call.
+  const __attribute__((address_space(4))) int32_t* bt_const =
+      (const __attribute__((address_space(4))) int32_t*)bt_row;
+  auto bt_of = [&](int t) {
+    const int e0 = (t < T ? t : T) * (kTileKeys / 16);
+    auto ent = [&](int j) { return bt_const[e0 + j < nblk ? e0 + j : nblk - 1]; };
+    return make_int4(ent(0), ent(1), ent(2), ent(3));
   };
+  auto pages_of = [&](const int4& e, int t) { return tile_pages_of(e, t * kTileKeys, n, a.num_pages); };
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int S0 = T0 / kStageTiles, S1 = T / kStageTiles;
   Stage<D, FP8> stg[kStageTiles];
   // Issues the loads of stage s (its tiles in T0..T); e4m3 pages land in stg.
-  auto issue = [&](int s, const int (&btv)[kStageTiles]) {
+  auto issue = [&](int s, const int4 (&btv)[kStageTiles]) {
 #pragma unroll
     for (int k = 0; k < kStageTiles; ++k) {
       const int t = s * kStageTiles + k;
@@ -460,16 +464,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   // Whether tile t needs a V zero fill: tile_partial of its pages, tested on
   // the entries directly (scalar compares: a tile is whole when it ends
   // inside the sequence and all four of its entries are in range).
-  auto tile_short = [&](int btv, int t) {
-    bool bad = (t + 1) * kTileKeys > n;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = __builtin_amdgcn_readlane(btv, j);
-      bad = bad || e < 0 || e >= a.num_pages;
-    }
-    return bad;
+  auto tile_short = [&](const int4& e, int t) {
+    const int np = a.num_pages;
+    return (t + 1) * kTileKeys > n || e.x < 0 || e.x >= np || e.y < 0 || e.y >= np || e.z < 0 || e.z >= np ||
+           e.w < 0 || e.w >= np;
   };
-  auto land = [&](int s, const int (&btv)[kStageTiles]) {
+  auto land = [&](int s, const int4 (&btv)[kStageTiles]) {
     if constexpr (FP8) {
 #pragma unroll
       for (int k = 0; k < kStageTiles; ++k)
@@ -487,9 +487,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
       if (partial) __syncthreads();
     }
   };
-  int btn[kStageTiles];
+  int4 btn[kStageTiles];
   {
-    int bt0[kStageTiles];
+    int4 bt0[kStageTiles];
 #pragma unroll
     for (int k = 0; k < kStageTiles; ++k) bt0[k] = bt_of(S0 * kStageTiles + k);
     issue(S0, bt0);
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 
   for (int s = S0; s <= S1; ++s) {
     const bool more = s < S1;
-    int bta[kStageTiles];
+    int4 bta[kStageTiles];
 #pragma unroll
     for (int k = 0; k < kStageTiles; ++k) bta[k] = bt_of((s + 2) * kStageTiles + k);
     if (more) issue(s + 1, btn);
