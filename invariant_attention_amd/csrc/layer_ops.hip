@@ -154,9 +154,9 @@ __device__ __forceinline__ void stage_barrier() {
 // base (the tile's first row at the K step) plus the lane's 32-bit offset, and
 // each fragment read is a per-lane LDS address of (slot, 16-k step) plus an
 // immediate for the 32-row block.  The loop itself then issues copies, LDS
-// reads and MFMAs with no vector address arithmetic: measured, that
-// arithmetic cost a quarter of the kernel's time, because a wave's VALU and
-// MFMA instructions here hardly overlap.
+// reads and MFMAs with no vector address arithmetic.  (A wave's VALU and MFMA
+// instructions in this loop hardly overlap, so every VALU instruction adds to
+// the step's time; forming the addresses in the loop measured ~5% slower.)
 template <class T>
 __global__ __launch_bounds__(64 * T::kWaves) void gemm_kernel(const __bf16* __restrict__ a,
                                                                const __bf16* __restrict__ wt,
