@@ -220,7 +220,7 @@ __device__ __forceinline__ const uint8_t* sgpr_base(const uint8_t* p) {
 // lane in lane order, each lane from an address of its own.  A page block's
 // K (D x 16 values) is contiguous in its page, so a tile's K is 4 blocks x
 // D/32 copies of 4 chunk rows (the lanes of an odd block fetch their row's
-// tokens in k_pos order); a V copy fills one operand run of the V region,
+// tokens in k_pos order); a V copy fills one 32-dim run of one page block,
 // each lane fetching the 16 bytes v_unit assigns it.
 template <int D>
 __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, const uint8_t* vc, const TilePages& tp,
@@ -232,8 +232,8 @@ __device__ __forceinline__ void direct_issue(uint8_t* slot, const uint8_t* kc, c
   auto head = [&](const uint8_t* pool, int pg) { return pool + ((size_t)pg * Hkv + kvh) * kHeadBytes; };
   // Each address is a wave-uniform base plus a 32-bit lane offset.  The lane
   // offset of a K copy: the lane's 16 bytes of the 1 KiB run, in k_pos order
-  // for an odd page block.  A V copy's lane takes its run from page block
-  // 2 ks2 + (lane / 32) at v_frag_off.
+  // for an odd page block.  A V copy's lane offset: the dim and token half
+  // its LDS unit holds (v_run_dim, v_run_half), the same in every run.
   __builtin_assume(w >= 0 && w < kPrefillWaves);  // so that the chunk -> page block map folds
   uint32_t k_even = (uint32_t)lane * 16;
   uint32_t k_odd = (uint32_t)((lane & ~15) | k_pos(1, lane & 15)) * 16;
