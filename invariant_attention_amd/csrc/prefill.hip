@@ -123,8 +123,8 @@ __device__ __forceinline__ int select4(int blk, const int (&x)[4]) {
   return (blk & 2) ? hi : lo;
 }
 
-// Issues the global loads of the tile at t0 for this thread's share.  btv
-// holds the tile's block-table entries in lanes 0..3.
+// Issues the global loads of the tile at t0 for this thread's share, given
+// the tile's 4 block-table entries e.
 template <int D, bool FP8>
 __device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const uint8_t* kc, const uint8_t* vc, const int4& e, int t0,
                                            int n, int num_pages, int kvh, int Hkv, int tid) {
@@ -277,9 +277,6 @@ __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp,
   }
 }
 
-__device__ __forceinline__ bool tile_partial(const TilePages& tp) {
-  return (tp.valid[0] & tp.valid[1] & tp.valid[2] & tp.valid[3]) != 16;
-}
 
 // Operand fragments of one tile from LDS: the K of k-step ks of score block
 // sb (the key of MFMA row r lies in page block k_block(sb, r)), and the V^T
@@ -461,9 +458,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   };
   // After the stage's loads have landed and a barrier: e4m3 tiles are stored
   // (FP8), bf16 tiles reaching past the sequence end are zero filled.
-  // Whether tile t needs a V zero fill: tile_partial of its pages, tested on
-  // the entries directly (scalar compares: a tile is whole when it ends
-  // inside the sequence and all four of its entries are in range).
+  // Whether tile t needs a V zero fill: some block of it holds fewer than 16
+  // keys, i.e. the tile reaches past the sequence end or one of its entries
+  // is out of range (such a block reads page 0 and holds no keys).  Scalar
+  // compares on the entries.
   auto tile_short = [&](const int4& e, int t) {
     const int np = a.num_pages;
     return (t + 1) * kTileKeys > n || e.x < 0 || e.x >= np || e.y < 0 || e.y >= np || e.z < 0 || e.z >= np ||
