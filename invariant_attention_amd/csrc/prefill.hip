@@ -277,7 +277,6 @@ __device__ __forceinline__ void direct_fixup(uint8_t* slot, const TilePages& tp,
   }
 }
 
-
 // Operand fragments of one tile from LDS: the K of k-step ks of score block
 // sb (the key of MFMA row r lies in page block k_block(sb, r)), and the V^T
 // run of k-step ks2 of dim block mb.
