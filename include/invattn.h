@@ -178,10 +178,18 @@ size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_s
 
 /* Device workspace for ia_paged_attn_prefill: 0 when max_seq_len <=
  * split_tokens (no row can see keys of two splits; NULL / 0 is then fine);
- * otherwise, for every (query row, query head), the fp32 merge of the splits
- * folded so far: total_q * Hq * d floats of U, then total_q * Hq * 2 floats of
- * (M, Z), each array rounded up to 256 bytes.  A row that sees one split only
- * never touches it. */
+ * otherwise the larger of two layouts, each array rounded up to 256 bytes:
+ *  - in-workgroup folds: for every (query row, query head) the fp32 merge of
+ *    the splits folded so far, total_q * Hq * d floats of U, then
+ *    total_q * Hq * 2 floats of (M, Z);
+ *  - split grid, offered while it takes at most 64 MiB: for every (query row,
+ *    query head, split) that split's fp32 state, total_q * Hq * ns * d floats,
+ *    then total_q * Hq * ns * 2 floats, ns = ceil(max_seq_len / split_tokens).
+ * A launch of fewer than 512 (sequence, row block, kv head) workgroups whose
+ * workspace holds the split-grid layout runs one workgroup per (row block,
+ * split) and then a merge of each row's splits in ascending order; otherwise
+ * each workgroup folds its rows' splits itself.  The two give the same bits.
+ * A row that sees one split only never touches the in-workgroup layout. */
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len);
 
 /*

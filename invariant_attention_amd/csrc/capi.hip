@@ -232,6 +232,13 @@ size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_s
 // Prefill workspace: for every query row and head, the fp32 merge (U, then
 // (M, Z)) of the splits folded so far.  Only a launch in which some row can
 // see keys of more than one split (max_seq_len > split_tokens) needs one.
+// Prefill workspace.  In-workgroup folds: the merge so far of every (row,
+// query head), when a row can see two splits.  Split grid: every (row, query
+// head, split)'s state, offered when that takes at most kSplitGridMaxBytes.
+constexpr size_t kSplitGridMaxBytes = (size_t)64 << 20;
+// Launches with fewer row-block workgroups than this take the split grid.
+constexpr int64_t kSplitGridMaxUnits = 512;
+
 static void prefill_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len, size_t* u, size_t* mz) {
   *u = *mz = 0;
   if (max_seq_len <= ctx->cfg.split_tokens) return;
@@ -240,11 +247,27 @@ static void prefill_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq
   *mz = align_up(rows * 2 * sizeof(float));
 }
 
+static int prefill_max_splits(const ia_ctx* ctx, int32_t max_seq_len) {
+  return (int)ceil_div(max_seq_len, ctx->cfg.split_tokens);
+}
+
+static void prefill_grid_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len, size_t* u, size_t* mz) {
+  *u = *mz = 0;
+  const int ns = prefill_max_splits(ctx, max_seq_len);
+  if (ns <= 1) return;
+  const size_t slots = (size_t)total_q * ctx->cfg.num_q_heads * ns;
+  const size_t bu = align_up(slots * ctx->cfg.head_dim * sizeof(float)), bmz = align_up(slots * 2 * sizeof(float));
+  if (bu + bmz > kSplitGridMaxBytes) return;
+  *u = bu;
+  *mz = bmz;
+}
+
 size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
   if (!ctx || total_q <= 0 || max_seq_len <= 0) return 0;
-  size_t u, mz;
+  size_t u, mz, gu, gmz;
   prefill_ws_parts(ctx, total_q, max_seq_len, &u, &mz);
-  return u + mz;
+  prefill_grid_ws_parts(ctx, total_q, max_seq_len, &gu, &gmz);
+  return u + mz > gu + gmz ? u + mz : gu + gmz;
 }
 
 ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -426,6 +449,22 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
   a.out = static_cast<__bf16*>(out);
   a.ws_u = u_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_mz = u_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes) : nullptr;
+  // A launch of few row-block workgroups (short chunks over long contexts)
+  // runs one workgroup per (row block, split) and a merge, when the workspace
+  // holds every split state: the same folds in the same order, so the same
+  // bits, with chains of one split instead of the whole context.
+  a.split_grid = 0;
+  a.max_splits = prefill_max_splits(ctx, max_seq_len);
+  size_t gu, gmz;
+  prefill_grid_ws_parts(ctx, total_q, max_seq_len, &gu, &gmz);
+  if (gu + gmz > 0 && workspace && ws_bytes >= gu + gmz &&
+      (int64_t)B * row_blocks * ctx->cfg.num_kv_heads < kSplitGridMaxUnits &&
+      (int64_t)B * row_blocks * ctx->cfg.num_kv_heads * a.max_splits < ((int64_t)1 << 31) &&
+      (int64_t)B * max_q_len * ctx->cfg.num_q_heads < ((int64_t)1 << 31)) {
+    a.split_grid = 1;
+    a.ws_u = static_cast<float*>(workspace);
+    a.ws_mz = reinterpret_cast<float*>(static_cast<char*>(workspace) + gu);
+  }
   a.c = ctx->c;
   a.B = B;
   a.Hq = ctx->cfg.num_q_heads;

@@ -56,8 +56,13 @@ struct PrefillArgs {
   const float* v_scale;
   const int32_t* block_table;
   __bf16* out;
-  float* ws_u;                // [total_q][Hq][D]: merge of a row's splits so far (rows that see > 1 split)
-  float* ws_mz;               // [total_q][Hq][2]: its (M, Z)
+  // In-workgroup folds: [total_q][Hq][D] merge of a row's splits so far and
+  // [total_q][Hq][2] its (M, Z).  Split grid: [total_q][Hq][max_splits][D]
+  // and [..][2], each row's state at the end of each split.
+  float* ws_u;
+  float* ws_mz;
+  int split_grid;             // 1: one workgroup per (row block, split), then prefill_merge_kernel
+  int max_splits;             // ceil(max_seq_len / split_tokens) (split grid)
   float c;
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;

@@ -84,7 +84,8 @@ def decode(ctx, pages: DevicePages, q: torch.Tensor, layout: wl.PageLayout, seq_
 
 
 def prefill(ctx, pages: DevicePages, q: torch.Tensor, cu: np.ndarray, layout: wl.PageLayout, seq_lens,
-            max_seq_len=None, max_q_len=None, stream=None):
+            max_seq_len=None, max_q_len=None, stream=None, workspace_bytes=None):
+    """workspace_bytes: the workspace passed (default: the size the library asks for)."""
     shape = pages.shape
     qd = q.to(DEV).contiguous()
     cu_d = torch.as_tensor(np.asarray(cu, dtype=np.int32), device=DEV)
@@ -94,7 +95,7 @@ def prefill(ctx, pages: DevicePages, q: torch.Tensor, cu: np.ndarray, layout: wl
     mql = int(q_lens.max(initial=0)) if max_q_len is None else int(max_q_len)
     msl = int(max(seq_lens)) if max_seq_len is None else int(max_seq_len)
     out = torch.empty((q.shape[0], shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
-    nws = ia.ia_prefill_workspace_bytes(ctx, int(q.shape[0]), msl)
+    nws = ia.ia_prefill_workspace_bytes(ctx, int(q.shape[0]), msl) if workspace_bytes is None else workspace_bytes
     ws = torch.empty(nws, dtype=torch.uint8, device=DEV) if nws else None
     ia.ia_paged_attn_prefill(ctx, qd, cu_d, sl, pages.k, pages.v, bt, mql, msl, out, pages.k_scale,
                              pages.v_scale, workspace=ws, stream=stream)

@@ -80,10 +80,13 @@ def test_workspace_size_formula():
                                                        + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 4 * 4))
     assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
                                                           + up(4 * 64 * 4))
-    # prefill: none while no row can see keys of two splits; else per (query row, head) the merge
-    # so far, d + 2 floats, in two arrays rounded up to 256 bytes
+    # prefill: none while no row can see keys of two splits; else the larger of per (query row, head)
+    # the merge so far and, while at most 64 MiB, per (query row, head, split) its state, d + 2
+    # floats each, in two arrays rounded up to 256 bytes
     assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2048) == 0
-    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2049) == up(1000 * 32 * 128 * 4) + up(1000 * 32 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2049) == up(1000 * 32 * 2 * 128 * 4) + up(1000 * 32 * 2 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 8192) == up(1000 * 32 * 4 * 128 * 4) + up(1000 * 32 * 4 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 8193) == up(1000 * 32 * 128 * 4) + up(1000 * 32 * 2 * 4)
     assert ia.ia_prefill_workspace_bytes(ctx, 0, 4096) == 0
 
 
@@ -136,7 +139,11 @@ def test_append_and_prefill_argument_errors():
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, None, 0,
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in ia.ia_last_error()
-    need = ia.ia_prefill_workspace_bytes(ctx, 10, 200)
+    # the size returned holds the split-grid layout (10 rows x 8 heads x 2 splits); the launch
+    # needs at least the in-workgroup layout (10 rows x 8 heads)
+    up = lambda x: (x + 255) // 256 * 256
+    assert ia.ia_prefill_workspace_bytes(ctx, 10, 200) == up(10 * 8 * 2 * 64 * 4) + up(10 * 8 * 2 * 2 * 4)
+    need = up(10 * 8 * 64 * 4) + up(10 * 8 * 2 * 4)
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, FAKE, need - 1,
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
 

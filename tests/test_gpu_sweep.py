@@ -5,7 +5,10 @@ Per case (head geometry, head dim, split length, sliding window, bf16 or e4m3 pa
 lengths drawn from a seeded generator, edge lengths mixed in):
 - decode with each kernel (AUTO, SPLIT, WIDE, SPREAD) and both cache hints matches the oracle
   within |err| <= 2e-3 + 1e-2 |ref|, and all of them give the same bits;
-- chunked prefill of the last q_len positions of each sequence matches the oracle;
+- chunked prefill of the last q_len positions of each sequence matches the oracle, and gives the
+  same bits with a workspace that holds only the in-workgroup fold layout (each workgroup folds
+  its rows' splits) as with the size the library asks for (a launch this small then runs one
+  workgroup per split and a separate merge);
 - the prefill row of each sequence's last position has exactly the decode output's bits (a
   decode row and the prefill row at the same position run the same operations in the same order:
   Vosti §5.3, the causal contract between prefill and decode)."""
@@ -103,5 +106,12 @@ def test_sweep_case(case):
     torch.cuda.synchronize()
     ok, err, ratio = gs.within_tolerance(pf, ref_pf)
     assert ok, f"{label} prefill: max err {err:.3e} ({ratio:.2f} of the bound)"
+    if max(lens) > shape.S:
+        up = lambda x: (x + 255) // 256 * 256
+        rows = int(q_pf.shape[0]) * shape.Hq
+        folds = gs.prefill(ctx0, pages, q_pf, cu_pf, layout, lens,
+                           workspace_bytes=up(rows * shape.d * 4) + up(rows * 2 * 4))
+        torch.cuda.synchronize()
+        assert np.array_equal(gs.bits(folds), gs.bits(pf)), f"{label}: split grid and in-workgroup folds differ"
     last_rows = gs.bits(pf)[np.asarray(cu_pf[1:]) - 1]
     assert np.array_equal(last_rows, outs[0]), f"{label}: prefill's last rows differ from decode in bits"
