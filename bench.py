@@ -729,9 +729,9 @@ def _prefill_world(shape, lens, layout_seed):
     return seqs, layout, ctx, k, v
 
 
-def prefill_workspace(ctx, total_q, max_seq_len):
+def prefill_workspace(ctx, B, total_q, max_q_len, max_seq_len):
     """The prefill workspace for a launch (None when its rows see one split only)."""
-    n = ia.ia_prefill_workspace_bytes(ctx, int(total_q), int(max_seq_len))
+    n = ia.ia_prefill_workspace_bytes(ctx, int(B), int(total_q), int(max_q_len), int(max_seq_len))
     return torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
 
 
@@ -744,7 +744,7 @@ def _prefill_rows(shape, seqs, layout, ctx, k, v, p0, p1):
     bt = torch.as_tensor(layout.block_table, device=DEV)
     out = torch.empty_like(q)
     ia.ia_paged_attn_prefill(ctx, q, cu, sl, k, v, bt, p1 - p0, p1, out,
-                             workspace=prefill_workspace(ctx, q.shape[0], p1))
+                             workspace=prefill_workspace(ctx, B, q.shape[0], p1 - p0, p1))
     return out.view(B, p1 - p0, shape.Hq, shape.d)
 
 
@@ -774,7 +774,7 @@ def invariance_variations(lens):
     sl = torch.as_tensor(np.array(lens8, np.int32), device=DEV)
     pre = torch.empty((8 * 16, shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
     ia.ia_paged_attn_prefill(w1.ctx, q16, cu, sl, w1.k, w1.v, w1.bt, 16, max(lens8), pre,
-                             workspace=prefill_workspace(w1.ctx, q16.shape[0], max(lens8)))
+                             workspace=prefill_workspace(w1.ctx, 8, q16.shape[0], 16, max(lens8)))
     pre = pre.view(8, 16, shape.Hq, shape.d)
     ws = torch.empty(ia.ia_decode_workspace_bytes(w1.ctx, 8, max(lens8)), dtype=torch.uint8, device=DEV)
     for j in range(16):
@@ -857,7 +857,7 @@ def prefill_tflops(steps: int, warmup: int):
     sl = torch.as_tensor(np.array(lens, np.int32), device=DEV)
     bt = torch.as_tensor(layout.block_table, device=DEV)
     out = torch.empty_like(q)
-    ws = prefill_workspace(ctx, q.shape[0], 4096)
+    ws = prefill_workspace(ctx, 8, q.shape[0], 4096, 4096)
     stream = torch.cuda.current_stream()
 
     def run():
@@ -1116,7 +1116,7 @@ def qwen235_points(steps, warmup):
     sl = torch.as_tensor(np.array([32768] * 16 + [nq] * 4, np.int32), device=DEV)
     btd = torch.as_tensor(bt, device=DEV)
     o = torch.empty_like(q)
-    ws = prefill_workspace(w.ctx, q.shape[0], 32768)
+    ws = prefill_workspace(w.ctx, 20, q.shape[0], nq, 32768)
     stream = torch.cuda.current_stream()
 
     def mixed():
@@ -1204,7 +1204,7 @@ def prefill_chunked(steps, warmup):
             cu = torch.as_tensor(np.arange(0, B * (p1 - p0) + 1, p1 - p0, dtype=np.int32), device=DEV)
             sl = torch.as_tensor(np.full(B, p1, np.int32), device=DEV)
             prepared.append((qc, cu, sl, torch.empty_like(qc), p1 - p0, p1,
-                             prefill_workspace(ctx, qc.shape[0], p1)))
+                             prefill_workspace(ctx, B, qc.shape[0], p1 - p0, p1)))
         return prepared
 
     def run(prepared):

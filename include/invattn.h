@@ -125,6 +125,29 @@ typedef enum { IA_DECODE_AUTO = 0, IA_DECODE_SPLIT = 1, IA_DECODE_WIDE = 2, IA_D
  *     set the caches can hold across calls. */
 typedef enum { IA_KV_HINT_AUTO = 0, IA_KV_HINT_STREAM = 1, IA_KV_HINT_CACHED = 2 } ia_kv_cache_hint;
 
+/* How a prefill launch whose rows can see two splits spreads its work.  Every
+ * choice folds a row's split states in ascending split order with the same
+ * operations, so all give the same bits.
+ *   IA_PREFILL_FOLD: one workgroup per (sequence, row block, kv head) walks
+ *     its rows' whole range of keys and folds each split into the rows'
+ *     merge at the split's end.
+ *   IA_PREFILL_AUTO: as FOLD, except that a sequence of at most 4 row blocks
+ *     whose keys reach a second split runs one workgroup per (row block, kv
+ *     head, split), each walking that split's keys and storing its rows'
+ *     split states, and a merge kernel then folds every row's states.  That
+ *     serves few rows over long keys (decode rows co-batched with prompts,
+ *     short chunks of long prompts), which FOLD leaves on a few workgroups.
+ *     A row block holds floor(16 / (Hq / Hkv)) x 8 positions for bf16
+ *     pages, half as many for e4m3 ones.
+ *   IA_PREFILL_SPLIT: as AUTO for sequences of any number of row blocks.
+ * AUTO and SPLIT apply to launches of fewer than 8192 (sequence, row block,
+ * kv head) workgroups whose workspace holds the split states (within 128 MiB;
+ * the bound halves the row blocks split per sequence until they fit); other
+ * launches run FOLD, and so do launches whose total_q leaves no room for a
+ * sequence short enough to split (total_q > (B - 1) * max_q_len + the
+ * positions of the row blocks split). */
+typedef enum { IA_PREFILL_AUTO = 0, IA_PREFILL_FOLD = 1, IA_PREFILL_SPLIT = 2 } ia_prefill_grid;
+
 typedef struct {
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads, Hq / Hkv <= 16 */
   int32_t num_kv_heads;  /* Hkv */
@@ -145,6 +168,7 @@ typedef struct {
   int32_t decode_kernel;  /* ia_decode_kernel (0 = AUTO) */
   int32_t kv_cache_hint;  /* ia_kv_cache_hint (0 = AUTO): how the decode split
                              kernel's page loads use the caches; never a value */
+  int32_t prefill_grid;   /* ia_prefill_grid (0 = AUTO); never a value */
 } ia_config;
 
 typedef struct ia_ctx ia_ctx;
@@ -177,20 +201,19 @@ const char* ia_version(void);
 size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_seq_len);
 
 /* Device workspace for ia_paged_attn_prefill: 0 when max_seq_len <=
- * split_tokens (no row can see keys of two splits; NULL / 0 is then fine);
- * otherwise the larger of two layouts, each array rounded up to 256 bytes:
- *  - in-workgroup folds: for every (query row, query head) the fp32 merge of
- *    the splits folded so far, total_q * Hq * d floats of U, then
- *    total_q * Hq * 2 floats of (M, Z);
- *  - split grid, offered while it takes at most 64 MiB: for every (query row,
- *    query head, split) that split's fp32 state, total_q * Hq * ns * d floats,
- *    then total_q * Hq * ns * 2 floats, ns = ceil(max_seq_len / split_tokens).
- * A launch of fewer than 512 (sequence, row block, kv head) workgroups whose
- * workspace holds the split-grid layout runs one workgroup per (row block,
- * split) and then a merge of each row's splits in ascending order; otherwise
- * each workgroup folds its rows' splits itself.  The two give the same bits.
- * A row that sees one split only never touches the in-workgroup layout. */
-size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len);
+ * split_tokens (no row can see keys of two splits; NULL / 0 is then fine).
+ * Otherwise one fp32 row state of d + 2 floats per (query row, query head):
+ * total_q * Hq * d floats of U, then total_q * Hq * 2 floats of (M, Z), each
+ * array rounded up to 256 bytes (the merge of the row's splits so far, or
+ * its split-0 state under the split grid); the launch refuses less.  When
+ * the launch can run the split grid (ia_prefill_grid) the size also holds,
+ * in two more arrays laid out the same way, B * r * (positions per row block)
+ * * (ceil(max_seq_len / split_tokens) - 1) * Hq states for the splits past
+ * the first, r = the row blocks it splits per sequence; a workspace without
+ * them runs in-workgroup folds (the same bits).  A workspace serves one call
+ * at a time. */
+size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t B, int32_t total_q, int32_t max_q_len,
+                                  int32_t max_seq_len);
 
 /*
  * kv_append: writes T new K/V rows into their page slots.  Enqueue it on the
@@ -287,9 +310,11 @@ size_t ia_decode_noalloc_scratch_bytes(void);
  *   max_q_len    host upper bound of q lengths (grid only)
  *   max_seq_len  host upper bound of seq_lens (grid only)
  *   out          dev [total_q][Hq][d] bf16
- *   workspace    dev, >= ia_prefill_workspace_bytes(ctx, total_q, max_seq_len)
- *                bytes, 16-byte aligned (NULL when that is 0); a smaller one
- *                is refused with IA_ERR_WORKSPACE_TOO_SMALL
+ *   workspace    dev, ia_prefill_workspace_bytes(ctx, B, total_q, max_q_len,
+ *                max_seq_len) bytes, 16-byte aligned (NULL when that is 0);
+ *                one without the split states runs in-workgroup folds, one
+ *                smaller than the row states is refused with
+ *                IA_ERR_WORKSPACE_TOO_SMALL
  */
 ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t* cu_q_lens,
                                 const int32_t* seq_lens, const void* k_cache, const void* v_cache,

@@ -33,6 +33,9 @@ IA_DECODE_SPREAD = 3
 IA_KV_HINT_AUTO = 0
 IA_KV_HINT_STREAM = 1
 IA_KV_HINT_CACHED = 2
+IA_PREFILL_AUTO = 0
+IA_PREFILL_FOLD = 1
+IA_PREFILL_SPLIT = 2
 IA_POOL_CONSTANT_HASH = 1
 
 EXPORTS = [
@@ -57,7 +60,7 @@ class ia_config(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("split_policy", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
-        ("decode_kernel", ctypes.c_int32), ("kv_cache_hint", ctypes.c_int32),
+        ("decode_kernel", ctypes.c_int32), ("kv_cache_hint", ctypes.c_int32), ("prefill_grid", ctypes.c_int32),
     ]
 
 
@@ -79,7 +82,7 @@ def load() -> ctypes.CDLL:
         "ia_last_error": ([], ctypes.c_char_p),
         "ia_version": ([], ctypes.c_char_p),
         "ia_decode_workspace_bytes": ([vp, i32, i32], sz),
-        "ia_prefill_workspace_bytes": ([vp, i32, i32], sz),
+        "ia_prefill_workspace_bytes": ([vp, i32, i32, i32, i32], sz),
         "ia_kv_append": ([vp, vp, vp, i64p, i32, vp, vp, i32, vp, vp, vp], ctypes.c_int),
         "ia_paged_attn_decode": ([vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "ia_paged_attn_prefill": ([vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp],
@@ -161,10 +164,10 @@ def ia_create(cfg: ia_config) -> ctypes.c_void_p:
 def make_config(Hq: int, Hkv: int, d: int, *, page_size: int = 16, split_tokens: int = 2048,
                 kv_dtype: int = IA_KV_BF16, split_policy: int = IA_SPLIT_FIXED, sm_scale: float | None = None,
                 sliding_window: int = 0, decode_kernel: int = IA_DECODE_AUTO,
-                kv_cache_hint: int = IA_KV_HINT_AUTO) -> ia_config:
+                kv_cache_hint: int = IA_KV_HINT_AUTO, prefill_grid: int = IA_PREFILL_AUTO) -> ia_config:
     scale = float(1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
     return ia_config(Hq, Hkv, d, page_size, split_tokens, kv_dtype, split_policy, scale, sliding_window,
-                     decode_kernel, kv_cache_hint)
+                     decode_kernel, kv_cache_hint, prefill_grid)
 
 
 def ia_last_error() -> str:
@@ -179,8 +182,8 @@ def ia_decode_workspace_bytes(ctx: Context, batch: int, max_seq_len: int) -> int
     return int(load().ia_decode_workspace_bytes(ctx.handle, batch, max_seq_len))
 
 
-def ia_prefill_workspace_bytes(ctx: Context, total_q: int, max_seq_len: int) -> int:
-    return int(load().ia_prefill_workspace_bytes(ctx.handle, total_q, max_seq_len))
+def ia_prefill_workspace_bytes(ctx: Context, B: int, total_q: int, max_q_len: int, max_seq_len: int) -> int:
+    return int(load().ia_prefill_workspace_bytes(ctx.handle, B, total_q, max_q_len, max_seq_len))
 
 
 def ia_kv_append(ctx: Context, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,

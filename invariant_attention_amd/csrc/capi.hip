@@ -211,6 +211,8 @@ ia_status ia_create(const ia_config* cfg, ia_ctx** out) {
   if (c.kv_cache_hint != IA_KV_HINT_AUTO && c.kv_cache_hint != IA_KV_HINT_STREAM &&
       c.kv_cache_hint != IA_KV_HINT_CACHED)
     return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown kv_cache_hint %d", c.kv_cache_hint);
+  if (c.prefill_grid != IA_PREFILL_AUTO && c.prefill_grid != IA_PREFILL_FOLD && c.prefill_grid != IA_PREFILL_SPLIT)
+    return fail(IA_ERR_UNSUPPORTED_CONFIG, "unknown prefill_grid %d", c.prefill_grid);
   ia_ctx* ctx = new (std::nothrow) ia_ctx;
   if (!ctx) return fail(IA_ERR_INTERNAL, "out of host memory");
   ctx->cfg = c;
@@ -229,45 +231,61 @@ size_t ia_decode_workspace_bytes(const ia_ctx* ctx, int32_t batch, int32_t max_s
   return u + ml + ord + x + mx;
 }
 
-// Prefill workspace: for every query row and head, the fp32 merge (U, then
-// (M, Z)) of the splits folded so far.  Only a launch in which some row can
-// see keys of more than one split (max_seq_len > split_tokens) needs one.
-// Prefill workspace.  In-workgroup folds: the merge so far of every (row,
-// query head), when a row can see two splits.  Split grid: every (row, query
-// head, split)'s state, offered when that takes at most kSplitGridMaxBytes.
-constexpr size_t kSplitGridMaxBytes = (size_t)64 << 20;
-// Launches with fewer row-block workgroups than this take the split grid.
-constexpr int64_t kSplitGridMaxUnits = 512;
+// Prefill workspace, when some row can see keys of two splits (max_seq_len >
+// split_tokens).  First one fp32 row state of d + 2 floats per (query row,
+// query head): U of every entry, then (M, Z) of every entry -- the merge of
+// the row's splits so far under in-workgroup folds, the state of split 0
+// under the split grid.  Then, for the split grid, the states of splits 1 ..
+// of the first split_rbs row blocks of every sequence.  The split grid is
+// offered to launches of fewer than kSplitMaxUnits row-block workgroups, for
+// sequences of at most kSplitMaxRowBlocks row blocks (few rows over long
+// keys: decode rows co-batched with prompts, short chunks of long prompts),
+// with its states in at most kSplitMaxBytes.
+constexpr size_t kSplitMaxBytes = (size_t)128 << 20;
+constexpr int64_t kSplitMaxUnits = 8192;
+constexpr int kSplitMaxRowBlocks = 4;
 
-static void prefill_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len, size_t* u, size_t* mz) {
-  *u = *mz = 0;
-  if (max_seq_len <= ctx->cfg.split_tokens) return;
-  const size_t rows = (size_t)total_q * ctx->cfg.num_q_heads;
-  *u = align_up(rows * ctx->cfg.head_dim * sizeof(float));
-  *mz = align_up(rows * 2 * sizeof(float));
+static size_t prefill_state_bytes(const ia_ctx* ctx, int64_t entries) {
+  return align_up((size_t)entries * ctx->cfg.head_dim * sizeof(float)) + align_up((size_t)entries * 2 * sizeof(float));
 }
 
 static int prefill_max_splits(const ia_ctx* ctx, int32_t max_seq_len) {
   return (int)ceil_div(max_seq_len, ctx->cfg.split_tokens);
 }
 
-static void prefill_grid_ws_parts(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len, size_t* u, size_t* mz) {
-  *u = *mz = 0;
-  const int ns = prefill_max_splits(ctx, max_seq_len);
-  if (ns <= 1) return;
-  const size_t slots = (size_t)total_q * ctx->cfg.num_q_heads * ns;
-  const size_t bu = align_up(slots * ctx->cfg.head_dim * sizeof(float)), bmz = align_up(slots * 2 * sizeof(float));
-  if (bu + bmz > kSplitGridMaxBytes) return;
-  *u = bu;
-  *mz = bmz;
+static int64_t prefill_row_blocks(const ia_ctx* ctx, int32_t max_q_len) {
+  return ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3));
 }
 
-size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t total_q, int32_t max_seq_len) {
-  if (!ctx || total_q <= 0 || max_seq_len <= 0) return 0;
-  size_t u, mz, gu, gmz;
-  prefill_ws_parts(ctx, total_q, max_seq_len, &u, &mz);
-  prefill_grid_ws_parts(ctx, total_q, max_seq_len, &gu, &gmz);
-  return u + mz > gu + gmz ? u + mz : gu + gmz;
+// Entries of the split states of splits 1 .. for split_rbs row blocks.
+static int64_t prefill_split_entries(const ia_ctx* ctx, int32_t B, int32_t max_seq_len, int rbs) {
+  const int ppg = ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3);
+  return (int64_t)B * rbs * ppg * (prefill_max_splits(ctx, max_seq_len) - 1) * ctx->cfg.num_q_heads;
+}
+
+// Row blocks per sequence that a launch splits (0: none), before the
+// workspace is checked.  When max_q_len exceeds them, a sequence that fits
+// leaves rows of the bound unused: total_q rows with none unused mean no
+// sequence fits, and nothing is split.
+static int prefill_split_rbs(const ia_ctx* ctx, int32_t B, int32_t total_q, int32_t max_q_len, int32_t max_seq_len) {
+  if (ctx->cfg.prefill_grid == IA_PREFILL_FOLD || max_seq_len <= ctx->cfg.split_tokens || B <= 0 || max_q_len <= 0)
+    return 0;
+  const int64_t rb = prefill_row_blocks(ctx, max_q_len);
+  if ((int64_t)B * rb * ctx->cfg.num_kv_heads >= kSplitMaxUnits) return 0;
+  int64_t rbs = ctx->cfg.prefill_grid == IA_PREFILL_SPLIT ? rb : (rb < kSplitMaxRowBlocks ? rb : kSplitMaxRowBlocks);
+  const int64_t ppg = ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3);
+  if (rbs < rb && (int64_t)total_q > (int64_t)(B - 1) * max_q_len + rbs * ppg) return 0;
+  while (rbs > 0 && prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_seq_len, (int)rbs)) > kSplitMaxBytes)
+    rbs /= 2;
+  return (int)rbs;
+}
+
+size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t B, int32_t total_q, int32_t max_q_len,
+                                  int32_t max_seq_len) {
+  if (!ctx || B <= 0 || total_q <= 0 || max_q_len <= 0 || max_seq_len <= ctx->cfg.split_tokens) return 0;
+  const int rbs = prefill_split_rbs(ctx, B, total_q, max_q_len, max_seq_len);
+  return prefill_state_bytes(ctx, (int64_t)total_q * ctx->cfg.num_q_heads) +
+         (rbs ? prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_seq_len, rbs)) : 0);
 }
 
 ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -426,15 +444,16 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
     return fail(IA_ERR_INVALID_ARG, "max_q_len and max_seq_len must be positive when total_q > 0");
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  const int64_t row_blocks = ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3));
+  const int64_t row_blocks = prefill_row_blocks(ctx, max_q_len);
   if ((int64_t)B * row_blocks * ctx->cfg.num_kv_heads >= ((int64_t)1 << 31))
     return fail(IA_ERR_INVALID_ARG, "grid too large");
-  size_t u_bytes, mz_bytes;
-  prefill_ws_parts(ctx, total_q, max_seq_len, &u_bytes, &mz_bytes);
-  if (u_bytes + mz_bytes > 0) {
-    if (!workspace || ws_bytes < u_bytes + mz_bytes)
-      return fail(IA_ERR_WORKSPACE_TOO_SMALL, "prefill workspace needs %zu bytes (got %zu)", u_bytes + mz_bytes,
-                  ws_bytes);
+  if ((int64_t)total_q * ctx->cfg.num_q_heads >= ((int64_t)1 << 31))
+    return fail(IA_ERR_INVALID_ARG, "total_q x num_q_heads must be below 2^31");
+  const bool multi_split = max_seq_len > ctx->cfg.split_tokens;
+  const size_t fold_bytes = multi_split ? prefill_state_bytes(ctx, (int64_t)total_q * ctx->cfg.num_q_heads) : 0;
+  if (multi_split) {
+    if (!workspace || ws_bytes < fold_bytes)
+      return fail(IA_ERR_WORKSPACE_TOO_SMALL, "prefill workspace needs %zu bytes (got %zu)", fold_bytes, ws_bytes);
     if (!aligned(workspace, 16)) return fail(IA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
   ia::PrefillArgs a;
@@ -447,23 +466,26 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
   a.v_scale = v_scale;
   a.block_table = block_table;
   a.out = static_cast<__bf16*>(out);
-  a.ws_u = u_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.ws_mz = u_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + u_bytes) : nullptr;
-  // A launch of few row-block workgroups (short chunks over long contexts)
-  // runs one workgroup per (row block, split) and a merge, when the workspace
-  // holds every split state: the same folds in the same order, so the same
-  // bits, with chains of one split instead of the whole context.
-  a.split_grid = 0;
   a.max_splits = prefill_max_splits(ctx, max_seq_len);
-  size_t gu, gmz;
-  prefill_grid_ws_parts(ctx, total_q, max_seq_len, &gu, &gmz);
-  if (gu + gmz > 0 && workspace && ws_bytes >= gu + gmz &&
-      (int64_t)B * row_blocks * ctx->cfg.num_kv_heads < kSplitGridMaxUnits &&
-      (int64_t)B * row_blocks * ctx->cfg.num_kv_heads * a.max_splits < ((int64_t)1 << 31) &&
-      (int64_t)B * max_q_len * ctx->cfg.num_q_heads < ((int64_t)1 << 31)) {
-    a.split_grid = 1;
-    a.ws_u = static_cast<float*>(workspace);
-    a.ws_mz = reinterpret_cast<float*>(static_cast<char*>(workspace) + gu);
+  a.ws_u = a.ws_mz = a.sg_u = a.sg_mz = nullptr;
+  a.split_rbs = 0;
+  if (multi_split) {
+    const size_t rows = (size_t)total_q * ctx->cfg.num_q_heads;
+    char* base = static_cast<char*>(workspace);
+    a.ws_u = reinterpret_cast<float*>(base);
+    a.ws_mz = reinterpret_cast<float*>(base + align_up(rows * ctx->cfg.head_dim * sizeof(float)));
+    // The split grid, when the workspace also holds its states (a workspace
+    // of the size ia_prefill_workspace_bytes reports does).
+    const int rbs = prefill_split_rbs(ctx, B, total_q, max_q_len, max_seq_len);
+    if (rbs > 0) {
+      const int64_t entries = prefill_split_entries(ctx, B, max_seq_len, rbs);
+      const int64_t grid = (int64_t)B * ctx->cfg.num_kv_heads * (row_blocks + (int64_t)rbs * (a.max_splits - 1));
+      if (ws_bytes >= fold_bytes + prefill_state_bytes(ctx, entries) && grid < ((int64_t)1 << 31)) {
+        a.split_rbs = rbs;
+        a.sg_u = reinterpret_cast<float*>(base + fold_bytes);
+        a.sg_mz = reinterpret_cast<float*>(base + fold_bytes + align_up((size_t)entries * ctx->cfg.head_dim * sizeof(float)));
+      }
+    }
   }
   a.c = ctx->c;
   a.B = B;

@@ -56,13 +56,19 @@ struct PrefillArgs {
   const float* v_scale;
   const int32_t* block_table;
   __bf16* out;
-  // In-workgroup folds: [total_q][Hq][D] merge of a row's splits so far and
-  // [total_q][Hq][2] its (M, Z).  Split grid: [total_q][Hq][max_splits][D]
-  // and [..][2], each row's state at the end of each split.
+  // Row states, entry (row, query head) of [total_q][Hq]: D fp32 of U (ws_u)
+  // and (M, Z) (ws_mz).  In-workgroup folds: the merge of the row's splits so
+  // far.  Split grid: the row's state at the end of split 0.
   float* ws_u;
   float* ws_mz;
-  int split_grid;             // 1: one workgroup per (row block, split), then prefill_merge_kernel
-  int max_splits;             // ceil(max_seq_len / split_tokens) (split grid)
+  // Split grid: the states of splits 1 .. max_splits - 1 of the rows of split
+  // sequences, entry ((b * split_rows + i) * (max_splits - 1) + s - 1) * Hq +
+  // head, split_rows = split_rbs x positions per row block.
+  float* sg_u;
+  float* sg_mz;
+  int split_rbs;              // sequences of at most this many row blocks whose keys reach a
+                              // second split run one workgroup per split (0: none)
+  int max_splits;             // ceil(max_seq_len / split_tokens)
   float c;
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;

@@ -343,56 +343,83 @@ __device__ __forceinline__ void fold_split(const PrefillArgs& a, RowState<D>& st
   if (!last && g == 0) *reinterpret_cast<f32x2*>(a.ws_mz + 2 * ridx) = f32x2{M, Z};
 }
 
-// Split grid: the state of one split for the lane's row, to slot
-// (row, split) of the workspace (the layout fold_split uses for a row).
+// Split grid: the state of one split for the lane's row, to entry `e` of
+// the state arrays (u, mz): the layout fold_split uses for a row's merge.
 template <int D>
-__device__ __forceinline__ void store_split(const PrefillArgs& a, const RowState<D>& st, size_t slot, int g) {
-  asm volatile("" : "+v"(slot));  // (as in fold_split: keep the address out of the tile loop)
-  float* wu = a.ws_u + slot * D + 4 * g;
+__device__ __forceinline__ void store_split(float* u, float* mz, const RowState<D>& st, size_t e, int g) {
+  asm volatile("" : "+v"(e));  // (as in fold_split: keep the address out of the tile loop)
+  float* wu = u + e * D + 4 * g;
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) *reinterpret_cast<f32x4*>(wu + 16 * mb) = st.u[mb];
-  if (g == 0) *reinterpret_cast<f32x2*>(a.ws_mz + 2 * slot) = f32x2{st.m, st.z};
+  if (g == 0) *reinterpret_cast<f32x2*>(mz + 2 * e) = f32x2{st.m, st.z};
 }
 
-// Split grid: one wave per (sequence, row, query head) folds the row's split
-// states in ascending split order -- the first seeds the merge, each later
-// one is merged into it (merge_scalars / merge_value), as fold_split does
-// inside a workgroup -- and writes the finalised bf16 row.
+// Positions one prefill workgroup covers.
+template <bool FP8>
+__device__ __forceinline__ int positions_per_workgroup(int group) {
+  return (kRows / group) * row_blocks_per_wave<FP8>() * kPrefillWaves;
+}
+
+// Whether a sequence runs split grid: the launch splits sequences of at most
+// split_rbs row blocks, and its keys reach a second split.
+__device__ __forceinline__ bool split_sequence(const PrefillArgs& a, int n, int ql, int ppg) {
+  return a.split_rbs > 0 && n > a.split_tokens && ql <= a.split_rbs * ppg;
+}
+
+// Entry of split s >= 1 of row i of sequence b (split grid).
+__device__ __forceinline__ size_t split_entry(const PrefillArgs& a, int b, int i, int s, int hq, int ppg) {
+  return (((size_t)b * (a.split_rbs * ppg) + i) * (a.max_splits - 1) + (s - 1)) * a.Hq + hq;
+}
+
+// Split grid: one wave per (sequence, row, query head) of the split
+// sequences folds the row's split states in ascending split order -- the
+// first seeds the merge, each later one is merged into it (merge_scalars /
+// merge_value), as fold_split does inside a workgroup -- and writes the
+// finalised bf16 row.  Waves of other sequences and rows return at once.
+constexpr int kMergeWaves = 4;
+
 template <int D, bool FP8>
-__global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kMergeWaves) void prefill_merge_kernel(PrefillArgs a) {
   constexpr int kPer = D / 64;
-  const int lane = threadIdx.x;
-  const int hq = blockIdx.x % a.Hq;
-  const int i = (blockIdx.x / a.Hq) % a.max_q_len;
-  const int b = blockIdx.x / a.Hq / a.max_q_len;
+  const int lane = threadIdx.x & 63;
+  const int ppg = positions_per_workgroup<FP8>(a.group);
+  const int rows = a.split_rbs * ppg;
+  const int64_t item = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  const int hq = (int)(item % a.Hq);
+  const int i = (int)((item / a.Hq) % rows);
+  const int b = (int)(item / a.Hq / rows);
+  if (b >= a.B) return;
   const int q0 = a.cu_q_lens[b];
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   int ql = a.cu_q_lens[b + 1] - q0;
   ql = ql < 0 ? 0 : (ql > a.max_q_len ? a.max_q_len : ql);
-  if (q0 < 0 || q0 > a.total_q - ql || i >= ql) return;
+  if (q0 < 0 || q0 > a.total_q - ql || i >= ql || !split_sequence(a, n, ql, ppg)) return;
   // Rows of a row-block workgroup whose first position is negative
   // (inconsistent lengths) are not computed, as in prefill_kernel.
-  const int ppg = (kRows / a.group) * row_blocks_per_wave<FP8>() * kPrefillWaves;
   if (n - ql + (i - i % ppg) < 0) return;
   const int p = n - ql + i;
   const int S = a.split_tokens;
   const int s0 = first_key(p, a.window) / S, s1 = p / S;
-  const size_t slot0 = ((size_t)(q0 + i) * a.Hq + hq) * a.max_splits;
-  const f32x2 mz0 = *reinterpret_cast<const f32x2*>(a.ws_mz + 2 * (slot0 + s0));
+  const size_t e0 = (size_t)(q0 + i) * a.Hq + hq;
+  auto u_of = [&](int s) { return s == 0 ? a.ws_u + e0 * D : a.sg_u + split_entry(a, b, i, s, hq, ppg) * D; };
+  auto mz_of = [&](int s) { return s == 0 ? a.ws_mz + 2 * e0 : a.sg_mz + 2 * split_entry(a, b, i, s, hq, ppg); };
+  const f32x2 mz0 = *reinterpret_cast<const f32x2*>(mz_of(s0));
   float M = mz0[0], Z = mz0[1];
   float U[kPer];
+  const float* u0 = u_of(s0);
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) U[k] = a.ws_u[(slot0 + s0) * D + kPer * lane + k];
+  for (int k = 0; k < kPer; ++k) U[k] = u0[kPer * lane + k];
   for (int s = s0 + 1; s <= s1; ++s) {
-    const f32x2 mz = *reinterpret_cast<const f32x2*>(a.ws_mz + 2 * (slot0 + s));
+    const f32x2 mz = *reinterpret_cast<const f32x2*>(mz_of(s));
+    const float* us = u_of(s);
     float wa, wb;
     merge_scalars(M, Z, mz[0], mz[1], wa, wb);
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) U[k] = merge_value(U[k], a.ws_u[(slot0 + s) * D + kPer * lane + k], wa, wb);
+    for (int k = 0; k < kPer; ++k) U[k] = merge_value(U[k], us[kPer * lane + k], wa, wb);
   }
   const float rz = final_rz(Z);
   const float vs = FP8 ? a.v_scale[hq / a.group] : 1.0f;
-  __bf16* out = a.out + ((size_t)(q0 + i) * a.Hq + hq) * D + kPer * lane;
+  __bf16* out = a.out + e0 * D + kPer * lane;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) out[k] = finalize(U[k], vs, rz);
 }
@@ -414,27 +441,34 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   // and walk the same K/V tiles, which its L2 then serves.  When the pair
   // count is not a multiple of 8 the order is simply row block (from the
   // end), b, kvh.
-  // Split grid: the grid repeats the row-block grid once per split, and the
-  // workgroup walks only the tiles of its split.
+  // Split grid: past the row-block grid come the workgroups of splits 1,
+  // 2, ... of the first split_rbs row blocks of every (sequence, kv head);
+  // those of sequences that are not split return at once.  In a split
+  // sequence each workgroup walks only the tiles of its split (split 0: the
+  // row-block grid's workgroup).
   const int pairs = a.B * a.Hkv;
   const int units = pairs * a.max_row_blocks;
-  int bid = blockIdx.x, sp_grid = 0;
-  if (a.split_grid) {
-    sp_grid = bid / units;
-    bid -= sp_grid * units;
-  }
-  int pair, rbi;
-  if (pairs % kXcds == 0) {
-    const int xcd = bid % kXcds, k = bid / kXcds;
-    pair = xcd + kXcds * (k / a.max_row_blocks);
-    rbi = k % a.max_row_blocks;
+  int pair, wrb, sp_grid = 0;
+  if ((int)blockIdx.x < units) {
+    const int bid = blockIdx.x;
+    int rbi;
+    if (pairs % kXcds == 0) {
+      const int xcd = bid % kXcds, k = bid / kXcds;
+      pair = xcd + kXcds * (k / a.max_row_blocks);
+      rbi = k % a.max_row_blocks;
+    } else {
+      pair = bid % pairs;
+      rbi = bid / pairs;
+    }
+    wrb = a.max_row_blocks - 1 - rbi;
   } else {
-    pair = bid % pairs;
-    rbi = bid / pairs;
+    const int e = blockIdx.x - units, per = pairs * a.split_rbs;
+    sp_grid = 1 + e / per;
+    pair = (e % per) % pairs;
+    wrb = (e % per) / pairs;
   }
   const int kvh = pair % a.Hkv;
   const int b = pair / a.Hkv;
-  const int wrb = a.max_row_blocks - 1 - rbi;
   const int q0 = a.cu_q_lens[b];
   const int n = clamp_len(a.seq_lens[b], a.max_seq_len);
   int ql = a.cu_q_lens[b + 1] - q0;
@@ -473,12 +507,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   float c = a.c;
   if constexpr (FP8) c = c * a.k_scale[kvh];
   const int S = a.split_tokens;
+  const bool split_grid = split_sequence(a, n, ql, ppg);
+  if (sp_grid > 0 && !split_grid) return;  // uniform over the workgroup
 
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
   const int nblk = (n + 15) >> 4;
   int T = pmax_wg / kTileKeys;                            // last tile
   int T0 = first_key(n - ql + i0, a.window) / kTileKeys;  // first tile
-  if (a.split_grid) {
+  if (split_grid) {
     T0 = max(T0, sp_grid * (S / kTileKeys));
     T = min(T, (sp_grid + 1) * (S / kTileKeys) - 1);
     if (T0 > T) return;  // uniform over the workgroup
@@ -650,8 +686,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
         for (int k = 0; k < kRB; ++k) {
           if (limit[k] >= sp * S && lo[k] < sp * S + S) {
             const size_t ridx = (size_t)(q0 + ii[k]) * a.Hq + hq;
-            if (a.split_grid)
-              store_split<D>(a, st[k], ridx * a.max_splits + sp, g);
+            if (split_grid && sp == 0)
+              store_split<D>(a.ws_u, a.ws_mz, st[k], ridx, g);
+            else if (split_grid)
+              store_split<D>(a.sg_u, a.sg_mz, st[k], split_entry(a, b, ii[k], sp, hq, ppg), g);
             else
               fold_split<D>(a, st[k], ridx, sp == lo[k] / S, sp == limit[k] / S, vs, g);
           }
@@ -672,17 +710,19 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
 template <int D, bool FP8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (a.B == 0 || a.max_q_len == 0) return hipSuccess;
-  const int64_t units = (int64_t)a.B * a.max_row_blocks * a.Hkv * (a.split_grid ? a.max_splits : 1);
+  const int64_t pairs = (int64_t)a.B * a.Hkv;
+  const int64_t units = pairs * a.max_row_blocks + (a.split_rbs ? pairs * a.split_rbs * (a.max_splits - 1) : 0);
   const int lds = 2 * kStageTiles * tile_lds_bytes<D>();  // two slots of a stage (64 KiB at head_dim 128)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3((unsigned)units), dim3(kPrefillThreads), lds, st, a);
-  if (!a.split_grid) return hipGetLastError();
+  if (!a.split_rbs) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_merge_kernel<D, FP8>), dim3((unsigned)((int64_t)a.B * a.max_q_len * a.Hq)), dim3(64), 0,
-                     st, a);
+  const int64_t items = (int64_t)a.B * a.split_rbs * prefill_positions_per_block(a.group, FP8) * a.Hq;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, FP8>), dim3((unsigned)((items + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(64 * kMergeWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -21,13 +21,13 @@ def within_tolerance(gpu: torch.Tensor, ref: np.ndarray):
 
 
 def make_ctx(shape: wl.AttnShape, fp8=False, by_count=False, split_tokens=None, window=0,
-             decode_kernel=ia.IA_DECODE_AUTO, kv_cache_hint=ia.IA_KV_HINT_AUTO):
+             decode_kernel=ia.IA_DECODE_AUTO, kv_cache_hint=ia.IA_KV_HINT_AUTO, prefill_grid=ia.IA_PREFILL_AUTO):
     cfg = ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P,
                          split_tokens=shape.S if split_tokens is None else split_tokens,
                          kv_dtype=ia.IA_KV_FP8_E4M3 if fp8 else ia.IA_KV_BF16,
                          split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
                          sm_scale=shape.scale, sliding_window=window, decode_kernel=decode_kernel,
-                         kv_cache_hint=kv_cache_hint)
+                         kv_cache_hint=kv_cache_hint, prefill_grid=prefill_grid)
     return ia.Context(cfg)
 
 
@@ -95,7 +95,8 @@ def prefill(ctx, pages: DevicePages, q: torch.Tensor, cu: np.ndarray, layout: wl
     mql = int(q_lens.max(initial=0)) if max_q_len is None else int(max_q_len)
     msl = int(max(seq_lens)) if max_seq_len is None else int(max_seq_len)
     out = torch.empty((q.shape[0], shape.Hq, shape.d), dtype=torch.bfloat16, device=DEV)
-    nws = ia.ia_prefill_workspace_bytes(ctx, int(q.shape[0]), msl) if workspace_bytes is None else workspace_bytes
+    nws = (ia.ia_prefill_workspace_bytes(ctx, len(q_lens), int(q.shape[0]), mql, msl) if workspace_bytes is None
+           else workspace_bytes)
     ws = torch.empty(nws, dtype=torch.uint8, device=DEV) if nws else None
     ia.ia_paged_attn_prefill(ctx, qd, cu_d, sl, pages.k, pages.v, bt, mql, msl, out, pages.k_scale,
                              pages.v_scale, workspace=ws, stream=stream)

@@ -49,6 +49,7 @@ def test_version_and_clean_error_state():
     (dict(Hq=32, Hkv=8, d=128, sliding_window=-1), "sliding_window"),
     (dict(Hq=32, Hkv=8, d=128, decode_kernel=4), "decode_kernel"),
     (dict(Hq=32, Hkv=8, d=128, kv_cache_hint=3), "kv_cache_hint"),
+    (dict(Hq=32, Hkv=8, d=128, prefill_grid=3), "prefill_grid"),
 ])
 def test_unsupported_configs_are_rejected(kw, msg):
     Hq, Hkv, d = kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d")
@@ -80,14 +81,35 @@ def test_workspace_size_formula():
                                                        + up(8 * 4 * 64 * 4) + up(8 * 16 * 4) + up(8 * 16 * 4 * 4))
     assert ia.ia_decode_workspace_bytes(bc, 4, 100000) == (up(4 * 64 * 32 * 128 * 4) + up(4 * 64 * 32 * 2 * 4)
                                                           + up(4 * 64 * 4))
-    # prefill: none while no row can see keys of two splits; else the larger of per (query row, head)
-    # the merge so far and, while at most 64 MiB, per (query row, head, split) its state, d + 2
-    # floats each, in two arrays rounded up to 256 bytes
-    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2048) == 0
-    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 2049) == up(1000 * 32 * 2 * 128 * 4) + up(1000 * 32 * 2 * 2 * 4)
-    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 8192) == up(1000 * 32 * 4 * 128 * 4) + up(1000 * 32 * 4 * 2 * 4)
-    assert ia.ia_prefill_workspace_bytes(ctx, 1000, 8193) == up(1000 * 32 * 128 * 4) + up(1000 * 32 * 2 * 4)
-    assert ia.ia_prefill_workspace_bytes(ctx, 0, 4096) == 0
+    # prefill: none while no row can see keys of two splits; else per (query row, head) a state of
+    # d + 2 floats (two arrays rounded up to 256 bytes), and for the split grid B x r row blocks of
+    # 32 positions (group 4, bf16) x the splits past the first x Hq more, r = min(4, row blocks)
+    def states(e):
+        return up(e * 128 * 4) + up(e * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 8, 1000, 125, 2048) == 0
+    assert ia.ia_prefill_workspace_bytes(ctx, 0, 0, 0, 4096) == 0
+    # 8 sequences, 125 rows each (4 row blocks), keys up to 2049 (2 splits)
+    assert ia.ia_prefill_workspace_bytes(ctx, 8, 1000, 125, 2049) == states(1000 * 32) + states(8 * 4 * 32 * 1 * 32)
+    # up to 8192 keys: 3 splits past the first; at most 300 rows: 10 row blocks, 4 of them split
+    assert ia.ia_prefill_workspace_bytes(ctx, 4, 1000, 300, 8192) == states(1000 * 32) + states(4 * 4 * 32 * 3 * 32)
+    # ... unless total_q leaves no room for a sequence of at most 4 row blocks (128 positions)
+    assert ia.ia_prefill_workspace_bytes(ctx, 4, 1029, 300, 8192) == states(1029 * 32)
+    assert ia.ia_prefill_workspace_bytes(ctx, 4, 1028, 300, 8192) == states(1028 * 32) + states(4 * 4 * 32 * 3 * 32)
+    # 1 sequence of 64 rows (2 row blocks)
+    assert ia.ia_prefill_workspace_bytes(ctx, 1, 64, 64, 4096) == states(64 * 32) + states(1 * 2 * 32 * 1 * 32)
+    # 8192 or more (sequence, row block, kv head) workgroups: folds only
+    assert ia.ia_prefill_workspace_bytes(ctx, 8, 8 * 4096, 4096, 4096) == states(8 * 4096 * 32)
+    # split states over 128 MiB: the row blocks split per sequence halve until they fit (here to 1)
+    big = ia.ia_prefill_workspace_bytes(ctx, 8, 800, 100, 65536)
+    assert big == states(800 * 32) + states(8 * 1 * 32 * 31 * 32)
+    # a launch of 8192 or more workgroups with few row blocks: folds only
+    assert ia.ia_prefill_workspace_bytes(ctx, 1024, 1024, 1, 65536) == states(1024 * 32)
+    fold = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048, prefill_grid=ia.IA_PREFILL_FOLD))
+    assert ia.ia_prefill_workspace_bytes(fold, 8, 1000, 125, 2049) == states(1000 * 32)
+    split = ia.Context(ia.make_config(32, 8, 128, split_tokens=2048, prefill_grid=ia.IA_PREFILL_SPLIT))
+    assert ia.ia_prefill_workspace_bytes(split, 4, 1200, 300, 8192) == states(1200 * 32) + states(4 * 10 * 32 * 3 * 32)
+    # the Qwen3-8B chunks of 256 (8 x 256 rows, 8 row blocks each) split nothing under AUTO
+    assert ia.ia_prefill_workspace_bytes(ctx, 8, 2048, 256, 4096) == states(2048 * 32)
 
 
 FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation first
@@ -139,11 +161,11 @@ def test_append_and_prefill_argument_errors():
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, None, 0,
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in ia.ia_last_error()
-    # the size returned holds the split-grid layout (10 rows x 8 heads x 2 splits); the launch
-    # needs at least the in-workgroup layout (10 rows x 8 heads)
+    # the launch needs at least the row states (10 rows x 8 heads); the size returned also holds
+    # the split states (2 sequences x 1 row block of 32 positions x 1 more split x 8 heads)
     up = lambda x: (x + 255) // 256 * 256
-    assert ia.ia_prefill_workspace_bytes(ctx, 10, 200) == up(10 * 8 * 2 * 64 * 4) + up(10 * 8 * 2 * 2 * 4)
     need = up(10 * 8 * 64 * 4) + up(10 * 8 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 2, 10, 5, 200) == need + up(2 * 32 * 8 * 64 * 4) + up(2 * 32 * 8 * 2 * 4)
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, FAKE, need - 1,
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
 
@@ -151,7 +173,9 @@ def test_append_and_prefill_argument_errors():
 def test_binding_constants_match_header():
     import re
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "invattn.h")).read()
-    for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_DECODE_SPREAD", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT"):
+    for name in ("IA_DECODE_AUTO", "IA_DECODE_SPLIT", "IA_DECODE_WIDE", "IA_DECODE_SPREAD", "IA_SPLIT_FIXED", "IA_SPLIT_BY_COUNT",
+                 "IA_KV_HINT_AUTO", "IA_KV_HINT_STREAM", "IA_KV_HINT_CACHED", "IA_PREFILL_AUTO", "IA_PREFILL_FOLD",
+                 "IA_PREFILL_SPLIT"):
         m = re.search(name + r" = (\d+)", hdr)
         assert m and int(m.group(1)) == getattr(ia, name), name
 

@@ -6,9 +6,9 @@ lengths drawn from a seeded generator, edge lengths mixed in):
 - decode with each kernel (AUTO, SPLIT, WIDE, SPREAD) and both cache hints matches the oracle
   within |err| <= 2e-3 + 1e-2 |ref|, and all of them give the same bits;
 - chunked prefill of the last q_len positions of each sequence matches the oracle, and gives the
-  same bits with a workspace that holds only the in-workgroup fold layout (each workgroup folds
-  its rows' splits) as with the size the library asks for (a launch this small then runs one
-  workgroup per split and a separate merge);
+  same bits under each prefill grid: in-workgroup folds (each workgroup folds its rows' splits),
+  the split grid for every sequence (one workgroup per split, then a merge kernel), and the
+  automatic choice; also the split grid given only the workspace the folds need (it then folds);
 - the prefill row of each sequence's last position has exactly the decode output's bits (a
   decode row and the prefill row at the same position run the same operations in the same order:
   Vosti §5.3, the causal contract between prefill and decode)."""
@@ -107,11 +107,12 @@ def test_sweep_case(case):
     ok, err, ratio = gs.within_tolerance(pf, ref_pf)
     assert ok, f"{label} prefill: max err {err:.3e} ({ratio:.2f} of the bound)"
     if max(lens) > shape.S:
-        up = lambda x: (x + 255) // 256 * 256
         rows = int(q_pf.shape[0]) * shape.Hq
-        folds = gs.prefill(ctx0, pages, q_pf, cu_pf, layout, lens,
-                           workspace_bytes=up(rows * shape.d * 4) + up(rows * 2 * 4))
-        torch.cuda.synchronize()
-        assert np.array_equal(gs.bits(folds), gs.bits(pf)), f"{label}: split grid and in-workgroup folds differ"
+        fold_only = (rows * shape.d * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256
+        for grid, ws in ((ia.IA_PREFILL_FOLD, None), (ia.IA_PREFILL_SPLIT, None), (ia.IA_PREFILL_SPLIT, fold_only)):
+            ctx_g = gs.make_ctx(shape, fp8=fp8, window=window, prefill_grid=grid)
+            o = gs.prefill(ctx_g, pages, q_pf, cu_pf, layout, lens, workspace_bytes=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(gs.bits(o), gs.bits(pf)), f"{label}: prefill grid {grid} (workspace {ws}) differs"
     last_rows = gs.bits(pf)[np.asarray(cu_pf[1:]) - 1]
     assert np.array_equal(last_rows, outs[0]), f"{label}: prefill's last rows differ from decode in bits"
