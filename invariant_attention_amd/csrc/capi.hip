@@ -253,14 +253,27 @@ static int prefill_max_splits(const ia_ctx* ctx, int32_t max_seq_len) {
   return (int)ceil_div(max_seq_len, ctx->cfg.split_tokens);
 }
 
-static int64_t prefill_row_blocks(const ia_ctx* ctx, int32_t max_q_len) {
-  return ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3));
+// Row blocks per wave (2 for bf16 pages, 1 for launches that would leave
+// compute units idle with 2, and for e4m3 pages), and positions per
+// workgroup.
+static int prefill_rb(const ia_ctx* ctx, int32_t B, int32_t max_q_len) {
+  const int64_t units2 = (int64_t)B * ceil_div(max_q_len, ia::prefill_positions_per_block(ctx->group, 2)) *
+                         ctx->cfg.num_kv_heads;
+  return ia::prefill_rows_per_wave(ctx->cfg.kv_dtype == IA_KV_FP8_E4M3, units2);
+}
+
+static int64_t prefill_ppg(const ia_ctx* ctx, int32_t B, int32_t max_q_len) {
+  return ia::prefill_positions_per_block(ctx->group, prefill_rb(ctx, B, max_q_len));
+}
+
+static int64_t prefill_row_blocks(const ia_ctx* ctx, int32_t B, int32_t max_q_len) {
+  return ceil_div(max_q_len, prefill_ppg(ctx, B, max_q_len));
 }
 
 // Entries of the split states of splits 1 .. for split_rbs row blocks.
-static int64_t prefill_split_entries(const ia_ctx* ctx, int32_t B, int32_t max_seq_len, int rbs) {
-  const int ppg = ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3);
-  return (int64_t)B * rbs * ppg * (prefill_max_splits(ctx, max_seq_len) - 1) * ctx->cfg.num_q_heads;
+static int64_t prefill_split_entries(const ia_ctx* ctx, int32_t B, int32_t max_q_len, int32_t max_seq_len, int rbs) {
+  return (int64_t)B * rbs * prefill_ppg(ctx, B, max_q_len) * (prefill_max_splits(ctx, max_seq_len) - 1) *
+         ctx->cfg.num_q_heads;
 }
 
 // Row blocks per sequence that a launch splits (0: none), before the
@@ -270,12 +283,13 @@ static int64_t prefill_split_entries(const ia_ctx* ctx, int32_t B, int32_t max_s
 static int prefill_split_rbs(const ia_ctx* ctx, int32_t B, int32_t total_q, int32_t max_q_len, int32_t max_seq_len) {
   if (ctx->cfg.prefill_grid == IA_PREFILL_FOLD || max_seq_len <= ctx->cfg.split_tokens || B <= 0 || max_q_len <= 0)
     return 0;
-  const int64_t rb = prefill_row_blocks(ctx, max_q_len);
+  const int64_t rb = prefill_row_blocks(ctx, B, max_q_len);
   if ((int64_t)B * rb * ctx->cfg.num_kv_heads >= kSplitMaxUnits) return 0;
   int64_t rbs = ctx->cfg.prefill_grid == IA_PREFILL_SPLIT ? rb : (rb < kSplitMaxRowBlocks ? rb : kSplitMaxRowBlocks);
-  const int64_t ppg = ia::prefill_positions_per_block(ctx->group, ctx->cfg.kv_dtype == IA_KV_FP8_E4M3);
+  const int64_t ppg = prefill_ppg(ctx, B, max_q_len);
   if (rbs < rb && (int64_t)total_q > (int64_t)(B - 1) * max_q_len + rbs * ppg) return 0;
-  while (rbs > 0 && prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_seq_len, (int)rbs)) > kSplitMaxBytes)
+  while (rbs > 0 &&
+         prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_q_len, max_seq_len, (int)rbs)) > kSplitMaxBytes)
     rbs /= 2;
   return (int)rbs;
 }
@@ -285,7 +299,7 @@ size_t ia_prefill_workspace_bytes(const ia_ctx* ctx, int32_t B, int32_t total_q,
   if (!ctx || B <= 0 || total_q <= 0 || max_q_len <= 0 || max_seq_len <= ctx->cfg.split_tokens) return 0;
   const int rbs = prefill_split_rbs(ctx, B, total_q, max_q_len, max_seq_len);
   return prefill_state_bytes(ctx, (int64_t)total_q * ctx->cfg.num_q_heads) +
-         (rbs ? prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_seq_len, rbs)) : 0);
+         (rbs ? prefill_state_bytes(ctx, prefill_split_entries(ctx, B, max_q_len, max_seq_len, rbs)) : 0);
 }
 
 ia_status ia_kv_append(const ia_ctx* ctx, const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -444,7 +458,7 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
     return fail(IA_ERR_INVALID_ARG, "max_q_len and max_seq_len must be positive when total_q > 0");
   if ((int64_t)bt_stride * ctx->cfg.page_size < max_seq_len)
     return fail(IA_ERR_INVALID_ARG, "bt_stride (%d) pages cannot hold max_seq_len (%d) keys", bt_stride, max_seq_len);
-  const int64_t row_blocks = prefill_row_blocks(ctx, max_q_len);
+  const int64_t row_blocks = prefill_row_blocks(ctx, B, max_q_len);
   if ((int64_t)B * row_blocks * ctx->cfg.num_kv_heads >= ((int64_t)1 << 31))
     return fail(IA_ERR_INVALID_ARG, "grid too large");
   if ((int64_t)total_q * ctx->cfg.num_q_heads >= ((int64_t)1 << 31))
@@ -467,6 +481,7 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
   a.block_table = block_table;
   a.out = static_cast<__bf16*>(out);
   a.max_splits = prefill_max_splits(ctx, max_seq_len);
+  a.rb = prefill_rb(ctx, B, max_q_len);
   a.ws_u = a.ws_mz = a.sg_u = a.sg_mz = nullptr;
   a.split_rbs = 0;
   if (multi_split) {
@@ -478,7 +493,7 @@ ia_status ia_paged_attn_prefill(const ia_ctx* ctx, const void* q, const int32_t*
     // of the size ia_prefill_workspace_bytes reports does).
     const int rbs = prefill_split_rbs(ctx, B, total_q, max_q_len, max_seq_len);
     if (rbs > 0) {
-      const int64_t entries = prefill_split_entries(ctx, B, max_seq_len, rbs);
+      const int64_t entries = prefill_split_entries(ctx, B, max_q_len, max_seq_len, rbs);
       const int64_t grid = (int64_t)B * ctx->cfg.num_kv_heads * (row_blocks + (int64_t)rbs * (a.max_splits - 1));
       if (ws_bytes >= fold_bytes + prefill_state_bytes(ctx, entries) && grid < ((int64_t)1 << 31)) {
         a.split_rbs = rbs;

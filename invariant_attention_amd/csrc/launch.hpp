@@ -69,6 +69,7 @@ struct PrefillArgs {
   int split_rbs;              // sequences of at most this many row blocks whose keys reach a
                               // second split run one workgroup per split (0: none)
   int max_splits;             // ceil(max_seq_len / split_tokens)
+  int rb;                     // 16-row blocks per wave (prefill_rows_per_wave)
   float c;
   int B, Hq, Hkv, group;
   int bt_stride, num_pages;
@@ -81,9 +82,13 @@ struct PrefillArgs {
 hipError_t launch_kv_append(int D, bool fp8, const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(int D, bool fp8, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st);
-// Query positions one prefill workgroup covers (its grid has
-// ceil(max_q_len / this) row blocks per (sequence, kv head)).
-int prefill_positions_per_block(int group, bool fp8);
+// Row blocks per wave of a prefill launch: fp8 pages 1; bf16 pages 2, or 1
+// when the launch would have fewer than 256 workgroups with 2 (units_two_blocks:
+// its (sequence, row block, kv head) count with 2).
+int prefill_rows_per_wave(bool fp8, int64_t units_two_blocks);
+// Query positions one prefill workgroup covers at rb row blocks per wave (its
+// grid has ceil(max_q_len / this) row blocks per (sequence, kv head)).
+int prefill_positions_per_block(int group, int rb);
 
 // Layer operators (layer_ops.hip).
 hipError_t launch_rmsnorm(const __bf16* x, const __bf16* w, __bf16* y, int M, int H, float eps, hipStream_t st);

@@ -56,11 +56,15 @@ constexpr int kPrefillWaves = 4;       // per workgroup; two workgroups per comp
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 // 16-row blocks per wave, sharing every K/V fragment read: two for bf16
 // pages; one for e4m3 pages, whose staging registers leave no room for a
-// second block within the 256 VGPRs of two waves per SIMD.
+// second block within the 256 VGPRs of two waves per SIMD.  bf16 launches
+// of fewer row-block workgroups than compute units take one block per wave
+// instead, which doubles their workgroups (a row's operations do not depend
+// on the other rows of its wave, so the bits are the same).
 template <bool FP8>
 constexpr int row_blocks_per_wave() {
   return FP8 ? 1 : 2;
 }
+constexpr int kSmallLaunchUnits = 256;
 constexpr int kStageTiles = 1;         // tiles per LDS slot (two slots)
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
@@ -354,10 +358,9 @@ __device__ __forceinline__ void store_split(float* u, float* mz, const RowState<
   if (g == 0) *reinterpret_cast<f32x2*>(mz + 2 * e) = f32x2{st.m, st.z};
 }
 
-// Positions one prefill workgroup covers.
-template <bool FP8>
-__device__ __forceinline__ int positions_per_workgroup(int group) {
-  return (kRows / group) * row_blocks_per_wave<FP8>() * kPrefillWaves;
+// Positions one prefill workgroup of the launch covers.
+__device__ __forceinline__ int positions_per_workgroup(const PrefillArgs& a) {
+  return (kRows / a.group) * a.rb * kPrefillWaves;
 }
 
 // Whether a sequence runs split grid: the launch splits sequences of at most
@@ -382,7 +385,7 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(64 * kMergeWaves) void prefill_merge_kernel(PrefillArgs a) {
   constexpr int kPer = D / 64;
   const int lane = threadIdx.x & 63;
-  const int ppg = positions_per_workgroup<FP8>(a.group);
+  const int ppg = positions_per_workgroup(a);
   const int rows = a.split_rbs * ppg;
   const int64_t item = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   const int hq = (int)(item % a.Hq);
@@ -424,9 +427,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void prefill_merge_kernel(Prefill
   for (int k = 0; k < kPer; ++k) out[k] = finalize(U[k], vs, rz);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int kRB>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int kRB = row_blocks_per_wave<FP8>();
+  static_assert(kRB >= 1 && kRB <= row_blocks_per_wave<FP8>(), "row blocks per wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   constexpr int kTileBytes = tile_lds_bytes<D>();
   const int tid = threadIdx.x;
@@ -707,34 +710,39 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillArgs
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int RB>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (a.B == 0 || a.max_q_len == 0) return hipSuccess;
   const int64_t pairs = (int64_t)a.B * a.Hkv;
   const int64_t units = pairs * a.max_row_blocks + (a.split_rbs ? pairs * a.split_rbs * (a.max_splits - 1) : 0);
   const int lds = 2 * kStageTiles * tile_lds_bytes<D>();  // two slots of a stage (64 KiB at head_dim 128)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, RB>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3((unsigned)units), dim3(kPrefillThreads), lds, st, a);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, RB>), dim3((unsigned)units), dim3(kPrefillThreads), lds, st, a);
   if (!a.split_rbs) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t items = (int64_t)a.B * a.split_rbs * prefill_positions_per_block(a.group, FP8) * a.Hq;
+  const int64_t items = (int64_t)a.B * a.split_rbs * prefill_positions_per_block(a.group, RB) * a.Hq;
   hipLaunchKernelGGL((prefill_merge_kernel<D, FP8>), dim3((unsigned)((items + kMergeWaves - 1) / kMergeWaves)),
                      dim3(64 * kMergeWaves), 0, st, a);
   return hipGetLastError();
 }
 
-int prefill_positions_per_block(int group, bool fp8) {
-  return (kRows / group) * (fp8 ? row_blocks_per_wave<true>() : row_blocks_per_wave<false>()) * kPrefillWaves;
+int prefill_rows_per_wave(bool fp8, int64_t units_two_blocks) {
+  return fp8 || units_two_blocks < kSmallLaunchUnits ? 1 : row_blocks_per_wave<false>();
 }
 
+int prefill_positions_per_block(int group, int rb) { return (kRows / group) * rb * kPrefillWaves; }
+
 hipError_t launch_prefill(int D, bool fp8, const PrefillArgs& a, hipStream_t st) {
-  if (D == 128 && fp8) return launch_prefill_t<128, true>(a, st);
-  if (D == 128) return launch_prefill_t<128, false>(a, st);
-  if (D == 64 && fp8) return launch_prefill_t<64, true>(a, st);
-  if (D == 64) return launch_prefill_t<64, false>(a, st);
+  if (a.rb != 1 && (fp8 || a.rb != row_blocks_per_wave<false>())) return hipErrorInvalidValue;
+  if (D == 128 && fp8) return launch_prefill_t<128, true, 1>(a, st);
+  if (D == 128 && a.rb == 1) return launch_prefill_t<128, false, 1>(a, st);
+  if (D == 128) return launch_prefill_t<128, false, 2>(a, st);
+  if (D == 64 && fp8) return launch_prefill_t<64, true, 1>(a, st);
+  if (D == 64 && a.rb == 1) return launch_prefill_t<64, false, 1>(a, st);
+  if (D == 64) return launch_prefill_t<64, false, 2>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -95,8 +95,11 @@ def test_workspace_size_formula():
     # ... unless total_q leaves no room for a sequence of at most 4 row blocks (128 positions)
     assert ia.ia_prefill_workspace_bytes(ctx, 4, 1029, 300, 8192) == states(1029 * 32)
     assert ia.ia_prefill_workspace_bytes(ctx, 4, 1028, 300, 8192) == states(1028 * 32) + states(4 * 4 * 32 * 3 * 32)
-    # 1 sequence of 64 rows (2 row blocks)
-    assert ia.ia_prefill_workspace_bytes(ctx, 1, 64, 64, 4096) == states(64 * 32) + states(1 * 2 * 32 * 1 * 32)
+    # 1 sequence of 64 rows: 8 workgroups with 2 row blocks per wave, fewer than the 256 compute
+    # units, so 1 row block per wave (16 positions per workgroup): 4 row blocks, all split
+    assert ia.ia_prefill_workspace_bytes(ctx, 1, 64, 64, 4096) == states(64 * 32) + states(1 * 4 * 16 * 1 * 32)
+    # 8 sequences of 64 rows (the Qwen3-8B chunks of 64): 128 workgroups, 1 row block per wave
+    assert ia.ia_prefill_workspace_bytes(ctx, 8, 512, 64, 4096) == states(512 * 32) + states(8 * 4 * 16 * 1 * 32)
     # 8192 or more (sequence, row block, kv head) workgroups: folds only
     assert ia.ia_prefill_workspace_bytes(ctx, 8, 8 * 4096, 4096, 4096) == states(8 * 4096 * 32)
     # split states over 128 MiB: the row blocks split per sequence halve until they fit (here to 1)
@@ -162,10 +165,11 @@ def test_append_and_prefill_argument_errors():
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in ia.ia_last_error()
     # the launch needs at least the row states (10 rows x 8 heads); the size returned also holds
-    # the split states (2 sequences x 1 row block of 32 positions x 1 more split x 8 heads)
+    # the split states: 2 sequences x 1 row block x 1 more split x 8 heads, the row block of 16
+    # positions (a launch this small runs one 16-row block per wave: 4 positions x 4 waves)
     up = lambda x: (x + 255) // 256 * 256
     need = up(10 * 8 * 64 * 4) + up(10 * 8 * 2 * 4)
-    assert ia.ia_prefill_workspace_bytes(ctx, 2, 10, 5, 200) == need + up(2 * 32 * 8 * 64 * 4) + up(2 * 32 * 8 * 2 * 4)
+    assert ia.ia_prefill_workspace_bytes(ctx, 2, 10, 5, 200) == need + up(2 * 16 * 8 * 64 * 4) + up(2 * 16 * 8 * 2 * 4)
     assert pre(ctx.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 64, 2, 10, 5, 200, FAKE, FAKE, need - 1,
                None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
 
