@@ -104,7 +104,7 @@ typedef enum { IA_SPLIT_FIXED = 0, IA_SPLIT_BY_COUNT = 1 } ia_split_policy;
  *     value updates for its dims.  The intermediate values live in the
  *     workspace.  Launches whose buffer would exceed 32768 (split, tile)
  *     slots run on SPLIT.
- *   IA_DECODE_AUTO runs SPREAD for launches of at most 64 split units
+ *   IA_DECODE_AUTO runs SPREAD for launches of at most 32 split units
  *     (batch x kv heads x splits of max_seq_len) whose splits are at most 32
  *     tiles (2048 keys) with at most 4 query heads per kv head, and SPLIT
  *     otherwise (measured: outside that range SPLIT is faster). */

@@ -64,7 +64,7 @@ int64_t decode_max_splits(const ia_ctx* ctx, int64_t batch, int64_t max_seq_len)
 // launches with few split units, where one compute unit per split leaves the
 // chip idle; it gives the split kernel's bits, so the choice below decides
 // speed only.  Its score buffer holds one slot per (unit, tile).
-constexpr int64_t kSpreadMaxUnits = 64;        // IA_DECODE_AUTO: at most this many split units
+constexpr int64_t kSpreadMaxUnits = 32;        // IA_DECODE_AUTO: at most this many split units
 constexpr int64_t kSpreadMaxSlots = 1 << 15;   // slots: <= 128 MiB of scores at 16 rows
 // IA_KV_HINT_AUTO: nontemporal page loads for launches of at least this many
 // split units (measured faster from about 700 units up on private pages, and

@@ -68,7 +68,7 @@ def test_workspace_size_formula():
     assert got == up(rows * 128 * 4) + up(rows * 2 * 4) + up(256 * 4 * 4)
     assert ia.ia_decode_workspace_bytes(ctx, 0, 8192) == 0
     bc = ia.Context(ia.make_config(32, 8, 128, split_policy=ia.IA_SPLIT_BY_COUNT))
-    # a launch of at most 64 split units runs the spread kernels, which add one slot per
+    # a launch of at most 32 split units runs the spread kernels, which add one slot per
     # (sequence, split, kv head, tile): group x 64 fp32 scores, 16 fp32 row maxima, 16 (alpha, sum, max, 0)
     slots = 1 * 4 * 8 * 32
     assert ia.ia_decode_workspace_bytes(ctx, 1, 8192) == (up(4 * 32 * 128 * 4) + up(4 * 32 * 2 * 4) + up(4 * 4)
