@@ -331,7 +331,7 @@ def summarize_spread_profile(trace_dir):
     print(SPREAD_PROFILE_MD)
 
 
-PREFILL_KERNEL = "prefill_kernel<128, false>"
+PREFILL_KERNEL = "prefill_kernel<128, false, 2>"
 PREFILL_SQ = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
               "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES"]
 # A second pass: issue, co-execution and waits (the SQ block takes at most 8 counters a run).
@@ -448,7 +448,7 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
     ws_rows = sum(max(0, n - shape.S) for n in lens) * shape.Hq  # rows that see two splits
     ws_bytes = ws_rows * (shape.d + 2) * 4
     lines = [
-        "# prefill_kernel<128, bf16> -- Qwen3-8B-shaped whole prefill, 8 prompts x 4096 tokens, causal",
+        "# prefill_kernel<128, bf16, 2 row blocks per wave> -- Qwen3-8B-shaped whole prefill, 8 prompts x 4096 tokens, causal",
         "",
         "32 query / 8 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits; algorithmic "
         f"flops per launch {flops:.6e} (4 x d x Hq x sum over rows of the p + 1 visible keys).",

@@ -159,7 +159,7 @@ def test_auto_with_a_workspace_sized_for_the_split_kernel_only():
     # Under AUTO a small launch runs the spread kernels; given only the split kernel's workspace it runs
     # the split kernel instead.  Both calls give the same bits.
     shape = wl.LLAMA3_8B
-    lens = [5000, 77]
+    lens = [3000, 77]  # 2 sequences x 8 kv heads x 2 splits = 32 units: AUTO's spread range
     seqs, layout, pages, q = _world(shape, lens)
     ctx = gs.make_ctx(shape)
     full = gs.decode(ctx, pages, q, layout, lens)
