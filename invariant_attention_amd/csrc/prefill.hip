@@ -20,6 +20,14 @@
 // all of a wave's positions are skipped, which is the identity on its rows'
 // states.
 //
+// Small launches.  A launch of fewer row-block workgroups than compute units
+// takes one row block per wave (twice the workgroups).  A sequence of few
+// row blocks whose keys reach a second split (decode rows co-batched with
+// prompts, short chunks of long prompts) can run split grid: one workgroup
+// per (row block, kv head, split) walks only that split's tiles and stores
+// its rows' split states, and prefill_merge_kernel folds them in ascending
+// order.  A row's operations and their order are the same in every case.
+//
 // Staging.  Tiles pass through two LDS slots: while the waves compute tile t,
 // the workgroup's loads of tile t+1 are in flight into the other slot; one
 // barrier per tile.  bf16 pages go from memory straight into LDS

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+from invariant_attention_amd import binding as ia
 from oracle import oracle
 from synth import workloads as wl
 from tests import gpu_side as gs
@@ -93,11 +94,14 @@ def test_qwen235b_long_decode_batch1_vs_16(qwen_mixed):
 def test_qwen235b_mixed_batch_equals_alone(qwen_mixed):
     """16 decode rows at 32768 context co-batched with 4 fresh 512-token prompts in one prefill
     call: every row equals its own run (decode entry for the decode rows, one prefill call per
-    prompt), and sampled rows match the oracle."""
+    prompt), and sampled rows match the oracle.  The call runs the decode rows one workgroup per
+    split (the automatic prefill grid) and gives the bits of in-workgroup folds."""
     shape, lens, layout, seqs, ctx, pages = qwen_mixed
     q_lens = [1] * 16 + [512] * 4
     q, cu = osd.queries(shape, seqs, SEED, q_lens)
     mixed = gs.prefill(ctx, pages, q, cu, layout, lens)
+    folds = gs.prefill(gs.make_ctx(shape, prefill_grid=ia.IA_PREFILL_FOLD), pages, q, cu, layout, lens)
+    assert _eq(mixed, folds)
     sub = wl.PageLayout(layout.num_pages, layout.block_table[:16], layout.pages[:16])
     alone_dec = gs.decode(ctx, pages, q[:16], sub, lens[:16])
     assert _eq(mixed[:16], alone_dec)
