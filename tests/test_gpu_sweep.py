@@ -116,3 +116,34 @@ def test_sweep_case(case):
             assert np.array_equal(gs.bits(o), gs.bits(pf)), f"{label}: prefill grid {grid} (workspace {ws}) differs"
     last_rows = gs.bits(pf)[np.asarray(cu_pf[1:]) - 1]
     assert np.array_equal(last_rows, outs[0]), f"{label}: prefill's last rows differ from decode in bits"
+
+
+@pytest.mark.parametrize("fp8,window", [(False, 0), (True, 0), (False, 300), (True, 300)])
+def test_prefill_grids_with_empty_short_and_long_sequences(fp8, window):
+    """One prefill call mixing sequences that the automatic grid splits (long keys, at most 4 row
+    blocks), sequences with no rows, sequences within one split, and a long sequence of more row
+    blocks (split only under IA_PREFILL_SPLIT): the three grids give the same bits, and the rows
+    match the oracle."""
+    shape = wl.AttnShape(Hq=16, Hkv=4, d=64, P=16, S=256)
+    lens = [1500, 90, 700, 2000, 256, 257, 3000, 40]
+    q_lens = [3, 0, 16, 200, 1, 257, 0, 40]
+    label = f"fp8={fp8} window={window}"
+    print(label, flush=True)
+    seqs = wl.make_sequences(lens)
+    layout = wl.layout_pages(91, lens, shape.P)
+    ks, vs = wl.fp8_scales(92, shape.Hkv, power_of_two=False) if fp8 else (None, None)
+    ref, q, cu, _, _ = osd.run_oracle(shape, seqs, layout, 93, q_lens, fp8=fp8, k_scale=ks, v_scale=vs,
+                                      window=window)
+    ctx0 = gs.make_ctx(shape, fp8=fp8, window=window)
+    pages = gs.DevicePages(shape, layout.num_pages, fp8, ks, vs)
+    gs.fill_sequences(ctx0, pages, seqs, layout, 93)
+    outs = []
+    for grid in (ia.IA_PREFILL_AUTO, ia.IA_PREFILL_FOLD, ia.IA_PREFILL_SPLIT):
+        ctx = gs.make_ctx(shape, fp8=fp8, window=window, prefill_grid=grid)
+        out = gs.prefill(ctx, pages, q, cu, layout, lens)
+        torch.cuda.synchronize()
+        ok, err, ratio = gs.within_tolerance(out, ref)
+        assert ok, f"{label} grid {grid}: max err {err:.3e} ({ratio:.2f} of the bound)"
+        outs.append(gs.bits(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), f"{label}: prefill grids differ in bits"
