@@ -24,6 +24,14 @@ namespace ia {
 
 constexpr int kDecodeWaves = 4;
 constexpr int kBtWindowTiles = 256;  // block-table entries staged per LDS refill: 4 per tile
+constexpr int kOrderBuckets = 64;  // last-split lengths, in tiles; longer ones share bucket 0
+// Launches of at most kSelfOrderMaxB sequences, more than kSelfOrderMinUnits
+// units and fewer than take the dispatch-order list have each workgroup find
+// its own unit in that order (measured on the Llama-3-8B shape, contexts
+// U[512, 8192]: +2.5% at batch 16, +2.8% at batch 48, the same at 32 and 64;
+// at batch 8, one round of units, 1.5% slower, hence the lower bound).
+constexpr int kSelfOrderMaxB = 64;
+constexpr int64_t kSelfOrderMinUnits = 256;
 
 // Split length for sequence b: the fixed deployment constant, or (comparison
 // variant only) the load-based length roundup(ceil(n / k), 64) with
@@ -147,6 +155,46 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(DecodeArgs a) {
     if (e < 0) return;  // past the listed units; uniform over the workgroup
     b = e / a.max_splits;
     s = e % a.max_splits;
+  } else if (a.self_order) {
+    // The same order for a launch of few sequences, found by every
+    // workgroup itself instead of by decode_order_kernel: whole splits first
+    // (by sequence), then the last splits by decreasing length in tiles (by
+    // sequence among equal lengths).  Thread t takes sequence t.
+    __shared__ int nf_s[kSelfOrderMaxB], q_s[kSelfOrderMaxB], pick[2];
+    const int t = threadIdx.x;
+    if (t == 0) pick[0] = -1;
+    if (t < a.B) {
+      const int nt = clamp_len(a.seq_lens[t], a.max_seq_len);
+      const int St = split_len(a.policy, a.split_tokens, nt, a.B);
+      const int nf = nt / St;
+      const int tiles = (nt - nf * St + kTileKeys - 1) / kTileKeys;
+      nf_s[t] = nf;
+      q_s[t] = tiles > 0 ? kOrderBuckets - (tiles < kOrderBuckets ? tiles : kOrderBuckets) : -1;
+    }
+    __syncthreads();
+    const int e = unit / a.Hkv;
+    if (t < a.B) {
+      int f0 = 0, whole = 0, rank = 0;
+      const int qt = q_s[t];
+      for (int i = 0; i < a.B; ++i) {
+        const int nfi = nf_s[i], qi = q_s[i];
+        whole += nfi;
+        f0 += i < t ? nfi : 0;
+        rank += (qi >= 0 && (qi < qt || (qi == qt && i < t))) ? 1 : 0;
+      }
+      if (e >= f0 && e < f0 + nf_s[t]) {
+        pick[0] = t;
+        pick[1] = e - f0;
+      }
+      if (qt >= 0 && e == whole + rank) {
+        pick[0] = t;
+        pick[1] = nf_s[t];
+      }
+    }
+    __syncthreads();
+    b = pick[0];
+    s = pick[1];
+    if (b < 0) return;  // past the listed units; uniform over the workgroup
   } else {
     b = (unit / a.Hkv) % a.B;
     s = unit / a.Hkv / a.B;
@@ -914,7 +962,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxB = kOrderThreads;
 constexpr int kOrderMinUnits = 2048;
-constexpr int kOrderBuckets = 64;  // last-split lengths, in tiles; longer ones share bucket 0
 
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a) {
   __shared__ int full_next;             // next free place in the whole-split part
@@ -996,12 +1043,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_wide_kernel<D, FP8>), dim3((unsigned)units), dim3(64 * kWideWaves), 0, st, a);
   } else {
     DecodeArgs sa = a;
+    sa.self_order = 0;
     if (a.order && a.B <= kOrderMaxB && units >= kOrderMinUnits) {
       hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, st, a);
       const hipError_t oe = hipGetLastError();
       if (oe != hipSuccess) return oe;
     } else {
       sa.order = nullptr;
+      sa.self_order = a.B <= kSelfOrderMaxB && units > kSelfOrderMinUnits;
     }
     if (a.nt)
       hipLaunchKernelGGL((decode_split_kernel<D, FP8, true>), dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, st, sa);

@@ -44,6 +44,8 @@ struct DecodeArgs {
                                // (score, weight, value); all give the same bits
   int tps;                     // spread: tile slots per split (the longest split of the launch, in tiles)
   int nt;                      // split kernel: nontemporal page loads (caching only, never values)
+  int self_order;              // split kernel without an order list: each workgroup finds its unit
+                               // in the list's order (B <= kSelfOrderMaxB)
 };
 
 struct PrefillArgs {
