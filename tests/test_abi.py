@@ -207,3 +207,26 @@ def test_layer_ops_empty_batch_is_a_noop_without_pointers():
     lib = ia.load()
     assert lib.ia_rmsnorm(None, None, 0, 64, 1e-5, None, None) == ia.IA_OK
     assert lib.ia_gemm_bf16(None, None, 0, 256, 64, None, None) == ia.IA_OK
+
+
+def test_header_is_plain_c_and_config_layout_matches_binding(tmp_path):
+    """include/invattn.h compiles as C99 (-pedantic, no warnings), and a C caller's ia_config has
+    the size and field offsets the ctypes binding passes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in ia.ia_config._fields_]
+    src = tmp_path / "hdr.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"invattn.h\"\nint main(void) {\n"
+                   "  printf(\"%zu\", sizeof(ia_config));\n"
+                   + "".join(f"  printf(\" %zu\", offsetof(ia_config, {f}));\n" for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "hdr"
+    proc = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                           os.path.dirname(HEADER), "-o", str(exe), str(src)], capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stderr
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(ia.ia_config)
+    assert out[1:] == [getattr(ia.ia_config, f).offset for f in fields]
