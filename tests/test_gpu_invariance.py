@@ -147,6 +147,23 @@ def test_v10_grid_bound_does_not_change_bits():
     assert _eq(w.decode_rows(max_seq_len=32768), base)
 
 
+def test_v10_prefill_grid_bounds_do_not_change_bits():
+    # max_q_len and max_seq_len size the prefill grid only.  Raising them changes the launch's
+    # plan -- rows per wave (one row block for a launch this small, two once the bound makes it
+    # large), which sequences run one workgroup per split, the split states' layout -- and no bit.
+    w = World(wl.LLAMA3_8B, [3000, 5000, 700, 2100], width=2048)
+    idx, q_lens = [0, 1, 2, 3], [64, 1, 40, 17]
+    seq_lens = [w.seqs[b].n for b in idx]
+    qs = torch.cat([w.seqs[b].q(SEED, w.shape, n - ql, n) for b, ql, n in zip(idx, q_lens, seq_lens)], 0)
+    cu = np.zeros(len(idx) + 1, np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    sub = wl.PageLayout(w.layout.num_pages, w.layout.block_table[idx], [w.layout.pages[b] for b in idx])
+    base = gs.prefill(w.ctx, w.pages, qs, cu, sub, seq_lens)
+    for mql, msl in ((64, 5000), (300, 5000), (512, 8192), (4096, 32768)):
+        out = gs.prefill(w.ctx, w.pages, qs, cu, sub, seq_lens, max_seq_len=msl, max_q_len=mql)
+        assert _eq(out, base), (mql, msl)
+
+
 # ------------------------------------------------------------- V5 / V9 / V3
 
 @pytest.mark.parametrize("shape,lens", [(wl.TINY, list(wl.TINY_LENS)),
