@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from invariant_attention_amd import binding as ia
@@ -230,3 +231,27 @@ def test_header_is_plain_c_and_config_layout_matches_binding(tmp_path):
     out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(ia.ia_config)
     assert out[1:] == [getattr(ia.ia_config, f).offset for f in fields]
+
+
+def test_prefill_workspace_bounds_over_random_launch_shapes():
+    """Over random launch bounds: no workspace while no row can see two splits; otherwise at
+    least the per-row states (what the launch requires), at most 128 MiB more for the split grid
+    (plus alignment), and exactly the per-row states under IA_PREFILL_FOLD."""
+    rng = np.random.default_rng(5)
+    up = lambda x: (x + 255) // 256 * 256
+    for Hq, Hkv, d, S in ((32, 8, 128, 2048), (64, 4, 128, 2048), (8, 2, 64, 128)):
+        auto = ia.Context(ia.make_config(Hq, Hkv, d, split_tokens=S))
+        fold = ia.Context(ia.make_config(Hq, Hkv, d, split_tokens=S, prefill_grid=ia.IA_PREFILL_FOLD))
+        split = ia.Context(ia.make_config(Hq, Hkv, d, split_tokens=S, prefill_grid=ia.IA_PREFILL_SPLIT))
+        for _ in range(300):
+            B = int(rng.integers(1, 300))
+            mql = int(rng.integers(1, 5000))
+            total_q = int(rng.integers(1, B * mql + 1))
+            msl = int(rng.integers(mql, 140000))
+            rows = total_q * Hq
+            need = up(rows * d * 4) + up(rows * 2 * 4) if msl > S else 0
+            assert ia.ia_prefill_workspace_bytes(fold, B, total_q, mql, msl) == need
+            for c in (auto, split):
+                got = ia.ia_prefill_workspace_bytes(c, B, total_q, mql, msl)
+                assert need <= got <= need + (128 << 20) + 512, (B, total_q, mql, msl, got, need)
+                assert (got == 0) == (msl <= S)
