@@ -289,6 +289,7 @@ def summarize_shared_prefix_profile(trace_dir, pmc_dir):
 
 
 SPREAD_PROFILE_MD = os.path.join(ROOT, "profiles", "decode_spread_kernels_llama3-8b_b1.md")
+MIXED_PROFILE_MD = os.path.join(ROOT, "profiles", "prefill_split_grid_qwen3-235b_mixed.md")
 
 
 def summarize_spread_profile(trace_dir):
@@ -329,6 +330,57 @@ def summarize_spread_profile(trace_dir):
     with open(SPREAD_PROFILE_MD, "w") as f:
         f.write("\n".join(lines))
     print(SPREAD_PROFILE_MD)
+
+
+def summarize_mixed_profile(trace_dir):
+    """Writes the kernel-trace summary of the Qwen3-235B mixed prefill call under the automatic grid
+    (prefill_kernel with one workgroup per split for the decode rows, then prefill_merge_kernel)
+    and under in-workgroup folds (prefill_kernel alone), from bench.py --mixed-only."""
+    trace = sorted(_csv_rows(os.path.join(trace_dir, "**", "*kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    split, merge, fold = [], [], []
+    for i, r in enumerate(trace):
+        if "prefill_kernel<" not in r["Kernel_Name"]:
+            continue
+        nxt = trace[i + 1]["Kernel_Name"] if i + 1 < len(trace) else ""
+        if "prefill_merge_kernel<" in nxt:
+            split.append(dur(r))
+            merge.append(dur(trace[i + 1]))
+        else:
+            fold.append(dur(r))
+    name = next((r["Kernel_Name"] for r in trace if "prefill_kernel<" in r["Kernel_Name"]), "prefill_kernel")
+    mname = next((r["Kernel_Name"] for r in trace if "prefill_merge_kernel<" in r["Kernel_Name"]), "prefill_merge_kernel")
+    stat = lambda v: (f"{len(v)} | {sum(v) / len(v):.0f} | {min(v)} | {max(v)}") if v else "0 | - | - | -"
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o mixed -- "
+           "python3 bench.py --mixed-only --steps 20 --warmup 5")
+    lines = [
+        "# prefill split grid -- Qwen3-235B-shaped mixed prefill call",
+        "",
+        "64 query / 4 KV heads, head_dim 128, bf16 pages of 16 tokens, fixed 2048-token splits; one prefill call of "
+        "16 one-row decode queries at 32768 keys and 4 fresh 512-token prompts, first under the automatic prefill "
+        "grid (each decode row's sequence runs one workgroup per (row block, KV head, split), then the merge "
+        "kernel folds the split states), then under in-workgroup folds (one workgroup per (row block, KV head) "
+        "walks all 512 tiles). Both give the same bits.",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace)",
+        "",
+        f"    {cmd}",
+        "",
+        "| launch | kernel | dispatches | average ns | min ns | max ns |",
+        "|---|---|---|---|---|---|",
+        f"| automatic grid | {name} | {stat(split)} |",
+        f"| automatic grid | {mname} | {stat(merge)} |",
+        f"| in-workgroup folds | {name} | {stat(fold)} |",
+        "",
+    ]
+    if split and fold:
+        a = (sum(split) + sum(merge)) / len(split)
+        f = sum(fold) / len(fold)
+        lines += [f"Per call: {a / 1e3:.1f} us under the automatic grid (attention and merge kernels) against "
+                  f"{f / 1e3:.1f} us under in-workgroup folds ({f / a:.2f}x).", ""]
+    with open(MIXED_PROFILE_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(MIXED_PROFILE_MD)
 
 
 PREFILL_KERNEL = "prefill_kernel<128, false, 2>"
@@ -529,13 +581,14 @@ def summarize_prefill_profile(trace_dir, pmc_dir):
     print(PREFILL_PROFILE_MD)
 
 
-def make_ctx(shape, by_count=False, fp8=False, decode_kernel=None, kv_cache_hint=None):
+def make_ctx(shape, by_count=False, fp8=False, decode_kernel=None, kv_cache_hint=None, prefill_grid=None):
     return ia.Context(ia.make_config(shape.Hq, shape.Hkv, shape.d, page_size=shape.P, split_tokens=shape.S,
                                      kv_dtype=ia.IA_KV_FP8_E4M3 if fp8 else ia.IA_KV_BF16,
                                      split_policy=ia.IA_SPLIT_BY_COUNT if by_count else ia.IA_SPLIT_FIXED,
                                      sm_scale=shape.scale,
                                      decode_kernel=ia.IA_DECODE_AUTO if decode_kernel is None else decode_kernel,
-                                     kv_cache_hint=ia.IA_KV_HINT_AUTO if kv_cache_hint is None else kv_cache_hint))
+                                     kv_cache_hint=ia.IA_KV_HINT_AUTO if kv_cache_hint is None else kv_cache_hint,
+                                     prefill_grid=ia.IA_PREFILL_AUTO if prefill_grid is None else prefill_grid))
 
 
 class DecodeWorld:
@@ -1065,31 +1118,11 @@ def kv_append_prefill_size(steps=20, warmup=5):
             "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
-def qwen235_points(steps, warmup):
-    """Qwen3-235B-A22B attention shape (64 query / 4 KV heads, head_dim 128, bf16): decode at 32768
-    context for batch 1 / 16 / 64 -- the automatic kernel choice, and the cost of invariance with the
-    split kernel pinned (fixed 2048-token splits against the split-by-count variant, same kernel) --
-    and the mixed batch: 16 decode rows at 32768 context co-batched with 4 fresh 512-token prefill
-    chunks in one prefill call."""
-    shape = wl.QWEN3_235B
-    w = DecodeWorld(shape, [32768] * 64, gpu_values=True)
-    ctxs = {"auto": w.ctx, "split_fixed": make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT),
-            "split_by_count": make_ctx(shape, by_count=True, decode_kernel=ia.IA_DECODE_SPLIT)}
-    out = {}
-    for B in (1, 16, 64):
-        kb = w.kv_bytes(range(B))
-        row = {}
-        for name, ctx in ctxs.items():
-            _, d_ms = time_steps(DecodeRunner(w, range(B), ctx), steps, warmup, with_append=False)
-            _, dc_ms = time_steps(DecodeRunner(w, range(B), ctx), max(5, steps // 5), 3, with_append=False, flush=True)
-            row[name] = {"decode_ms": round(d_ms, 4), "gbs": round(kb / d_ms / 1e6, 1),
-                         "hbm_frac": round(kb / d_ms / 1e6 / HBM_PEAK_GBS, 4), "decode_ms_cold": round(dc_ms, 4),
-                         "gbs_cold": round(kb / dc_ms / 1e6, 1)}
-        row["fixed_over_by_count_time_same_kernel"] = round(row["split_fixed"]["decode_ms"] /
-                                                            row["split_by_count"]["decode_ms"], 3)
-        out[f"B{B}"] = row
-        log(f"qwen3-235b 32k B={B}: {row}")
-    # Mixed batch: one prefill call of 16 one-row decode queries (n = 32768) + 4 fresh 512-token prompts.
+def qwen235_mixed_call(w, steps, warmup):
+    """The Qwen3-235B mixed batch: one prefill call of 16 one-row decode queries at 32768 keys (the
+    first 16 sequences of w) and 4 fresh 512-token prompts, under the automatic prefill grid (the
+    decode rows run one workgroup per split) and under in-workgroup folds."""
+    shape = w.shape
     nq = 512
     lens_p = [nq] * 4
     layout_p = wl.layout_pages(21, lens_p, shape.P)
@@ -1119,15 +1152,52 @@ def qwen235_points(steps, warmup):
     ws = prefill_workspace(w.ctx, 20, q.shape[0], nq, 32768)
     stream = torch.cuda.current_stream()
 
-    def mixed():
-        ia.ia_paged_attn_prefill(w.ctx, q, cu, sl, kk, vv, btd, nq, 32768, o, workspace=ws, stream=stream)
-
-    ms = _timed(mixed, steps, warmup)
     flops = 4.0 * shape.d * shape.Hq * (16 * 32768 + 4 * nq * (nq + 1) / 2)
-    out["mixed_16x32k_decode_4x512_prefill"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-                                                 "decode_kv_gbs": round(w.kv_bytes(range(16)) / ms / 1e6, 1)}
-    log(f"qwen3-235b mixed: {out['mixed_16x32k_decode_4x512_prefill']}")
-    del w, kk, vv, kp, vp
+    out = {}
+    for name, grid in (("auto", ia.IA_PREFILL_AUTO), ("fold", ia.IA_PREFILL_FOLD)):
+        ctx = w.ctx if grid == ia.IA_PREFILL_AUTO else make_ctx(shape, prefill_grid=grid)
+
+        def mixed():
+            ia.ia_paged_attn_prefill(ctx, q, cu, sl, kk, vv, btd, nq, 32768, o, workspace=ws, stream=stream)
+
+        ms = _timed(mixed, steps, warmup)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                     "decode_kv_gbs": round(w.kv_bytes(range(16)) / ms / 1e6, 1)}
+    del kk, vv, kp, vp
+    torch.cuda.empty_cache()
+    return out
+
+
+def qwen235_points(steps, warmup):
+    """Qwen3-235B-A22B attention shape (64 query / 4 KV heads, head_dim 128, bf16): decode at 32768
+    context for batch 1 / 16 / 64 -- the automatic kernel choice, and the cost of invariance with the
+    split kernel pinned (fixed 2048-token splits against the split-by-count variant, same kernel) --
+    and the mixed batch: 16 decode rows at 32768 context co-batched with 4 fresh 512-token prefill
+    chunks in one prefill call."""
+    shape = wl.QWEN3_235B
+    w = DecodeWorld(shape, [32768] * 64, gpu_values=True)
+    ctxs = {"auto": w.ctx, "split_fixed": make_ctx(shape, decode_kernel=ia.IA_DECODE_SPLIT),
+            "split_by_count": make_ctx(shape, by_count=True, decode_kernel=ia.IA_DECODE_SPLIT)}
+    out = {}
+    for B in (1, 16, 64):
+        kb = w.kv_bytes(range(B))
+        row = {}
+        for name, ctx in ctxs.items():
+            _, d_ms = time_steps(DecodeRunner(w, range(B), ctx), steps, warmup, with_append=False)
+            _, dc_ms = time_steps(DecodeRunner(w, range(B), ctx), max(5, steps // 5), 3, with_append=False, flush=True)
+            row[name] = {"decode_ms": round(d_ms, 4), "gbs": round(kb / d_ms / 1e6, 1),
+                         "hbm_frac": round(kb / d_ms / 1e6 / HBM_PEAK_GBS, 4), "decode_ms_cold": round(dc_ms, 4),
+                         "gbs_cold": round(kb / dc_ms / 1e6, 1)}
+        row["fixed_over_by_count_time_same_kernel"] = round(row["split_fixed"]["decode_ms"] /
+                                                            row["split_by_count"]["decode_ms"], 3)
+        out[f"B{B}"] = row
+        log(f"qwen3-235b 32k B={B}: {row}")
+    # Mixed batch: one prefill call of 16 one-row decode queries (n = 32768) + 4 fresh 512-token prompts.
+    mixed = qwen235_mixed_call(w, steps, warmup)
+    out["mixed_16x32k_decode_4x512_prefill"] = mixed["auto"]
+    out["mixed_16x32k_decode_4x512_prefill_folds"] = mixed["fold"]
+    log(f"qwen3-235b mixed: {mixed}")
+    del w
     torch.cuda.empty_cache()
     return out
 
@@ -1268,12 +1338,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time the prefill workload only (for profilers)")
     ap.add_argument("--layer-only", action="store_true", help="time the layer operators only (for profilers)")
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="time the Qwen3-235B mixed prefill call only, automatic grid and folds (for profilers)")
     ap.add_argument("--shared-prefix-only", action="store_true",
                     help="time the Llama-3.1-70B shared-prefix decode only (for profilers)")
     ap.add_argument("--summarize-shared-prefix-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-prefill-profile", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--summarize-spread-profile", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-mixed-profile", metavar="TRACE_DIR")
     ap.add_argument("--summarize-layer-profile", nargs=2, metavar=("TRACE_DIR", "LAYER_JSON"))
     args = ap.parse_args()
     if args.summarize_profile:
@@ -1287,6 +1360,9 @@ def main():
         return
     if args.summarize_spread_profile:
         summarize_spread_profile(args.summarize_spread_profile)
+        return
+    if args.summarize_mixed_profile:
+        summarize_mixed_profile(args.summarize_mixed_profile)
         return
     if args.summarize_layer_profile:
         summarize_layer_profile(*args.summarize_layer_profile)
@@ -1305,6 +1381,10 @@ def main():
         return
     if args.layer_only:
         print(json.dumps({"layer_ops": layer_ops(args.steps, args.warmup)}), flush=True)
+        return
+    if args.mixed_only:
+        w = DecodeWorld(wl.QWEN3_235B, [32768] * 16, gpu_values=True)
+        print(json.dumps({"qwen235_mixed": qwen235_mixed_call(w, args.steps, args.warmup)}), flush=True)
         return
     if args.shared_prefix_only:
         shape = wl.LLAMA31_70B
